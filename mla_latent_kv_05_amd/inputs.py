@@ -1,0 +1,307 @@
+"""Seeded synthetic inputs for absorbed-MLA decode.
+
+This module only *creates* inputs: it draws seeded random numbers, rounds them
+to the storage precisions the kernels read (fp32, bf16, OCP fp8 e4m3fn with a
+per-token fp32 scale), and lays them out as a paged latent cache with a
+shuffled block table.  It holds none of the attention arithmetic; both the
+float64 oracle and the HIP path consume what it returns.
+
+Workloads (shapes from DeepSeek-V2/V3 as tabulated on the itwiki "Multi-head
+latent attention" page, section "DeepSeek-V2·V3 settings": n_h=128, d_h=128,
+d_c=512, d_h^R=64; the toy layer uses the dimensions of that page's
+"Implementation" example):
+
+* ``toy_layer``      d=1024, n_h=8, d_h=64, d_c=128, d_cq=256, d_r=32, fp32,
+                     T=256 tokens at positions 0..255.
+* ``decode_case``    V3-shaped absorbed decode: q_lat ~ N(0, 1/512),
+                     q_rope ~ N(0, 1), c^KV and k^R ~ N(0, 1), paged 64-token
+                     blocks, bf16 or fp8 content cache.
+
+Random streams: ``numpy.random.Generator(PCG64(seed))``; large tensors are
+drawn in float32 (ziggurat) and rounded round-to-nearest-even to bf16.
+
+Storage layouts (shared contract with the C ABI):
+
+* bf16 / fp32 cache: ``[num_blocks, block_size, d_c + d_r]`` row-major, one row
+  per token = ``[c^KV | k^R]``.
+* fp8 cache: per block ``[block_size*d_c e4m3fn | block_size*d_r bf16 k^R |
+  block_size fp32 scale]``, i.e. 644 bytes per token at d_c=512, d_r=64.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BLOCK = 64
+
+# --------------------------------------------------------------------------
+# rounding to storage formats (input creation only)
+# --------------------------------------------------------------------------
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even).
+
+    Returns the raw 16-bit patterns as uint16.  NaN stays NaN."""
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = a.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def bf16_bits_as_f32(bits) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32)
+
+
+def _e4m3fn_positive_table() -> np.ndarray:
+    # all non-negative finite e4m3fn values, indexed by their 7-bit code 0..126
+    vals = np.empty(127, dtype=np.float64)
+    for code in range(127):
+        e, m = code >> 3, code & 7
+        vals[code] = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+_E4M3_POS = _e4m3fn_positive_table()
+E4M3_MAX = 448.0
+
+
+def encode_e4m3fn(x) -> np.ndarray:
+    """Encode values as OCP fp8 e4m3fn codes: round to nearest, ties to even
+    code (even mantissa), saturating at +-448."""
+    x = np.asarray(x, dtype=np.float64)
+    mag = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.searchsorted(_E4M3_POS, mag, side="left")  # first code with value >= mag
+    hi = np.clip(hi, 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    vhi, vlo = _E4M3_POS[hi], _E4M3_POS[lo]
+    dhi, dlo = vhi - mag, mag - vlo
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(mag == vhi, hi, code).astype(np.uint8)
+    sign = (np.signbit(x) & (code != 0)).astype(np.uint8) << 7
+    return (code | sign).astype(np.uint8)
+
+
+def quantize_rows_e4m3(c) -> tuple[np.ndarray, np.ndarray]:
+    """Per-token fp8 quantisation of content rows ``c`` [..., d_c].
+
+    scale_t = amax_t / 448 in fp32 (1.0 for an all-zero row),
+    code = e4m3fn(c / scale_t)."""
+    c = np.asarray(c, dtype=np.float32)
+    amax = np.abs(c).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    codes = encode_e4m3fn(c.astype(np.float64) / scale.astype(np.float64)[..., None])
+    return codes, scale
+
+
+# --------------------------------------------------------------------------
+# toy layer (fp32): d=1024, n_h=8, d_h=64, d_c=128, d_cq=256, d_r=32
+# --------------------------------------------------------------------------
+
+TOY_DIMS = dict(d=1024, n_h=8, d_h=64, d_c=128, d_cq=256, d_r=32)
+
+
+def toy_layer(seed: int = 1, B: int = 1, T: int = 256, dims: dict | None = None,
+              dtype=np.float32) -> dict:
+    """Weights i.i.d. N(0, 1/fan_in) stored [out, in]; hidden states N(0,1);
+    positions 0..T-1.  Values are drawn in float64 and rounded to ``dtype``."""
+    dm = dict(TOY_DIMS if dims is None else dims)
+    d, n_h, d_h, d_c, d_cq, d_r = (dm[k] for k in ("d", "n_h", "d_h", "d_c", "d_cq", "d_r"))
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shapes = {  # name: (out, in)
+        "w_dq": (d_cq, d), "w_uq": (n_h * d_h, d_cq), "w_qr": (n_h * d_r, d_cq),
+        "w_dkv": (d_c, d), "w_kr": (d_r, d), "w_uk": (n_h * d_h, d_c),
+        "w_uv": (n_h * d_h, d_c), "w_o": (d, n_h * d_h),
+    }
+    out = {"dims": dm}
+    for name, (o, i) in shapes.items():
+        out[name] = (rng.standard_normal((o, i)) / math.sqrt(i)).astype(dtype)
+    out["h"] = rng.standard_normal((B, T, d)).astype(dtype)
+    out["pos"] = np.arange(T, dtype=np.int64)
+    return out
+
+
+# --------------------------------------------------------------------------
+# absorbed decode workloads
+# --------------------------------------------------------------------------
+
+
+@dataclass
+class DecodeCase:
+    B: int
+    s_q: int
+    n_h: int
+    d_c: int
+    d_r: int
+    d_h: int
+    block_size: int
+    kv_dtype: str               # "bf16" | "fp8" | "f32"
+    q_dtype: str                # "bf16" | "f32"
+    seq_lens: np.ndarray        # [B] int32
+    block_table: np.ndarray     # [B, max_blocks] int32 (unused slots = -1 ... or poison)
+    cache: np.ndarray           # storage array (uint16 for bf16, uint8 for fp8, float32)
+    q_lat: np.ndarray           # [B, s_q, n_h, d_c] storage (uint16 bf16 bits or float32)
+    q_rope: np.ndarray          # [B, s_q, n_h, d_r]
+    softmax_scale: float
+    num_blocks: int
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def row_bytes(self) -> int:
+        if self.kv_dtype == "fp8":
+            return self.d_c + 2 * self.d_r + 4
+        return (self.d_c + self.d_r) * (2 if self.kv_dtype == "bf16" else 4)
+
+    @property
+    def block_bytes(self) -> int:
+        return self.row_bytes * self.block_size
+
+    @property
+    def latent_bytes(self) -> int:
+        return int(self.seq_lens.astype(np.int64).sum()) * self.row_bytes
+
+
+def _draw(rng, shape, std, kind):
+    if kind == "f64":
+        return rng.standard_normal(shape) * std
+    return rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
+
+
+def make_lengths(kind: str, B: int, rng, L: int | None = None,
+                 lo: int = 128, hi: int = 32768) -> np.ndarray:
+    if kind == "fixed":
+        return np.full(B, L, dtype=np.int32)
+    if kind == "loguniform":
+        u = rng.uniform(math.log(lo), math.log(hi), size=B)
+        return np.clip(np.floor(np.exp(u)), lo, hi).astype(np.int32)
+    raise ValueError(kind)
+
+
+def decode_case(seed: int, B: int, seq_lens, s_q: int = 1, n_h: int = 128,
+                d_c: int = 512, d_r: int = 64, d_h: int = 128, kv_dtype: str = "bf16",
+                q_dtype: str = "bf16", block_size: int = BLOCK, q_lat_std: float | None = None,
+                extra_blocks: int = 0, tail_fill: str = "random") -> DecodeCase:
+    """Paged absorbed-decode inputs.
+
+    ``seq_lens`` is an int, or an array of per-sequence lengths.  Physical
+    block ids are one seeded permutation of 0..num_blocks-1 handed out in
+    (sequence, logical block) order.  ``extra_blocks`` adds unreferenced
+    physical blocks; ``tail_fill`` = "nan" poisons the unused tail rows of each
+    sequence's last block (bf16/f32 caches) to show they are never read into
+    the result."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = np.full(B, seq_lens, dtype=np.int32) if np.isscalar(seq_lens) else \
+        np.asarray(seq_lens, dtype=np.int32)
+    assert lens.shape == (B,) and (lens >= s_q).all()
+    nblk = (lens + block_size - 1) // block_size
+    max_blocks = int(nblk.max())
+    num_blocks = int(nblk.sum()) + extra_blocks
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    k = 0
+    for b in range(B):
+        table[b, : nblk[b]] = perm[k: k + nblk[b]]
+        k += nblk[b]
+    D = d_c + d_r
+    kind = "f32" if (kv_dtype != "f32" and q_dtype != "f32") else "f64"
+    rows = _draw(rng, (num_blocks, block_size, D), 1.0, kind)
+    if kv_dtype == "bf16":
+        cache = f32_to_bf16_bits(rows)
+    elif kv_dtype == "f32":
+        cache = rows.astype(np.float32)
+    elif kv_dtype == "fp8":
+        codes, scale = quantize_rows_e4m3(rows[..., :d_c])
+        kr = f32_to_bf16_bits(rows[..., d_c:])
+        blk = np.empty((num_blocks, block_size * (d_c + 2 * d_r + 4)), dtype=np.uint8)
+        o1 = block_size * d_c
+        o2 = o1 + block_size * d_r * 2
+        blk[:, :o1] = codes.reshape(num_blocks, -1)
+        blk[:, o1:o2] = kr.reshape(num_blocks, -1).view(np.uint8).reshape(num_blocks, -1)
+        blk[:, o2:] = scale.reshape(num_blocks, -1).view(np.uint8).reshape(num_blocks, -1)
+        cache = blk
+    else:
+        raise ValueError(kv_dtype)
+    if tail_fill == "nan" and kv_dtype in ("bf16", "f32"):
+        for b in range(B):
+            used = lens[b] - (nblk[b] - 1) * block_size
+            if used < block_size:
+                pb = table[b, nblk[b] - 1]
+                cache[pb, used:] = 0x7FC0 if kv_dtype == "bf16" else np.nan
+    if q_lat_std is None:
+        q_lat_std = 1.0 / math.sqrt(d_c)
+    ql = _draw(rng, (B, s_q, n_h, d_c), q_lat_std, kind)
+    qr = _draw(rng, (B, s_q, n_h, d_r), 1.0, kind)
+    if q_dtype == "bf16":
+        ql, qr = f32_to_bf16_bits(ql), f32_to_bf16_bits(qr)
+    else:
+        ql, qr = ql.astype(np.float32), qr.astype(np.float32)
+    return DecodeCase(B=B, s_q=s_q, n_h=n_h, d_c=d_c, d_r=d_r, d_h=d_h,
+                      block_size=block_size, kv_dtype=kv_dtype, q_dtype=q_dtype,
+                      seq_lens=lens, block_table=table, cache=cache, q_lat=ql,
+                      q_rope=qr, softmax_scale=1.0 / math.sqrt(d_h + d_r),
+                      num_blocks=num_blocks)
+
+
+def projection_weights(seed: int, T_q: int, n_h: int = 128, d_h: int = 128,
+                       d_c: int = 512, dtype: str = "bf16") -> dict:
+    """Inputs for the query absorption and the W^UV up-projection at V3 shapes.
+
+    q^C ~ N(0,1) [T_q, n_h, d_h]; W^UK ~ N(0, 1/(d_h*d_c)) so that the absorbed
+    query has variance 1/d_c like the decode workloads; W^UV ~ N(0, 1/d_c)
+    (fan-in d_c); o_lat ~ N(0, 1/64) stands in for a decode output.  Both
+    weights are stored [n_h*d_h, d_c] ([out, in])."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kind = "f32" if dtype == "bf16" else "f64"
+    q_c = _draw(rng, (T_q, n_h, d_h), 1.0, kind)
+    w_uk = _draw(rng, (n_h * d_h, d_c), 1.0 / math.sqrt(d_h * d_c), kind)
+    w_uv = _draw(rng, (n_h * d_h, d_c), 1.0 / math.sqrt(d_c), kind)
+    o_lat = _draw(rng, (T_q, n_h, d_c), 1.0 / 8.0, kind)
+    conv = f32_to_bf16_bits if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    return {"q_c": conv(q_c), "w_uk": conv(w_uk), "w_uv": conv(w_uv), "o_lat": conv(o_lat),
+            "dtype": dtype, "T_q": T_q, "n_h": n_h, "d_h": d_h, "d_c": d_c}
+
+
+# --------------------------------------------------------------------------
+# the five workloads
+# --------------------------------------------------------------------------
+
+WORKLOADS = {
+    "toy_fp32_T256": dict(kind="toy", seed=1),
+    "v3_bf16_B64_ctx8192": dict(kind="decode", seed=2, B=64, lens=("fixed", 8192), s_q=1,
+                                kv_dtype="bf16"),
+    "v3_bf16_B128_ctxlogU128-32768": dict(kind="decode", seed=3, B=128,
+                                          lens=("loguniform", None), s_q=1, kv_dtype="bf16"),
+    "v3_bf16_B4_ctx131072": dict(kind="decode", seed=4, B=4, lens=("fixed", 131072), s_q=1,
+                                 kv_dtype="bf16"),
+    "v3_fp8_B64_ctx16384_sq2": dict(kind="decode", seed=5, B=64, lens=("fixed", 16384), s_q=2,
+                                    kv_dtype="fp8"),
+}
+
+
+def workload_lengths(name: str, B: int | None = None) -> np.ndarray:
+    w = WORKLOADS[name]
+    B = w["B"] if B is None else B
+    rng = np.random.Generator(np.random.PCG64(w["seed"] + 1000))
+    kind, L = w["lens"]
+    return make_lengths(kind, B, rng, L)
+
+
+def workload_case(name: str, B: int | None = None, L: int | None = None, **kw) -> DecodeCase:
+    """A decode workload; ``B``/``L`` shrink it for quick tests."""
+    w = WORKLOADS[name]
+    B = w["B"] if B is None else B
+    lens = workload_lengths(name, B)
+    if L is not None:
+        lens = np.minimum(lens, L).astype(np.int32) if w["lens"][0] != "fixed" else \
+            np.full(B, L, dtype=np.int32)
+    return decode_case(w["seed"], B, lens, s_q=w["s_q"], kv_dtype=w["kv_dtype"], **kw)

@@ -1,0 +1,332 @@
+"""Float64 CPU oracle for Multi-head Latent Attention decode.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, obviously-correct
+reference that the HIP path is checked against.  Only the test-suite, the
+package smoke check and the benchmark's CPU-baseline leg may import it; the
+product path never does.  It imports nothing from the HIP side and shares no
+code with it.
+
+Source of truth: the itwiki article "멀티 헤드 잠재 어텐션" (Multi-head latent
+attention), section "구조" (Structure):
+
+* "키·값 공동 압축" (joint KV compression): c^KV_t = W^DKV h_t,
+  k^C_t = W^UK c^KV_t, v^C_t = W^UV c^KV_t; queries c^Q_t = W^DQ h_t,
+  q^C_t = W^UQ c^Q_t.
+* "분리 RoPE" (decoupled RoPE): q^R_t = RoPE(W^QR c^Q_t) (one per head),
+  k^R_t = RoPE(W^KR h_t) (shared by all heads); q = [q^C; q^R], k = [k^C; k^R];
+  o_{t,i} = sum_{j<=t} softmax_j(q^T k / sqrt(d_h + d_h^R)) v^C_{j,i};
+  u_t = W^O [o_{t,1}; ...; o_{t,n_h}].
+* "행렬 흡수" (matrix absorption): q^T W^UK c = (W^UK^T q)^T c, so the content
+  query is moved into latent space and dotted with the cached c^KV; every
+  head then uses the same c^KV as key and value ("MQA mode"), and W^UV is
+  applied after the weighted latent sum.
+
+The lecture page "MHA · GQA · MQA · MLA" (section "Why Projection Absorption
+Helps") states the same absorption identity and the 512 + 64 = 576 values per
+token and layer that the cache holds.
+
+Readings where the pages leave a step open (each one is also listed with the
+design notes):
+
+* RoPE is the half-split form: pairs (x_k, x_{k+d/2}) are rotated by the
+  angle pos * base^(-2k/d), base 10000 (the article's implementation example
+  uses this pairing).  Angles are computed in float64.
+* Weights are stored [out, in]; W^UK and W^UV are viewed per head as
+  [n_h, d_h, d_c] (head i = rows i*d_h .. (i+1)*d_h-1).
+* Decode queries: the cache already holds the s_q new tokens; query i of a
+  sequence of length L sits at position L - s_q + i and sees keys
+  0 .. L - s_q + i (the "j <= t" of the attention equation).
+* LSE is the natural log of the sum of exp(scaled score) over visible keys.
+
+Storage decoders (bf16 bits, OCP fp8 e4m3fn codes, the paged fp8 block
+layout) are written here from the formats' definitions.
+
+Parity status: every function below is pinned by tests/test_oracle.py
+(absorbed vs materialised agreement, closed forms, torch's CPU
+scaled_dot_product_attention, complex-number rotation, the cache arithmetic
+the pages print).  The fp8 *scheme* (per-token amax/448 scale) is a reading of
+"FP8 content cache, BF16 RoPE key" and is pinned only by self-consistency and
+the e4m3fn format facts.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# storage decoders
+# --------------------------------------------------------------------------
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bfloat16 bit patterns -> float64 (exact): the 16 bits are the top half
+    of an IEEE binary32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def e4m3fn_to_f64(codes) -> np.ndarray:
+    """OCP 8-bit float E4M3 ("fn": no infinities) -> float64.
+
+    Layout s.eeee.mmm, exponent bias 7.  e=0 encodes subnormals m/8 * 2^-6;
+    e=15, m=7 is NaN; everything else is (1 + m/8) * 2^(e-7).  Max 448."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = s * mag
+    return np.where((e == 15) & (m == 7), np.nan, out)
+
+
+def paged_rows(cache, block_table_row, L, kv_dtype, d_c, d_r, block_size):
+    """Logical rows 0..L-1 of one sequence, gathered through its block table.
+
+    Returns (c [L, d_c], k_r [L, d_r]) in float64.  Token j lives in physical
+    block table[j // block_size] at slot j % block_size."""
+    c = np.empty((L, d_c))
+    kr = np.empty((L, d_r))
+    for j in range(0, L, block_size):
+        n = min(block_size, L - j)
+        pb = int(block_table_row[j // block_size])
+        blk = cache[pb]
+        if kv_dtype == "bf16":
+            rows = bf16_to_f64(blk[:n])
+            c[j:j + n], kr[j:j + n] = rows[:, :d_c], rows[:, d_c:d_c + d_r]
+        elif kv_dtype == "f32":
+            rows = np.asarray(blk[:n], dtype=np.float64)
+            c[j:j + n], kr[j:j + n] = rows[:, :d_c], rows[:, d_c:d_c + d_r]
+        elif kv_dtype == "fp8":
+            raw = np.asarray(blk, dtype=np.uint8)
+            o1 = block_size * d_c
+            o2 = o1 + block_size * d_r * 2
+            codes = raw[:o1].reshape(block_size, d_c)[:n]
+            kbits = raw[o1:o2].view(np.uint16).reshape(block_size, d_r)[:n]
+            scale = raw[o2:o2 + 4 * block_size].view(np.float32)[:n].astype(np.float64)
+            c[j:j + n] = e4m3fn_to_f64(codes) * scale[:, None]
+            kr[j:j + n] = bf16_to_f64(kbits)
+        else:
+            raise ValueError(kv_dtype)
+    return c, kr
+
+
+# --------------------------------------------------------------------------
+# RoPE (decoupled position part)
+# --------------------------------------------------------------------------
+
+
+def rope(x, pos, base: float = 10000.0):
+    """Half-split rotary embedding.  x [..., T, d], pos [T].
+
+    Pair k (k < d/2) is (x_k, x_{k+d/2}); it is rotated by the angle
+    pos * base^(-2k/d)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    theta = base ** (-2.0 * np.arange(half, dtype=np.float64) / d)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * theta[None, :]
+    cos, sin = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+# --------------------------------------------------------------------------
+# cache arithmetic ("캐시 크기 비교" table of the itwiki article)
+# --------------------------------------------------------------------------
+
+
+def cache_elements_per_token(method: str, n_h=128, d_h=128, n_g=1, d_c=512, d_r=64, layers=1):
+    """KV-cache elements per token: MHA 2 n_h d_h l, GQA 2 n_g d_h l,
+    MQA 2 d_h l, MLA (d_c + d_h^R) l."""
+    if method == "MHA":
+        return 2 * n_h * d_h * layers
+    if method == "GQA":
+        return 2 * n_g * d_h * layers
+    if method == "MQA":
+        return 2 * d_h * layers
+    if method == "MLA":
+        return (d_c + d_r) * layers
+    raise ValueError(method)
+
+
+# --------------------------------------------------------------------------
+# softmax attention pieces
+# --------------------------------------------------------------------------
+
+
+def _softmax_rows(s):
+    """Row softmax of s (masked entries = -inf) and the row log-sum-exp."""
+    m = np.max(s, axis=-1, keepdims=True)
+    p = np.exp(s - m)
+    z = p.sum(axis=-1, keepdims=True)
+    return p / z, (m + np.log(z))[..., 0]
+
+
+def attention_probs(q_lat, q_rope, c, kr, scale, visible):
+    """Softmax weights of one query row set over its visible keys.
+
+    q_lat [n, d_c], q_rope [n, d_r], c [L, d_c], kr [L, d_r]; keys 0..visible-1
+    are visible.  Returns p [n, visible] and lse [n]."""
+    s = (q_lat @ c[:visible].T + q_rope @ kr[:visible].T) * scale
+    return _softmax_rows(s)
+
+
+# --------------------------------------------------------------------------
+# O1: MHA mode (materialise k^C and v^C per head)
+# --------------------------------------------------------------------------
+
+
+def project(h, W, pos):
+    """The per-token projections of the layer (compression + decoupled RoPE).
+
+    h [B, T, d].  Returns c_kv [B,T,d_c], k_r [B,T,d_r], q_c [B,T,n_h,d_h],
+    q_r [B,T,n_h,d_r] (all float64)."""
+    dm = W["dims"]
+    n_h, d_h, d_r = dm["n_h"], dm["d_h"], dm["d_r"]
+    h = np.asarray(h, dtype=np.float64)
+    f = lambda name: np.asarray(W[name], dtype=np.float64)
+    B, T, _ = h.shape
+    c_kv = h @ f("w_dkv").T
+    k_r = np.stack([rope(h[b] @ f("w_kr").T, pos) for b in range(B)])
+    c_q = h @ f("w_dq").T
+    q_c = (c_q @ f("w_uq").T).reshape(B, T, n_h, d_h)
+    qr_flat = (c_q @ f("w_qr").T).reshape(B, T, n_h, d_r)
+    q_r = np.empty_like(qr_flat)
+    for b in range(B):
+        for i in range(n_h):
+            q_r[b, :, i] = rope(qr_flat[b, :, i], pos)
+    return c_kv, k_r, q_c, q_r
+
+
+def mha_mode_layer(h, W, pos):
+    """Full layer in MHA mode.
+
+    Returns dict with u [B,T,d] (layer output), o [B,T,n_h,d_h] (per-head
+    attention outputs before W^O), lse [B,T,n_h], and the projections."""
+    dm = W["dims"]
+    n_h, d_h, d_r = dm["n_h"], dm["d_h"], dm["d_r"]
+    c_kv, k_r, q_c, q_r = project(h, W, pos)
+    B, T = c_kv.shape[:2]
+    w_uk = np.asarray(W["w_uk"], dtype=np.float64)
+    w_uv = np.asarray(W["w_uv"], dtype=np.float64)
+    k_c = (c_kv @ w_uk.T).reshape(B, T, n_h, d_h)
+    v_c = (c_kv @ w_uv.T).reshape(B, T, n_h, d_h)
+    scale = 1.0 / math.sqrt(d_h + d_r)
+    causal = np.tril(np.ones((T, T), dtype=bool))  # key j visible to query t iff j <= t
+    o = np.empty((B, T, n_h, d_h))
+    lse = np.empty((B, T, n_h))
+    for b in range(B):
+        for i in range(n_h):
+            s = (q_c[b, :, i] @ k_c[b, :, i].T + q_r[b, :, i] @ k_r[b].T) * scale
+            s = np.where(causal, s, -np.inf)
+            p, lse[b, :, i] = _softmax_rows(s)
+            o[b, :, i] = p @ v_c[b, :, i]
+    u = o.reshape(B, T, n_h * d_h) @ np.asarray(W["w_o"], dtype=np.float64).T
+    return {"u": u, "o": o, "lse": lse, "c_kv": c_kv, "k_r": k_r, "q_c": q_c, "q_r": q_r}
+
+
+# --------------------------------------------------------------------------
+# absorption, MQA-mode decode, combine, up-projection
+# --------------------------------------------------------------------------
+
+
+def absorb_q(q_c, w_uk, n_h, d_h):
+    """q_lat[t,i,:] = W^UK_i^T q^C[t,i,:]; w_uk [n_h*d_h, d_c] ([out, in])."""
+    w = np.asarray(w_uk, dtype=np.float64).reshape(n_h, d_h, -1)
+    q = np.asarray(q_c, dtype=np.float64)
+    return np.einsum("thk,hkc->thc", q, w)
+
+
+def up_proj_v(o_lat, w_uv, n_h, d_h):
+    """o[t,i,:] = W^UV_i o_lat[t,i,:]; w_uv [n_h*d_h, d_c] ([out, in])."""
+    w = np.asarray(w_uv, dtype=np.float64).reshape(n_h, d_h, -1)
+    return np.einsum("thc,hkc->thk", np.asarray(o_lat, dtype=np.float64), w)
+
+
+def mqa_decode_rows(q_lat, q_rope, c, kr, scale, key_range=None):
+    """MQA-mode decode of one sequence on contiguous latent rows.
+
+    q_lat [s_q, n_h, d_c], q_rope [s_q, n_h, d_r]; c [L, d_c], kr [L, d_r].
+    Query i sees keys 0 .. L - s_q + i.  ``key_range`` = (lo, hi) restricts
+    the keys to [lo, hi) on top of that (a split-KV partition); a row with no
+    visible key gets o = 0 and lse = -inf.
+
+    Returns o_lat [s_q, n_h, d_c] and lse [s_q, n_h]."""
+    s_q, n_h, d_c = q_lat.shape
+    L = c.shape[0]
+    lo, hi = (0, L) if key_range is None else key_range
+    o = np.zeros((s_q, n_h, d_c))
+    lse = np.full((s_q, n_h), -np.inf)
+    for i in range(s_q):
+        vis_hi = min(hi, L - s_q + i + 1)
+        if vis_hi <= lo:
+            continue
+        s = (q_lat[i] @ c[lo:vis_hi].T + q_rope[i] @ kr[lo:vis_hi].T) * scale
+        p, lse[i] = _softmax_rows(s)
+        o[i] = p @ c[lo:vis_hi]
+    return o, lse
+
+
+def combine_lse(o_parts, lse_parts):
+    """Merge partial results of disjoint key sets.
+
+    o_parts [S, ..., D] (each normalised over its own keys), lse_parts [S, ...].
+    lse = log sum_s exp(lse_s); o = sum_s exp(lse_s - lse) o_s.  Parts with
+    lse = -inf carry no weight; if all are -inf the result is o = 0,
+    lse = -inf."""
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = np.max(lse_parts, axis=0)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(lse_parts - m_safe)
+    z = w.sum(axis=0)
+    lse = np.where(z > 0, m_safe + np.log(np.where(z > 0, z, 1.0)), -np.inf)
+    o = np.einsum("s...,s...d->...d", w, o_parts) / np.where(z > 0, z, 1.0)[..., None]
+    return o, lse
+
+
+def decode_case_rows(case, b):
+    """(q_lat [s_q,n_h,d_c], q_rope [s_q,n_h,d_r], c [L,d_c], kr [L,d_r]) in
+    float64 for sequence b of an inputs.DecodeCase-like object."""
+    L = int(case.seq_lens[b])
+    c, kr = paged_rows(case.cache, case.block_table[b], L, case.kv_dtype,
+                       case.d_c, case.d_r, case.block_size)
+    dec = bf16_to_f64 if case.q_dtype == "bf16" else (lambda a: np.asarray(a, np.float64))
+    return dec(case.q_lat[b]), dec(case.q_rope[b]), c, kr
+
+
+def mqa_decode_case(case, seqs=None):
+    """O2 on a paged case: returns o_lat [B', s_q, n_h, d_c], lse [B', s_q, n_h]
+    for the sequences in ``seqs`` (default all)."""
+    seqs = range(case.B) if seqs is None else seqs
+    outs, lses = [], []
+    for b in seqs:
+        ql, qr, c, kr = decode_case_rows(case, b)
+        o, l = mqa_decode_rows(ql, qr, c, kr, case.softmax_scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
+def absorbed_layer(h, W, pos):
+    """O3: the same layer computed in MQA mode (absorbed), from the same
+    projections as mha_mode_layer.  Returns u, o, lse, o_lat."""
+    dm = W["dims"]
+    n_h, d_h, d_r = dm["n_h"], dm["d_h"], dm["d_r"]
+    c_kv, k_r, q_c, q_r = project(h, W, pos)
+    B, T = c_kv.shape[:2]
+    scale = 1.0 / math.sqrt(d_h + d_r)
+    o = np.empty((B, T, n_h, d_h))
+    o_lat = np.empty((B, T, n_h, dm["d_c"]))
+    lse = np.empty((B, T, n_h))
+    for b in range(B):
+        q_lat = absorb_q(q_c[b], W["w_uk"], n_h, d_h)           # [T, n_h, d_c]
+        # every query row t is a decode step over the first t+1 cache rows
+        ol, l = mqa_decode_rows(q_lat, q_r[b], c_kv[b], k_r[b], scale)  # s_q = T
+        o_lat[b], lse[b] = ol, l
+        o[b] = up_proj_v(ol, W["w_uv"], n_h, d_h)
+    u = o.reshape(B, T, n_h * d_h) @ np.asarray(W["w_o"], dtype=np.float64).T
+    return {"u": u, "o": o, "lse": lse, "o_lat": o_lat}

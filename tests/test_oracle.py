@@ -1,0 +1,346 @@
+"""Pins for the float64 oracle (CPU only).
+
+Each test ties the oracle to something other than itself: figures the pages
+print, closed forms, a textbook library routine (torch's CPU
+scaled_dot_product_attention, numpy complex rotation), brute force in 50-digit
+arithmetic, and invariants the method guarantees."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_kv_05_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "cache_arithmetic.json")
+
+
+def _small_decode(seed=0, s_q=2, n_h=4, d_c=16, d_r=8, L=37):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((s_q, n_h, d_c)), rng.standard_normal((s_q, n_h, d_r)),
+            rng.standard_normal((L, d_c)), rng.standard_normal((L, d_r)))
+
+
+# ---------------------------------------------------------------- pages' figures
+
+def test_cache_arithmetic_golden():
+    g = json.load(open(GOLDEN))
+    for it in g["items"]:
+        assert oracle.cache_elements_per_token(it["method"], **it["args"]) == it["elements"], it
+    for r in g["ratios"]:
+        v = r["num"] / r["den"]
+        if "exact" in r:
+            assert v == r["exact"]
+        else:
+            assert abs(v - r["approx"]) <= r["tol"]
+    lec = g["bytes_bf16"][0]
+    per = lec["per_layer_bytes"]
+    assert 2 * oracle.cache_elements_per_token("MHA", n_h=32, d_h=128) == per["MHA"]
+    assert 2 * oracle.cache_elements_per_token("GQA", n_g=8, d_h=128) == per["GQA-8"]
+    assert 2 * oracle.cache_elements_per_token("MQA", d_h=128) == per["MQA"]
+    assert 2 * oracle.cache_elements_per_token("MLA") == per["MLA"]
+    assert abs(per["MLA"] / 1024 - lec["mla_approx_kib"]) < 0.05
+    chart = g["bytes_bf16"][1]
+    for m, kib in chart["kib_per_token"].items():
+        el = {"MHA": oracle.cache_elements_per_token("MHA", n_h=32, d_h=128),
+              "GQA-8": oracle.cache_elements_per_token("GQA", n_g=8, d_h=128),
+              "MLA": oracle.cache_elements_per_token("MLA"),
+              "MQA": oracle.cache_elements_per_token("MQA", d_h=128)}[m]
+        assert el * 2 * chart["layers"] / 1024 == kib
+    for it in g["bytes_bf16"][2:]:
+        assert abs(it["elements"] * 2 / 1024 - it["approx_kb"]) <= it["tol_kb"] + 0.5
+    s = g["scale"]
+    assert abs(1.0 / math.sqrt(s["d_h"] + s["d_r"]) - s["value"]) < 1e-16
+
+
+def test_storage_row_bytes_match_pages():
+    # one bf16 latent row is 576 values = 1152 bytes ("about 1.1 KiB")
+    c = inputs.decode_case(0, B=1, seq_lens=64, n_h=4)
+    assert c.row_bytes == 1152 and c.d_c + c.d_r == 576
+    f = inputs.decode_case(0, B=1, seq_lens=64, n_h=4, kv_dtype="fp8")
+    assert f.row_bytes == 512 + 128 + 4
+
+
+# ---------------------------------------------------------------- absorption (M1)
+
+def _toy_weights(seed, dims):
+    return inputs.toy_layer(seed=seed, B=2, T=12, dims=dims, dtype=np.float64)
+
+
+def test_absorbed_equals_mha_page_example():
+    """The article runs both forms in float64 at B=2, T=12 with its example
+    dimensions and reports agreement at the 1e-15 level."""
+    W = _toy_weights(7, inputs.TOY_DIMS)
+    h, pos = W["h"], W["pos"]
+    a = oracle.mha_mode_layer(h, W, pos)
+    b = oracle.absorbed_layer(h, W, pos)
+    assert np.max(np.abs(a["u"] - b["u"])) <= 1e-14 * max(1.0, np.max(np.abs(a["u"])))
+    assert np.max(np.abs(a["o"] - b["o"])) <= 1e-14 * np.max(np.abs(a["o"]))
+    assert np.max(np.abs(a["lse"] - b["lse"])) <= 1e-13
+
+
+def test_absorbed_equals_mha_toy_config_T256():
+    W = inputs.toy_layer(seed=1, B=1, T=256, dtype=np.float64)
+    a = oracle.mha_mode_layer(W["h"], W, W["pos"])
+    b = oracle.absorbed_layer(W["h"], W, W["pos"])
+    assert np.max(np.abs(a["o"] - b["o"])) <= 1e-13 * np.max(np.abs(a["o"]))
+    assert np.max(np.abs(a["u"] - b["u"])) <= 1e-13 * np.max(np.abs(a["u"]))
+
+
+def test_absorbed_equals_mha_v3_shapes():
+    dims = dict(d=512, n_h=128, d_h=128, d_c=512, d_cq=256, d_r=64)
+    W = inputs.toy_layer(seed=3, B=1, T=40, dims=dims, dtype=np.float64)
+    a = oracle.mha_mode_layer(W["h"], W, W["pos"])
+    b = oracle.absorbed_layer(W["h"], W, W["pos"])
+    assert np.max(np.abs(a["o"] - b["o"])) <= 1e-13 * np.max(np.abs(a["o"]))
+
+
+def test_absorption_identity():
+    rng = np.random.default_rng(5)
+    n_h, d_h, d_c = 8, 16, 32
+    w = rng.standard_normal((n_h * d_h, d_c))
+    q = rng.standard_normal((3, n_h, d_h))
+    cvec = rng.standard_normal(d_c)
+    k = (w @ cvec).reshape(n_h, d_h)        # k^C = W^UK c, per head
+    lhs = np.einsum("thk,hk->th", q, k)      # q^T k
+    rhs = oracle.absorb_q(q, w, n_h, d_h) @ cvec
+    assert np.max(np.abs(lhs - rhs)) <= 1e-13 * np.max(np.abs(lhs))
+
+
+def test_mpmath_bruteforce_tiny():
+    """MHA-mode definition evaluated in 50-digit arithmetic on a tiny case
+    (materialised keys/values per head) vs the oracle's absorbed decode."""
+    mp = pytest.importorskip("mpmath")
+    mp.mp.dps = 50
+    rng = np.random.default_rng(11)
+    n_h, d_h, d_c, d_r, L, s_q = 2, 3, 4, 2, 4, 2
+    w_uk = rng.standard_normal((n_h * d_h, d_c))
+    w_uv = rng.standard_normal((n_h * d_h, d_c))
+    q_c = rng.standard_normal((s_q, n_h, d_h))
+    q_r = rng.standard_normal((s_q, n_h, d_r))
+    c = rng.standard_normal((L, d_c))
+    kr = rng.standard_normal((L, d_r))
+    scale = 1.0 / math.sqrt(d_h + d_r)
+    ql = oracle.absorb_q(q_c, w_uk, n_h, d_h)
+    o_lat, lse = oracle.mqa_decode_rows(ql, q_r, c, kr, scale)
+    o = oracle.up_proj_v(o_lat, w_uv, n_h, d_h)
+    M = lambda a: mp.mpf(float(a))
+    for i in range(s_q):
+        t = L - s_q + i
+        for hh in range(n_h):
+            keys = []
+            for j in range(t + 1):
+                kc = [sum(M(w_uk[hh * d_h + a, b]) * M(c[j, b]) for b in range(d_c)) for a in range(d_h)]
+                sc = sum(M(q_c[i, hh, a]) * kc[a] for a in range(d_h)) + \
+                    sum(M(q_r[i, hh, a]) * M(kr[j, a]) for a in range(d_r))
+                keys.append(sc * M(scale))
+            z = sum(mp.e ** s for s in keys)
+            assert abs(float(mp.log(z)) - lse[i, hh]) <= 1e-14
+            for a in range(d_h):
+                val = sum(mp.e ** keys[j] / z *
+                          sum(M(w_uv[hh * d_h + a, b]) * M(c[j, b]) for b in range(d_c))
+                          for j in range(t + 1))
+                assert abs(float(val) - o[i, hh, a]) <= 1e-14 * max(1.0, abs(float(val)))
+
+
+# ---------------------------------------------------------------- library routine
+
+@pytest.mark.parametrize("s_q,L", [(1, 1), (1, 37), (2, 2), (2, 37), (3, 70)])
+def test_o2_matches_torch_sdpa(s_q, L):
+    ql, qr, c, kr = _small_decode(seed=L, s_q=s_q, L=L)
+    scale = 1.0 / math.sqrt(24)
+    o, lse = oracle.mqa_decode_rows(ql, qr, c, kr, scale)
+    q = torch.from_numpy(np.concatenate([ql, qr], -1)).permute(1, 0, 2)[None]   # [1,n_h,s_q,576']
+    k = torch.from_numpy(np.concatenate([c, kr], -1))[None, None].expand(1, ql.shape[1], -1, -1)
+    v = torch.from_numpy(c)[None, None].expand(1, ql.shape[1], -1, -1)
+    pos_q = torch.arange(L - s_q, L)[:, None]
+    mask = torch.arange(L)[None, :] <= pos_q                               # j <= t
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
+    ref = ref[0].permute(1, 0, 2).numpy()
+    assert np.max(np.abs(o - ref)) <= 1e-14
+    # lse from torch's logsumexp on the same masked scores
+    s = (q @ k.transpose(-1, -2)) * scale
+    s = s.masked_fill(~mask, float("-inf"))
+    ref_lse = torch.logsumexp(s, -1)[0].permute(1, 0).numpy()
+    assert np.max(np.abs(lse - ref_lse)) <= 1e-13
+
+
+def test_o1_matches_torch_sdpa_mha_mode():
+    """The MHA-mode layer's attention core equals torch's attention with
+    d_qk = d_h + d_r and d_v = d_h."""
+    W = inputs.toy_layer(seed=4, B=1, T=20, dtype=np.float64)
+    out = oracle.mha_mode_layer(W["h"], W, W["pos"])
+    dm = W["dims"]
+    n_h, d_h = dm["n_h"], dm["d_h"]
+    kc = (out["c_kv"][0] @ np.asarray(W["w_uk"]).T).reshape(20, n_h, d_h)
+    vc = (out["c_kv"][0] @ np.asarray(W["w_uv"]).T).reshape(20, n_h, d_h)
+    q = torch.from_numpy(np.concatenate([out["q_c"][0], out["q_r"][0]], -1)).permute(1, 0, 2)
+    kr = np.broadcast_to(out["k_r"][0][:, None, :], (20, n_h, dm["d_r"]))
+    k = torch.from_numpy(np.concatenate([kc, kr], -1)).permute(1, 0, 2)
+    v = torch.from_numpy(vc).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, is_causal=True, scale=1 / math.sqrt(d_h + dm["d_r"]))
+    assert np.max(np.abs(ref.permute(1, 0, 2).numpy() - out["o"][0])) <= 1e-14
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_single_key_returns_that_row():
+    ql, qr, c, kr = _small_decode(seed=1, s_q=1, L=1)
+    o, lse = oracle.mqa_decode_rows(ql, qr, c, kr, 0.3)
+    assert np.array_equal(o[0], np.broadcast_to(c[0], o[0].shape))
+    s0 = (np.einsum("hc,c->h", ql[0], c[0]) + np.einsum("hr,r->h", qr[0], kr[0])) * 0.3
+    assert np.max(np.abs(lse[0] - s0)) <= 1e-15 * max(1, np.max(np.abs(s0)))
+
+
+def test_zero_query_is_uniform_mean():
+    _, _, c, kr = _small_decode(seed=2, L=29)
+    s_q, n_h = 2, 4
+    o, lse = oracle.mqa_decode_rows(np.zeros((s_q, n_h, 16)), np.zeros((s_q, n_h, 8)), c, kr, 0.1)
+    for i in range(s_q):
+        vis = 29 - s_q + i + 1
+        assert np.max(np.abs(o[i] - c[:vis].mean(0))) <= 1e-15
+        assert np.max(np.abs(lse[i] - math.log(vis))) <= 1e-15
+
+
+def test_two_keys_sigmoid():
+    from scipy.special import expit
+    ql, qr, c, kr = _small_decode(seed=3, s_q=1, L=2)
+    scale = 0.25
+    o, _ = oracle.mqa_decode_rows(ql, qr, c, kr, scale)
+    s = (ql[0] @ c.T + qr[0] @ kr.T) * scale
+    w0 = expit(s[:, 0] - s[:, 1])
+    ref = w0[:, None] * c[0] + (1 - w0)[:, None] * c[1]
+    assert np.max(np.abs(o[0] - ref)) <= 1e-15
+
+
+def test_dominant_key():
+    ql, qr, c, kr = _small_decode(seed=4, s_q=1, L=9)
+    qr = np.zeros_like(qr)
+    ql = np.zeros_like(ql)
+    kr = np.zeros_like(kr)
+    kr[5, 0] = 1.0
+    qr[0, :, 0] = 1e4                    # key 5 scores 1e4*scale above every other
+    o, _ = oracle.mqa_decode_rows(ql, qr, c, kr, 1.0)
+    assert np.max(np.abs(o[0] - c[5])) <= 1e-12
+
+
+def test_softmax_rows_sum_to_one():
+    ql, qr, c, kr = _small_decode(seed=5, s_q=1, L=50)
+    p, _ = oracle.attention_probs(ql[0], qr[0], c, kr, 0.2, 50)
+    assert np.all(p >= 0)
+    assert np.max(np.abs(p.sum(-1) - 1)) <= 1e-15
+
+
+def test_causal_rows_differ_only_by_last_keys():
+    """s_q=2: the first new token must not see the second (j <= t)."""
+    ql, qr, c, kr = _small_decode(seed=6, s_q=2, L=10)
+    o, lse = oracle.mqa_decode_rows(ql, qr, c, kr, 0.3)
+    o0, l0 = oracle.mqa_decode_rows(ql[:1], qr[:1], c[:9], kr[:9], 0.3)
+    assert np.array_equal(o[0], o0[0]) and np.array_equal(lse[0], l0[0])
+
+
+# ---------------------------------------------------------------- RoPE
+
+def test_rope_is_complex_rotation():
+    rng = np.random.default_rng(0)
+    d, T = 32, 19
+    x = rng.standard_normal((T, d))
+    pos = np.arange(T) * 3 + 1
+    z = x[:, : d // 2] + 1j * x[:, d // 2:]
+    theta = np.power(10000.0, -np.arange(d // 2) * 2.0 / d)
+    zr = z * np.exp(1j * pos[:, None] * theta[None, :])
+    ref = np.concatenate([zr.real, zr.imag], -1)
+    assert np.max(np.abs(oracle.rope(x, pos) - ref)) <= 1e-13
+
+
+def test_rope_properties():
+    rng = np.random.default_rng(1)
+    d = 64
+    q, k = rng.standard_normal((1, d)), rng.standard_normal((1, d))
+    assert np.array_equal(oracle.rope(q, np.array([0])), q)
+    r = oracle.rope(q, np.array([1234]))
+    assert abs(np.linalg.norm(r) - np.linalg.norm(q)) <= 1e-12
+    # <R_m q, R_n k> depends only on m - n
+    def dot(m, n):
+        return float((oracle.rope(q, np.array([m])) @ oracle.rope(k, np.array([n])).T)[0, 0])
+    assert abs(dot(17, 5) - dot(112, 100)) <= 1e-12
+    assert abs(dot(17, 5) - float((oracle.rope(q, np.array([12])) @ k.T)[0, 0])) <= 1e-12
+
+
+# ---------------------------------------------------------------- split / combine / paging
+
+@pytest.mark.parametrize("cuts", [[0, 37], [0, 1, 37], [0, 10, 20, 30, 37], [0, 36, 36, 37]])
+def test_split_combine_equals_unsplit(cuts):
+    ql, qr, c, kr = _small_decode(seed=8, s_q=2, L=37)
+    full_o, full_l = oracle.mqa_decode_rows(ql, qr, c, kr, 0.2)
+    parts = [oracle.mqa_decode_rows(ql, qr, c, kr, 0.2, key_range=(a, b))
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    o, lse = oracle.combine_lse([p[0] for p in parts], [p[1] for p in parts])
+    assert np.max(np.abs(o - full_o)) <= 1e-14
+    assert np.max(np.abs(lse - full_l)) <= 1e-14
+
+
+def test_combine_all_empty():
+    o, lse = oracle.combine_lse(np.zeros((3, 2, 5)), np.full((3, 2), -np.inf))
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def test_paging_invariance():
+    a = inputs.decode_case(3, B=3, seq_lens=np.array([70, 128, 5]), n_h=4, d_c=16, d_r=8)
+    b = inputs.decode_case(3, B=3, seq_lens=np.array([70, 128, 5]), n_h=4, d_c=16, d_r=8)
+    # re-permute b's physical blocks
+    rng = np.random.default_rng(99)
+    perm = rng.permutation(b.num_blocks)
+    newc = np.empty_like(b.cache)
+    newc[perm] = b.cache
+    b.cache = newc
+    b.block_table = np.where(b.block_table >= 0, perm[np.maximum(b.block_table, 0)], -1)
+    oa, la = oracle.mqa_decode_case(a)
+    ob, lb = oracle.mqa_decode_case(b)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+# ---------------------------------------------------------------- storage formats
+
+def test_e4m3fn_decoder_matches_torch_and_format_facts():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3fn_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert ours[0x7E] == 448.0 and np.isnan(ours[0x7F]) and ours[0x38] == 1.0
+    assert ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6 and ours[0xB8] == -1.0
+
+
+def test_bf16_decoder_matches_torch():
+    bits = np.random.default_rng(0).integers(0, 2 ** 16, size=5000, dtype=np.uint16)
+    ours = oracle.bf16_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+
+
+def test_fp8_cache_roundtrip_error_bound():
+    case = inputs.decode_case(9, B=2, seq_lens=np.array([100, 64]), n_h=4, kv_dtype="fp8")
+    rng = np.random.Generator(np.random.PCG64(9))
+    rng.permutation(case.num_blocks)
+    rows = rng.standard_normal((case.num_blocks, 64, 576), dtype=np.float32)
+    for b in range(2):
+        L = int(case.seq_lens[b])
+        c, kr = oracle.paged_rows(case.cache, case.block_table[b], L, "fp8", 512, 64, 64)
+        logical = np.concatenate([rows[case.block_table[b, j]] for j in range((L + 63) // 64)])[:L]
+        x = logical[:, :512].astype(np.float64)
+        scale = np.abs(x).max(1) / 448.0
+        err = np.abs(c - x)
+        # e4m3 has 3 mantissa bits: half-ulp relative bound 2^-4 for normals,
+        # absolute bound 2^-10 * scale in the subnormal range; plus fp32 scale rounding
+        bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale[:, None]) * (1 + 1e-6)
+        assert np.all(err <= bound)
+        assert np.array_equal(kr, oracle.bf16_to_f64(inputs.f32_to_bf16_bits(logical[:, 512:])))
