@@ -1,0 +1,180 @@
+/*
+ * mla_decode.h -- C ABI of libmla.so: absorbed ("MQA mode") Multi-head Latent
+ * Attention decode on AMD Instinct MI355X (gfx950).
+ *
+ * The method (itwiki article "Multi-head latent attention", section
+ * "Structure"): each token caches only its compressed latent c^KV (d_c values)
+ * and one decoupled-RoPE key k^R (d_r values) shared by all heads.  In MQA
+ * mode the key up-projection W^UK is folded into the query, every head's
+ * latent query is dotted directly with the cached c^KV, the position term
+ * q^R . k^R is added, scores are scaled by 1/sqrt(d_h + d_h^R) and softmaxed
+ * causally, the softmax weights sum the c^KV rows, and W^UV is applied to that
+ * latent output afterwards.
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or retains memory; it keeps no state between calls
+ *    apart from a per-device cache of kernel attributes.
+ *  - Every call enqueues work on `stream` (a hipStream_t passed as void*; NULL
+ *    is the default stream) and returns without synchronising.
+ *  - Tensors are row-major with the last dimension contiguous.  Strides are
+ *    in elements.
+ *  - Return value: MLA_OK or a negative MLA_ERR_* code.  On an error return
+ *    nothing has been enqueued, except for MLA_ERR_LAUNCH, which reports a
+ *    failed kernel launch (hipGetLastError) and may leave earlier kernels of
+ *    the same call enqueued.
+ *  - Weights follow the nn.Linear storage convention [out, in]:
+ *    W^UK and W^UV are [n_h*d_h, d_c]; head i owns rows i*d_h .. (i+1)*d_h-1.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define MLA_F32 0      /* IEEE binary32 */
+#define MLA_BF16 1     /* bfloat16 */
+#define MLA_FP8_E4M3 2 /* OCP 8-bit float E4M3 ("fn": max 448, no infinities) */
+
+/* status codes */
+#define MLA_OK 0
+#define MLA_ERR_INVALID_ARG (-1) /* null pointer, non-positive size, bad dtype code */
+#define MLA_ERR_UNSUPPORTED (-2) /* valid but not implemented combination */
+#define MLA_ERR_MISALIGNED (-3)  /* a pointer/stride breaks the 16-byte alignment rule */
+#define MLA_ERR_WORKSPACE (-4)   /* workspace missing or smaller than required */
+#define MLA_ERR_LAUNCH (-5)      /* the HIP runtime rejected a kernel launch */
+
+/* flags for mla_decode_absorbed */
+#define MLA_FLAG_FORCE_GENERIC 1 /* use the portable fp32 kernel even when the
+                                    MFMA kernel applies (for cross-checks) */
+
+/*
+ * mla_absorb_q -- fold W^UK into the query (absorption identity
+ * q^T W^UK c = (W^UK^T q)^T c; itwiki "Multi-head latent attention", section
+ * "Matrix absorption"; lecture "MHA · GQA · MQA · MLA", section "Why
+ * Projection Absorption Helps").
+ *
+ *   q_lat[t, i, c] = sum_k q_nope[t, i, k] * w_uk[i*d_h + k, c]
+ *
+ *  q_nope  [T_q, n_h, d_h], token stride q_stride_t (>= n_h*d_h), dtype act_dtype
+ *  w_uk    [n_h*d_h, d_c],  dtype w_dtype
+ *  q_lat   [T_q, n_h, d_c], token stride qlat_stride_t (>= n_h*d_c), dtype out_dtype
+ *  act_dtype, w_dtype in {MLA_F32, MLA_BF16}; out_dtype in {MLA_F32, MLA_BF16}.
+ *  Accumulation is fp32.  bf16 activations and weights take the MFMA kernel
+ *  (needs d_h % 16 == 0, d_c % 32 == 0, 16-byte aligned rows); other
+ *  combinations take a plain fp32 kernel.  T_q == 0 is a no-op.
+ */
+int mla_absorb_q(const void* q_nope, int64_t q_stride_t, const void* w_uk, void* q_lat,
+                 int64_t qlat_stride_t, int T_q, int n_h, int d_h, int d_c, int act_dtype,
+                 int w_dtype, int out_dtype, void* stream);
+
+/*
+ * mla_decode_workspace_bytes -- size of the scratch buffer mla_decode_absorbed
+ * needs for the given batch shape (split-KV partial outputs, their
+ * log-sum-exps and the work list).  max_blocks_per_seq and num_splits as in
+ * mla_decode_absorbed.  Uses the current HIP device's compute-unit count.
+ * Returns 0 on invalid arguments.
+ */
+size_t mla_decode_workspace_bytes(int B, int s_q, int n_h, int d_c, int max_blocks_per_seq,
+                                  int num_splits);
+
+/*
+ * mla_decode_absorbed -- MQA-mode attention of s_q new tokens per sequence
+ * over a paged latent cache (itwiki "Multi-head latent attention", sections
+ * "Decoupled RoPE" and "Matrix absorption").
+ *
+ * For sequence b of length L = seq_lens[b], query token i (0 <= i < s_q)
+ * sits at position L - s_q + i and sees keys j = 0 .. L - s_q + i:
+ *   s[j]  = softmax_scale * (q_lat[b,i,h,:] . c_j + q_rope[b,i,h,:] . kR_j)
+ *   o_lat[b,i,h,:] = sum_j softmax(s)[j] * c_j
+ *   lse[b,i,h]     = log(sum_j exp(s[j]))          (natural log)
+ * The caller passes softmax_scale = 1/sqrt(d_h + d_h^R).
+ *
+ *  q_lat    [B, s_q, n_h, d_c], dtype q_dtype (MLA_BF16 or MLA_F32), contiguous
+ *  q_rope   [B, s_q, n_h, d_r], dtype q_dtype, contiguous
+ *  kv_cache paged cache, block_size tokens per block, physical block p at
+ *           byte offset p * block_bytes:
+ *           kv_dtype MLA_BF16 / MLA_F32: [num_blocks, block_size, d_c + d_r],
+ *             each token row = [c^KV | k^R];
+ *           kv_dtype MLA_FP8_E4M3: per block [block_size*d_c e4m3fn content |
+ *             block_size*d_r bf16 k^R | block_size fp32 per-token scales];
+ *             c_j = e4m3(code) * scale_j (the RoPE key stays bf16).
+ *  block_table [B, max_blocks_per_seq] int32: logical block k of sequence b
+ *           is physical block block_table[b*max_blocks_per_seq + k].
+ *  seq_lens [B] int32 (device).
+ *  o_lat    [B, s_q, n_h, d_c], dtype out_dtype (MLA_F32 or MLA_BF16).
+ *  lse      [B, s_q, n_h] fp32, or NULL.
+ *  num_splits  0 = automatic split-KV planning from the lengths and the
+ *           device's compute-unit count; k > 0 = each sequence is cut into
+ *           min(k, its block count) contiguous partitions, raised where a
+ *           partition would exceed 2048 blocks.
+ *  workspace   device buffer of at least mla_decode_workspace_bytes(...)
+ *           bytes; its contents need no initialisation and are clobbered.
+ *  flags    0 or MLA_FLAG_FORCE_GENERIC.
+ *
+ * Kernel selection: bf16 queries, bf16 or fp8 cache, n_h == 128, d_c == 512,
+ * d_r == 64, block_size == 64 and 16-byte aligned cache/query pointers take
+ * the MFMA kernel; everything else (fp32, other shapes) takes a portable
+ * fp32 kernel.  Constraints: 1 <= s_q <= 16, d_c <= 2048, d_r <= 256,
+ * d_c % 4 == 0.
+ * Device-side preconditions (not checked, they would need a synchronisation):
+ *   s_q <= seq_lens[b] <= max_blocks_per_seq*block_size, and every table
+ *   entry a sequence uses names a valid block.  Slots of the last block past
+ *   seq_lens[b] are never read into the result (they may hold NaN).
+ * Concurrent calls must use distinct workspaces.
+ */
+int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_cache,
+                        const int32_t* block_table, int max_blocks_per_seq,
+                        const int32_t* seq_lens, int B, int s_q, int n_h, int d_c, int d_r,
+                        int block_size, float softmax_scale, int q_dtype, int kv_dtype,
+                        int out_dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                        void* o_lat, float* lse, int flags, void* stream);
+
+/*
+ * mla_combine_lse -- merge split-KV partial results (log-sum-exp combine):
+ *   lse[n] = log sum_s exp(lse_part[n,s]),
+ *   out[n,:] = sum_s exp(lse_part[n,s] - lse[n]) * o_part[n,s,:]
+ * Each o_part[n,s,:] is normalised over its own keys.  Splits with
+ * lse_part = -inf carry no weight; a row whose splits are all -inf gets
+ * out = 0, lse = -inf.
+ *
+ *  o_part   [N, S, D] fp32
+ *  lse_part [N, S] fp32
+ *  splits_per_row [N] int32 (device) with 0 <= value <= S, or NULL for S
+ *  out      [N, D], dtype out_dtype (MLA_F32 or MLA_BF16)
+ *  lse_out  [N] fp32, or NULL
+ *  Requires D % 4 == 0 and 16-byte aligned o_part/out.  N == 0 is a no-op.
+ */
+int mla_combine_lse(const float* o_part, const float* lse_part, const int32_t* splits_per_row,
+                    int N, int S, int D, void* out, float* lse_out, int out_dtype, void* stream);
+
+/*
+ * mla_up_proj_v -- apply W^UV after the weighted latent sum (itwiki
+ * "Multi-head latent attention", section "Matrix absorption"):
+ *
+ *   o[t, i, k] = sum_c w_uv[i*d_h + k, c] * o_lat[t, i, c]
+ *
+ *  o_lat [T_q, n_h, d_c], token stride olat_stride_t, dtype act_dtype
+ *  w_uv  [n_h*d_h, d_c], dtype w_dtype
+ *  o     [T_q, n_h, d_h], token stride o_stride_t, dtype out_dtype
+ *  bf16 activations and weights take the MFMA kernel (needs d_c % 16 == 0,
+ *  d_h % 32 == 0, 16-byte aligned rows); other combinations a plain fp32
+ *  kernel.  Accumulation is fp32.  T_q == 0 is a no-op.
+ */
+int mla_up_proj_v(const void* o_lat, int64_t olat_stride_t, const void* w_uv, void* o,
+                  int64_t o_stride_t, int T_q, int n_h, int d_c, int d_h, int act_dtype,
+                  int w_dtype, int out_dtype, void* stream);
+
+/* mla_status_string -- static, human-readable text for a status code. */
+const char* mla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,203 @@
+// C ABI of libmla.so: argument validation, kernel selection and launch.
+// Declarations and contracts: include/mla_decode.h.
+#include "mla_decode.h"
+#include "mla_internal.h"
+
+#include <atomic>
+
+namespace mla {
+int mfma_max_unit_pages();
+}
+
+using namespace mla;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// compute units of the current device (cached; 0 on failure)
+int current_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    int v = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool act_dtype_ok(int d) { return d == MLA_F32 || d == MLA_BF16; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
+
+struct DecodeShape {
+  int B, s_q, n_h, d_c, d_r, block_size, max_blocks, num_splits;
+};
+
+bool mfma_eligible(const DecodeShape& s, int q_dtype, int kv_dtype) {
+  return q_dtype == MLA_BF16 && (kv_dtype == MLA_BF16 || kv_dtype == MLA_FP8_E4M3) && s.n_h == 128 &&
+         s.d_c == 512 && s.d_r == 64 && s.block_size == 64;
+}
+
+// upper bound on planned units for this shape
+WsLayout layout_for(const DecodeShape& s, int n_cu) {
+  WsLayout L = ws_layout(s.B, s.s_q, s.n_h, s.d_c, s.num_splits, n_cu);
+  // partitions are capped at mfma_max_unit_pages() pages
+  const long long cap = mfma_max_unit_pages();
+  const long long per_seq_min = (s.max_blocks + cap - 1) / cap;
+  const long long need = (long long)s.B * per_seq_min;
+  if (need > L.units_max) {
+    WsLayout M = ws_layout(s.B, s.s_q, s.n_h, s.d_c, (int)per_seq_min, n_cu);
+    if (M.total > L.total) L = M;
+  }
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument (null pointer, bad size or dtype code)";
+    case MLA_ERR_UNSUPPORTED: return "unsupported combination of shapes/dtypes";
+    case MLA_ERR_MISALIGNED: return "pointer or stride is not 16-byte aligned";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int mla_absorb_q(const void* q_nope, int64_t q_stride_t, const void* w_uk, void* q_lat,
+                 int64_t qlat_stride_t, int T_q, int n_h, int d_h, int d_c, int act_dtype, int w_dtype,
+                 int out_dtype, void* stream) {
+  if (T_q < 0 || n_h <= 0 || d_h <= 0 || d_c <= 0) return MLA_ERR_INVALID_ARG;
+  if (!act_dtype_ok(act_dtype) || !act_dtype_ok(w_dtype) || !act_dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
+  if (T_q == 0) return MLA_OK;
+  if (!q_nope || !w_uk || !q_lat) return MLA_ERR_INVALID_ARG;
+  if (q_stride_t < (int64_t)n_h * d_h || qlat_stride_t < (int64_t)n_h * d_c) return MLA_ERR_INVALID_ARG;
+  const bool mfma = act_dtype == MLA_BF16 && w_dtype == MLA_BF16;
+  if (mfma) {
+    if (d_h % 16 != 0 || d_c % 32 != 0) return MLA_ERR_UNSUPPORTED;
+    if (!aligned16(q_nope) || !aligned16(w_uk) || q_stride_t % 8 != 0) return MLA_ERR_MISALIGNED;
+  }
+  return launch_status(launch_absorb(q_nope, q_stride_t, w_uk, q_lat, qlat_stride_t, T_q, n_h, d_h, d_c,
+                                     act_dtype, w_dtype, out_dtype, mfma, (hipStream_t)stream));
+}
+
+int mla_up_proj_v(const void* o_lat, int64_t olat_stride_t, const void* w_uv, void* o, int64_t o_stride_t,
+                  int T_q, int n_h, int d_c, int d_h, int act_dtype, int w_dtype, int out_dtype,
+                  void* stream) {
+  if (T_q < 0 || n_h <= 0 || d_h <= 0 || d_c <= 0) return MLA_ERR_INVALID_ARG;
+  if (!act_dtype_ok(act_dtype) || !act_dtype_ok(w_dtype) || !act_dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
+  if (T_q == 0) return MLA_OK;
+  if (!o_lat || !w_uv || !o) return MLA_ERR_INVALID_ARG;
+  if (olat_stride_t < (int64_t)n_h * d_c || o_stride_t < (int64_t)n_h * d_h) return MLA_ERR_INVALID_ARG;
+  const bool mfma = act_dtype == MLA_BF16 && w_dtype == MLA_BF16;
+  if (mfma) {
+    if (d_c % 16 != 0 || d_h % 32 != 0) return MLA_ERR_UNSUPPORTED;
+    if (!aligned16(o_lat) || !aligned16(w_uv) || olat_stride_t % 8 != 0) return MLA_ERR_MISALIGNED;
+  }
+  return launch_status(launch_up_proj(o_lat, olat_stride_t, w_uv, o, o_stride_t, T_q, n_h, d_c, d_h,
+                                      act_dtype, w_dtype, out_dtype, mfma, (hipStream_t)stream));
+}
+
+size_t mla_decode_workspace_bytes(int B, int s_q, int n_h, int d_c, int max_blocks_per_seq, int num_splits) {
+  if (B <= 0 || s_q <= 0 || n_h <= 0 || d_c <= 0 || max_blocks_per_seq <= 0 || num_splits < 0) return 0;
+  const int n_cu = current_cu_count();
+  if (n_cu <= 0) return 0;
+  DecodeShape s{B, s_q, n_h, d_c, 0, 0, max_blocks_per_seq, num_splits};
+  return layout_for(s, n_cu).total;
+}
+
+int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_cache, const int32_t* block_table,
+                        int max_blocks_per_seq, const int32_t* seq_lens, int B, int s_q, int n_h, int d_c,
+                        int d_r, int block_size, float softmax_scale, int q_dtype, int kv_dtype, int out_dtype,
+                        int num_splits, void* workspace, size_t workspace_bytes, void* o_lat, float* lse,
+                        int flags, void* stream) {
+  if (B <= 0 || s_q <= 0 || n_h <= 0 || d_c <= 0 || d_r < 0 || block_size <= 0 || max_blocks_per_seq <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (num_splits < 0 || (flags & ~MLA_FLAG_FORCE_GENERIC)) return MLA_ERR_INVALID_ARG;
+  if (!act_dtype_ok(q_dtype) || !act_dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
+  if (kv_dtype != MLA_F32 && kv_dtype != MLA_BF16 && kv_dtype != MLA_FP8_E4M3) return MLA_ERR_INVALID_ARG;
+  if (!q_lat || !kv_cache || !block_table || !seq_lens || !o_lat) return MLA_ERR_INVALID_ARG;
+  if (d_r > 0 && !q_rope) return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return MLA_ERR_INVALID_ARG;
+  if (s_q > 16 || d_c > 2048 || d_r > 256 || d_c % 4 != 0) return MLA_ERR_UNSUPPORTED;
+  if (kv_dtype == MLA_FP8_E4M3 && (d_r % 8 != 0 || d_c % 16 != 0)) return MLA_ERR_UNSUPPORTED;
+  if (!aligned16(o_lat)) return MLA_ERR_MISALIGNED;
+  if (!workspace) return MLA_ERR_WORKSPACE;
+
+  const int n_cu = current_cu_count();
+  if (n_cu <= 0) return MLA_ERR_LAUNCH;
+  DecodeShape shp{B, s_q, n_h, d_c, d_r, block_size, max_blocks_per_seq, num_splits};
+  const WsLayout L = layout_for(shp, n_cu);
+  if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_MISALIGNED;
+
+  bool fast = !(flags & MLA_FLAG_FORCE_GENERIC) && mfma_eligible(shp, q_dtype, kv_dtype);
+  if (fast && (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(kv_cache))) fast = false;
+
+  uint8_t* ws = (uint8_t*)workspace;
+  DecodeArgs a{};
+  a.q_lat = q_lat;
+  a.q_rope = q_rope;
+  a.kv = kv_cache;
+  a.table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = o_lat;
+  a.lse = lse;
+  a.ws_header = (int*)ws;
+  a.work = (const int4*)(ws + L.work);
+  a.seq = (const int2*)(ws + L.seq);
+  a.lse_part = (float*)(ws + L.lse_part);
+  a.o_part = (float*)(ws + L.o_part);
+  const long long elem = kv_dtype == MLA_F32 ? 4 : 2;
+  a.block_bytes = kv_dtype == MLA_FP8_E4M3 ? (long long)block_size * (d_c + 2 * d_r + 4)
+                                           : (long long)block_size * (d_c + d_r) * elem;
+  a.max_blocks = max_blocks_per_seq;
+  a.B = B; a.s_q = s_q; a.n_h = n_h; a.d_c = d_c; a.d_r = d_r; a.block_size = block_size;
+  a.scale = softmax_scale;
+  a.q_dtype = q_dtype; a.kv_dtype = kv_dtype; a.out_dtype = out_dtype;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int grid_x = fast ? (n_cu / s_q > 0 ? n_cu / s_q : 1) : (L.units_max < n_cu ? L.units_max : n_cu);
+
+  PlanArgs p{};
+  p.seq_lens = seq_lens;
+  p.ws_header = (int*)ws;
+  p.work = (int4*)(ws + L.work);
+  p.seq = (int2*)(ws + L.seq);
+  p.B = B;
+  p.block_size = block_size;
+  p.num_splits = num_splits;
+  p.slots_per_wave = grid_x;
+  p.min_chunk = fast ? 8 : 4;
+  p.max_chunk = mfma_max_unit_pages();
+  p.units_max = L.units_max;
+  hipError_t e = launch_plan(p, st);
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  e = fast ? launch_decode_mfma(a, grid_x, st) : launch_decode_generic(a, grid_x, st);
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  e = launch_combine_units(a, st);
+  return launch_status(e);
+}
+
+int mla_combine_lse(const float* o_part, const float* lse_part, const int32_t* splits_per_row, int N, int S,
+                    int D, void* out, float* lse_out, int out_dtype, void* stream) {
+  if (N < 0 || S <= 0 || D <= 0 || !act_dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
+  if (D % 4 != 0) return MLA_ERR_UNSUPPORTED;
+  if (N == 0) return MLA_OK;
+  if (!o_part || !lse_part || !out) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(o_part) || !aligned16(out)) return MLA_ERR_MISALIGNED;
+  return launch_status(launch_combine_lse(o_part, lse_part, splits_per_row, N, S, D, out, lse_out, out_dtype,
+                                          (hipStream_t)stream));
+}
+
+}  // extern "C"

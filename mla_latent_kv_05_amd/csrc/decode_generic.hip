@@ -1,0 +1,359 @@
+// Split planning, the portable fp32 decode kernel, and the log-sum-exp combine.
+//
+// Method: itwiki "Multi-head latent attention", sections "Decoupled RoPE" and
+// "Matrix absorption" -- in MQA mode each head's latent query is dotted with
+// the cached c^KV, the RoPE term q^R.k^R is added, scores are scaled by
+// 1/sqrt(d_h + d_h^R), softmaxed over the keys j <= t, and the weights sum
+// the c^KV rows.  Split-KV partitions and their log-sum-exp merge are this
+// library's mechanism for spreading one sequence over many compute units.
+#include "device_util.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+// ============================================================== planner
+// One workgroup.  Cuts each sequence into contiguous block ranges ("units").
+// Automatic mode picks the partition length c (in blocks) that minimises
+// an estimated makespan  waves(c) * (c + overhead)  over 1..kMaxAutoWaves
+// waves of `slots_per_wave` concurrent units, where overhead stands for the
+// partial-result write and merge of a split sequence.
+
+constexpr int kPlanThreads = 1024;
+
+__device__ int block_sum(int v, int* red) {
+  int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  int t = 0;
+  for (int i = 0; i < kPlanThreads / 64; ++i) t += red[i];
+  return t;
+}
+
+__device__ int block_max(int v, int* red) {
+  int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  int t = 0;
+  for (int i = 0; i < kPlanThreads / 64; ++i) t = max(t, red[i]);
+  return t;
+}
+
+__device__ __forceinline__ int nblocks_of(const PlanArgs& a, int b) {
+  int L = a.seq_lens[b];
+  int n = (L + a.block_size - 1) / a.block_size;
+  return n < 1 ? 1 : n;
+}
+
+__device__ int units_for_chunk(const PlanArgs& a, int c, int* red) {
+  int cnt = 0;
+  for (int b = threadIdx.x; b < a.B; b += kPlanThreads) cnt += (nblocks_of(a, b) + c - 1) / c;
+  return block_sum(cnt, red);
+}
+
+// partitions of a sequence with n blocks: explicit count (raised where a
+// partition would exceed max_chunk blocks) or ceil(n / chunk)
+__device__ __forceinline__ int units_of(const PlanArgs& a, int n, int chunk) {
+  if (a.num_splits > 0) {
+    int u = min(a.num_splits, n);
+    int need = (n + a.max_chunk - 1) / a.max_chunk;
+    return max(u, need);
+  }
+  return (n + chunk - 1) / chunk;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ int red[kPlanThreads / 64];
+  __shared__ int scan[kPlanThreads];
+  const int tid = threadIdx.x;
+
+  int chunk = 0, waves = 1;
+  if (a.num_splits <= 0) {
+    int max_n = 0;
+    for (int b = tid; b < a.B; b += kPlanThreads) max_n = max(max_n, nblocks_of(a, b));
+    max_n = block_max(max_n, red);
+    const int overhead = 4;
+    long long best_cost = -1;
+    for (int k = 1; k <= kMaxAutoWaves; ++k) {
+      int target = k * a.slots_per_wave;
+      int hi = min(max_n, a.max_chunk);
+      int lo = min(a.min_chunk, hi);
+      if (lo < 1) lo = 1;
+      // smallest c in [lo, hi] with units(c) <= target (hi always qualifies or is the floor)
+      while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        if (units_for_chunk(a, mid, red) <= target) hi = mid; else lo = mid + 1;
+      }
+      int c = lo;
+      int u = units_for_chunk(a, c, red);
+      int w = (u + a.slots_per_wave - 1) / a.slots_per_wave;
+      long long cost = (long long)w * (c + (u > a.B ? overhead : 0));
+      if (best_cost < 0 || cost < best_cost) { best_cost = cost; chunk = c; waves = w; }
+    }
+  }
+
+  // per-thread run of consecutive sequences for the prefix sum
+  const int per = (a.B + kPlanThreads - 1) / kPlanThreads;
+  const int b0 = tid * per, b1 = min(a.B, b0 + per);
+  int local = 0;
+  for (int b = b0; b < b1; ++b) {
+    int n = nblocks_of(a, b);
+    local += units_of(a, n, chunk);
+  }
+  scan[tid] = local;
+  __syncthreads();
+  for (int o = 1; o < kPlanThreads; o <<= 1) {
+    int v = tid >= o ? scan[tid - o] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  int first = scan[tid] - local;
+  for (int b = b0; b < b1; ++b) {
+    int n = nblocks_of(a, b);
+    int u = units_of(a, n, chunk);
+    int len = (n + u - 1) / u;
+    a.seq[b] = make_int2(first, u);
+    for (int k = 0; k < u; ++k) {
+      int s0 = k * len, s1 = min(n, s0 + len);
+      a.work[first + k] = make_int4(b, s0, s1, u > 1 ? first + k : -1);
+    }
+    first += u;
+  }
+  if (tid == kPlanThreads - 1) {
+    WsHeader* h = (WsHeader*)a.ws_header;
+    h->n_units = scan[tid];
+    h->chunk_blocks = chunk;
+    h->waves = waves;
+  }
+}
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// ============================================================== generic decode
+// One wavefront per query row (query token i, head h), exact online softmax
+// token by token in fp32.  Lanes split the d_c + d_r dimensions.  Any shapes
+// within the ABI limits, fp32 / bf16 / fp8 caches.
+
+constexpr int kMaxQ = 36;  // (2048 + 256) / 64
+constexpr int kMaxC = 32;  // 2048 / 64
+
+template <int KV>
+__device__ __forceinline__ void load_kv_row(const DecodeArgs& a, const uint8_t* blk, int slot,
+                                            int lane, int nc, float* cv, float* kr_out) {
+  // content dims lane + 64k (k < nc) and RoPE dims lane + 64k (k < 4)
+  if (KV == 2) {  // fp8: [bs*d_c codes | bs*d_r bf16 | bs fp32 scale]
+    const uint8_t* codes = blk + (size_t)slot * a.d_c;
+    const uint16_t* kr = (const uint16_t*)(blk + (size_t)a.block_size * a.d_c) + (size_t)slot * a.d_r;
+    const float sc = ((const float*)(blk + (size_t)a.block_size * (a.d_c + 2 * a.d_r)))[slot];
+#pragma unroll
+    for (int k = 0; k < kMaxC; ++k) {
+      int d = lane + 64 * k;
+      cv[k] = (k < nc && d < a.d_c) ? e4m3fn_to_f32(codes[d]) * sc : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      int d = lane + 64 * k;
+      kr_out[k] = d < a.d_r ? bf16_bits_to_f32(kr[d]) : 0.f;
+    }
+  } else {
+    const size_t row = (size_t)slot * (a.d_c + a.d_r);
+#pragma unroll
+    for (int k = 0; k < kMaxC; ++k) {
+      int d = lane + 64 * k;
+      cv[k] = (k < nc && d < a.d_c) ? load_elem(blk, row + d, KV) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      int d = lane + 64 * k;
+      kr_out[k] = d < a.d_r ? load_elem(blk, row + a.d_c + d, KV) : 0.f;
+    }
+  }
+}
+
+template <int KV>
+__global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int R = a.s_q * a.n_h;
+  const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const int qi = r / a.n_h, h = r % a.n_h;
+  const int nc = (a.d_c + 63) / 64;
+  const int n_units = ((const WsHeader*)a.ws_header)->n_units;
+
+  for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+    const int4 wk = a.work[unit];
+    const int b = wk.x;
+    const int L = a.seq_lens[b];
+    const int vis = L - a.s_q + qi + 1;
+    const int t0 = wk.y * a.block_size;
+    const int t1 = min(wk.z * a.block_size, vis);
+
+    const long long qrow = ((long long)b * a.s_q + qi) * a.n_h + h;
+    float qc[kMaxC], qr[4], acc[kMaxC];
+#pragma unroll
+    for (int k = 0; k < kMaxC; ++k) {
+      int d = lane + 64 * k;
+      qc[k] = (k < nc && d < a.d_c) ? load_elem(a.q_lat, qrow * a.d_c + d, a.q_dtype) : 0.f;
+      acc[k] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      int d = lane + 64 * k;
+      qr[k] = d < a.d_r ? load_elem(a.q_rope, qrow * a.d_r + d, a.q_dtype) : 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+    for (int j = t0; j < t1; ++j) {
+      const int pb = a.table[(long long)b * a.max_blocks + j / a.block_size];
+      const uint8_t* blk = (const uint8_t*)a.kv + (long long)pb * a.block_bytes;
+      float cv[kMaxC], kr[4];
+      load_kv_row<KV>(a, blk, j % a.block_size, lane, nc, cv, kr);
+      float part = 0.f;
+#pragma unroll
+      for (int k = 0; k < kMaxC; ++k)
+        if (k < nc) part += qc[k] * cv[k];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) part += qr[k] * kr[k];
+      const float s = wave_sum(part) * a.scale;
+      const float m_new = fmaxf(m, s);
+      const float f = expf(m - m_new);  // m = -inf -> 0
+      const float p = expf(s - m_new);
+      l = l * f + p;
+#pragma unroll
+      for (int k = 0; k < kMaxC; ++k)
+        if (k < nc) acc[k] = acc[k] * f + p * cv[k];
+      m = m_new;
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float lse_v = l > 0.f ? m + logf(l) : -INFINITY;
+    if (wk.w < 0) {
+#pragma unroll
+      for (int k = 0; k < kMaxC; ++k) {
+        int d = lane + 64 * k;
+        if (k < nc && d < a.d_c) store_elem(a.out, qrow * a.d_c + d, acc[k] * inv, a.out_dtype);
+      }
+      if (lane == 0 && a.lse) a.lse[qrow] = lse_v;
+    } else {
+      const long long prow = (long long)wk.w * R + r;
+#pragma unroll
+      for (int k = 0; k < kMaxC; ++k) {
+        int d = lane + 64 * k;
+        if (k < nc && d < a.d_c) a.o_part[prow * a.d_c + d] = acc[k] * inv;
+      }
+      if (lane == 0) a.lse_part[prow] = lse_v;
+    }
+  }
+}
+
+hipError_t launch_decode_generic(const DecodeArgs& a, int units_max, hipStream_t s) {
+  const int R = a.s_q * a.n_h;
+  dim3 grid(units_max < 1024 ? units_max : 1024, (R + 3) / 4);
+  if (a.kv_dtype == 0)
+    hipLaunchKernelGGL(decode_generic_kernel<0>, grid, dim3(256), 0, s, a);
+  else if (a.kv_dtype == 1)
+    hipLaunchKernelGGL(decode_generic_kernel<1>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_generic_kernel<2>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ============================================================== combine
+// lse = log sum_s exp(lse_s); out = sum_s exp(lse_s - lse) o_s.  One thread
+// per 4 output values.
+
+__device__ __forceinline__ void merge_row(const float* o_base, long long o_stride,
+                                          const float* l_base, long long l_stride, int S,
+                                          int c4, float4& out, float& lse_out) {
+  float m = -INFINITY;
+  for (int k = 0; k < S; ++k) m = fmaxf(m, l_base[k * l_stride]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float z = 0.f;
+  if (m != -INFINITY) {
+    for (int k = 0; k < S; ++k) {
+      const float w = expf(l_base[k * l_stride] - m);
+      if (w == 0.f) continue;  // an empty split may hold anything in o
+      const float4 v = ((const float4*)(o_base + k * o_stride))[c4];
+      acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+      z += w;
+    }
+  }
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  out = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  lse_out = z > 0.f ? m + logf(z) : -INFINITY;
+}
+
+__device__ __forceinline__ void store4(void* out, long long base, float4 v, int dt) {
+  if (dt == 0) {
+    *(float4*)((float*)out + base) = v;
+  } else {
+    uint16_t* o = (uint16_t*)out + base;
+    uint2 pk;
+    pk.x = (uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16);
+    pk.y = (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16);
+    *(uint2*)o = pk;
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_units_kernel(DecodeArgs a) {
+  const int bq = blockIdx.y;
+  const int b = bq / a.s_q, qi = bq % a.s_q;
+  const int2 sq = a.seq[b];
+  if (sq.y <= 1) return;
+  const int d4 = a.d_c / 4;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int h = idx / d4, c4 = idx % d4;
+  if (h >= a.n_h) return;
+  const int R = a.s_q * a.n_h;
+  const int r = qi * a.n_h + h;
+  const long long prow = (long long)sq.x * R + r;
+  float4 o;
+  float lse_v;
+  merge_row(a.o_part + prow * a.d_c, (long long)R * a.d_c, a.lse_part + prow, R, sq.y, c4, o,
+            lse_v);
+  const long long orow = ((long long)b * a.s_q + qi) * a.n_h + h;
+  store4(a.out, orow * a.d_c + 4 * c4, o, a.out_dtype);
+  if (c4 == 0 && a.lse) a.lse[orow] = lse_v;
+}
+
+hipError_t launch_combine_units(const DecodeArgs& a, hipStream_t s) {
+  const int per = a.n_h * (a.d_c / 4);
+  dim3 grid((per + 255) / 256, a.B * a.s_q);
+  hipLaunchKernelGGL(combine_units_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void combine_lse_kernel(const float* o_part, const float* lse_part,
+                                                          const int32_t* splits, int N, int S, int D,
+                                                          void* out, float* lse_out, int out_dt) {
+  const int d4 = D / 4;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)N * d4) return;
+  const int n = (int)(idx / d4), c4 = (int)(idx % d4);
+  int cnt = splits ? splits[n] : S;
+  cnt = cnt < 0 ? 0 : (cnt > S ? S : cnt);
+  float4 o;
+  float lse_v;
+  merge_row(o_part + (long long)n * S * D, D, lse_part + (long long)n * S, 1, cnt, c4, o, lse_v);
+  store4(out, (long long)n * D + 4 * c4, o, out_dt);
+  if (c4 == 0 && lse_out) lse_out[n] = lse_v;
+}
+
+hipError_t launch_combine_lse(const float* o_part, const float* lse_part, const int32_t* splits,
+                              int N, int S, int D, void* out, float* lse_out, int out_dtype,
+                              hipStream_t s) {
+  long long total = (long long)N * (D / 4);
+  dim3 grid((unsigned)((total + 255) / 256));
+  hipLaunchKernelGGL(combine_lse_kernel, grid, dim3(256), 0, s, o_part, lse_part, splits, N, S, D,
+                     out, lse_out, out_dtype);
+  return hipGetLastError();
+}
+
+}  // namespace mla

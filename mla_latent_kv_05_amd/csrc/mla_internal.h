@@ -1,0 +1,101 @@
+// Internal declarations shared by the HIP translation units of libmla.so.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// ---------------------------------------------------------------- workspace
+// Layout of the decode workspace (all offsets 256-byte aligned):
+//   [0]           WsHeader
+//   work          int4[units_max]    (b, first_block, end_block, slot)
+//   seq           int2[B]            (first unit, unit count)
+//   lse_part      float[units_max * R]
+//   o_part        float[units_max * R * d_c]
+// with R = s_q * n_h rows per sequence.  slot = -1 marks a sequence that has
+// a single unit: that unit writes the final output directly.
+struct WsHeader {
+  int n_units;
+  int chunk_blocks;  // planned partition length in blocks (diagnostic)
+  int waves;         // planned waves of units (diagnostic)
+  int pad[61];
+};
+
+struct WsLayout {
+  size_t work, seq, lse_part, o_part, total;
+  int units_max;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Upper bound on work units: explicit splits -> B*splits; automatic planning
+// -> up to `max_waves` waves of `slots` units plus one rounding unit per sequence.
+constexpr int kMaxAutoWaves = 3;
+
+inline WsLayout ws_layout(int B, int s_q, int n_h, int d_c, int num_splits, int n_cu) {
+  WsLayout L{};
+  long long units;
+  if (num_splits > 0)
+    units = (long long)B * num_splits;
+  else
+    units = (long long)kMaxAutoWaves * n_cu + B;
+  L.units_max = (int)units;
+  size_t R = (size_t)s_q * n_h;
+  size_t off = align256(sizeof(WsHeader));
+  L.work = off; off = align256(off + (size_t)units * 16);
+  L.seq = off; off = align256(off + (size_t)B * 8);
+  L.lse_part = off; off = align256(off + (size_t)units * R * 4);
+  L.o_part = off; off = align256(off + (size_t)units * R * d_c * 4);
+  L.total = off;
+  return L;
+}
+
+// ---------------------------------------------------------------- parameters
+struct DecodeArgs {
+  const void* q_lat;
+  const void* q_rope;
+  const void* kv;
+  const int32_t* table;
+  const int32_t* seq_lens;
+  void* out;
+  float* lse;
+  int* ws_header;  // -> WsHeader
+  const int4* work;
+  const int2* seq;
+  float* lse_part;
+  float* o_part;
+  long long block_bytes;
+  int max_blocks;
+  int B, s_q, n_h, d_c, d_r, block_size;
+  float scale;
+  int q_dtype, kv_dtype, out_dtype;
+};
+
+struct PlanArgs {
+  const int32_t* seq_lens;
+  int* ws_header;
+  int4* work;
+  int2* seq;
+  int B, block_size, num_splits;
+  int slots_per_wave;  // concurrent units per wave of the decode kernel
+  int min_chunk;       // smallest partition (blocks) automatic planning uses
+  int max_chunk;       // largest partition (blocks) any unit may have
+  int units_max;
+};
+
+// launchers (return hipError_t of the launch)
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_decode_generic(const DecodeArgs& a, int units_max, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t s);
+hipError_t launch_combine_units(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine_lse(const float* o_part, const float* lse_part, const int32_t* splits,
+                              int N, int S, int D, void* out, float* lse_out, int out_dtype,
+                              hipStream_t s);
+hipError_t launch_absorb(const void* q, long long q_st, const void* w, void* out, long long o_st,
+                         int T, int n_h, int d_h, int d_c, int act_dt, int w_dt, int out_dt,
+                         bool mfma, hipStream_t s);
+hipError_t launch_up_proj(const void* o_lat, long long a_st, const void* w, void* out,
+                          long long o_st, int T, int n_h, int d_c, int d_h, int act_dt,
+                          int w_dt, int out_dt, bool mfma, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,101 @@
+"""Host-side checks of libmla.so that need no GPU: the library loads, exports
+every function include/mla_decode.h declares, and rejects invalid arguments
+with the documented status codes before touching the device."""
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from mla_latent_kv_05_amd import binding
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
+                                reason="libmla.so not built (python -m mla_latent_kv_05_amd.build)")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE = 0, -1, -2, -3, -4
+
+
+def test_header_functions_exported():
+    names = binding.header_functions()
+    assert set(names) == {"mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_absorbed",
+                          "mla_combine_lse", "mla_up_proj_v", "mla_status_string"}
+    L = binding.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert f" T {n}" in out, n
+
+
+def test_library_is_gfx950_code():
+    """The embedded device code bundle targets gfx950 (and nothing else)."""
+    blob = open(binding.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+    for other in (b"--gfx942", b"--gfx90a", b"--gfx1100"):
+        assert other not in blob
+
+
+def test_status_strings():
+    for code in (OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, -5):
+        s = binding.status_string(code)
+        assert s and s != "unknown status"
+    assert binding.status_string(12345) == "unknown status"
+
+
+FAKE = 0x1000  # never dereferenced: validation fails before any device access
+
+
+def _decode(**over):
+    a = dict(q_lat=FAKE, q_rope=FAKE, kv=FAKE, table=FAKE, max_blocks=4, lens=FAKE, B=2, s_q=1, n_h=128, d_c=512,
+             d_r=64, bs=64, scale=0.072, qdt=1, kvdt=1, odt=1, splits=0, ws=FAKE, ws_bytes=1 << 30, out=FAKE,
+             lse=None, flags=0)
+    a.update(over)
+    return binding.lib().mla_decode_absorbed(a["q_lat"], a["q_rope"], a["kv"], a["table"], a["max_blocks"],
+                                             a["lens"], a["B"], a["s_q"], a["n_h"], a["d_c"], a["d_r"], a["bs"],
+                                             a["scale"], a["qdt"], a["kvdt"], a["odt"], a["splits"], a["ws"],
+                                             a["ws_bytes"], a["out"], a["lse"], a["flags"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q_lat=None), INVALID), (dict(kv=None), INVALID), (dict(table=None), INVALID),
+    (dict(lens=None), INVALID), (dict(out=None), INVALID), (dict(q_rope=None), INVALID),
+    (dict(B=0), INVALID), (dict(s_q=0), INVALID), (dict(n_h=-1), INVALID), (dict(bs=0), INVALID),
+    (dict(max_blocks=0), INVALID), (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(qdt=2), INVALID), (dict(kvdt=7), INVALID), (dict(odt=2), INVALID), (dict(splits=-1), INVALID),
+    (dict(flags=8), INVALID), (dict(s_q=17), UNSUPPORTED), (dict(d_c=4096), UNSUPPORTED),
+    (dict(d_c=510), UNSUPPORTED), (dict(d_r=300), UNSUPPORTED), (dict(kvdt=2, d_r=60), UNSUPPORTED),
+    (dict(out=FAKE + 4), MISALIGNED), (dict(ws=None), WORKSPACE),
+])
+def test_decode_argument_validation(over, code):
+    assert _decode(**over) == code
+
+
+def test_projection_argument_validation():
+    L = binding.lib()
+    # absorb: T_q=0 is a no-op even with null pointers
+    assert L.mla_absorb_q(None, 0, None, None, 0, 0, 128, 128, 512, 1, 1, 1, None) == OK
+    assert L.mla_absorb_q(None, 16384, FAKE, FAKE, 65536, 4, 128, 128, 512, 1, 1, 1, None) == INVALID
+    assert L.mla_absorb_q(FAKE, 100, FAKE, FAKE, 65536, 4, 128, 128, 512, 1, 1, 1, None) == INVALID  # stride
+    assert L.mla_absorb_q(FAKE, 16384, FAKE, FAKE, 65536, 4, 128, 128, 512, 2, 1, 1, None) == INVALID  # dtype
+    assert L.mla_absorb_q(FAKE, 16384, FAKE, FAKE, 65536, 4, 128, 120, 512, 1, 1, 1, None) == UNSUPPORTED
+    assert L.mla_absorb_q(FAKE + 2, 16384, FAKE, FAKE, 65536, 4, 128, 128, 512, 1, 1, 1, None) == MISALIGNED
+    assert L.mla_up_proj_v(None, 0, None, None, 0, 0, 128, 512, 128, 1, 1, 1, None) == OK
+    assert L.mla_up_proj_v(FAKE, 65536, None, FAKE, 16384, 4, 128, 512, 128, 1, 1, 1, None) == INVALID
+    assert L.mla_up_proj_v(FAKE, 65536, FAKE, FAKE, 16384, 4, 128, 512, 100, 1, 1, 1, None) == UNSUPPORTED
+    assert L.mla_up_proj_v(FAKE, 65540, FAKE, FAKE, 16384, 4, 128, 512, 128, 1, 1, 1, None) == MISALIGNED
+
+
+def test_combine_argument_validation():
+    L = binding.lib()
+    assert L.mla_combine_lse(None, None, None, 0, 4, 512, None, None, 0, None) == OK
+    assert L.mla_combine_lse(None, FAKE, None, 8, 4, 512, FAKE, None, 0, None) == INVALID
+    assert L.mla_combine_lse(FAKE, FAKE, None, 8, 0, 512, FAKE, None, 0, None) == INVALID
+    assert L.mla_combine_lse(FAKE, FAKE, None, 8, 4, 510, FAKE, None, 0, None) == UNSUPPORTED
+    assert L.mla_combine_lse(FAKE + 8, FAKE, None, 8, 4, 512, FAKE, None, 0, None) == MISALIGNED
+
+
+def test_workspace_bytes_invalid():
+    L = binding.lib()
+    assert L.mla_decode_workspace_bytes(0, 1, 128, 512, 4, 0) == 0
+    assert L.mla_decode_workspace_bytes(2, 1, 128, 512, 4, -1) == 0

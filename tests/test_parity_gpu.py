@@ -1,0 +1,249 @@
+"""GPU parity: every C-ABI entry point against the float64 oracle on the same
+seeded, rounded inputs (MI355X only)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_kv_05_amd import binding, inputs
+
+from gpu_helpers import (assert_bf16_close, assert_f32_close, assert_lse_close, bf16_dev, case_to_device,
+                         f32_dev, run_decode, say)
+
+pytestmark = pytest.mark.gpu
+
+V3 = dict(n_h=128, d_c=512, d_r=64, d_h=128)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.lib()
+
+
+# ------------------------------------------------------------------ toy layer, fp32
+
+def _toy_paged(rows: np.ndarray, block_size: int, seed: int):
+    """Place [T, D] fp32 rows into a shuffled paged cache (test plumbing)."""
+    T, D = rows.shape
+    nblk = (T + block_size - 1) // block_size
+    perm = np.random.default_rng(seed).permutation(nblk)
+    cache = np.zeros((nblk, block_size, D), dtype=np.float32)
+    for j in range(nblk):
+        n = min(block_size, T - j * block_size)
+        cache[perm[j], :n] = rows[j * block_size: j * block_size + n]
+    return cache, perm.astype(np.int32)[None]
+
+
+@pytest.mark.parametrize("s_q,block_size,splits", [(1, 64, 0), (1, 64, 3), (16, 64, 0), (4, 32, 2)])
+def test_toy_layer_fp32_end_to_end(s_q, block_size, splits):
+    """Toy MLA layer (d=1024, n_h=8, d_h=64, d_c=128, d_r=32, T=256, fp32):
+    absorb -> paged decode -> up-projection vs the MHA-mode oracle."""
+    say(f"toy fp32 s_q={s_q} bs={block_size} splits={splits}")
+    W = inputs.toy_layer(seed=1, B=1, T=256)
+    dm = W["dims"]
+    n_h, d_h, d_c, d_r = dm["n_h"], dm["d_h"], dm["d_c"], dm["d_r"]
+    ref = oracle.mha_mode_layer(W["h"], W, W["pos"])
+    T = 256
+    rows = np.concatenate([ref["c_kv"][0], ref["k_r"][0]], -1).astype(np.float32)
+    cache, table = _toy_paged(rows, block_size, seed=11)
+    q_c = ref["q_c"][0, T - s_q:].astype(np.float32)                      # [s_q, n_h, d_h]
+    q_r = ref["q_r"][0, T - s_q:].astype(np.float32)                      # [s_q, n_h, d_r]
+    dev = "cuda"
+    q_lat = binding.absorb_q(f32_dev(q_c), f32_dev(W["w_uk"]))             # [s_q, n_h, d_c] fp32
+    o_lat, lse = binding.decode(q_lat.view(1, s_q, n_h, d_c), f32_dev(q_r).view(1, s_q, n_h, d_r),
+                                f32_dev(cache), torch.from_numpy(table).to(dev),
+                                torch.tensor([T], dtype=torch.int32, device=dev), 1.0 / math.sqrt(d_h + d_r),
+                                block_size=block_size, out_dtype=torch.float32, num_splits=splits)
+    o = binding.up_proj_v(o_lat.view(s_q, n_h, d_c), f32_dev(W["w_uv"]), d_h)
+    torch.cuda.synchronize()
+    o_ref = ref["o"][0, T - s_q:]
+    assert_f32_close(o.cpu().numpy().astype(np.float64), o_ref, "o")
+    assert_lse_close(lse.cpu().numpy()[0].astype(np.float64), ref["lse"][0, T - s_q:], "lse", tol=1e-5)
+    # absorbed latent output matches the oracle's absorbed form
+    o3 = oracle.absorbed_layer(W["h"], W, W["pos"])
+    assert_f32_close(o_lat.cpu().numpy()[0].astype(np.float64), o3["o_lat"][0, T - s_q:], "o_lat")
+
+
+# ------------------------------------------------------------------ V3 shapes, reduced sizes
+
+RAGGED = np.array([1, 31, 32, 33, 63, 64, 65, 127, 1000, 4097], dtype=np.int32)
+
+
+@pytest.mark.parametrize("force_generic", [False, True])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_v3_bf16_ragged_lengths(force_generic, splits):
+    say(f"v3 bf16 ragged generic={force_generic} splits={splits}")
+    case = inputs.decode_case(21, B=len(RAGGED), seq_lens=RAGGED, kv_dtype="bf16", tail_fill="nan", **V3)
+    g, gl = run_decode(case, num_splits=splits, force_generic=force_generic)
+    o, ol = oracle.mqa_decode_case(case)
+    assert_bf16_close(g, o, "o_lat")
+    assert_lse_close(gl, ol, "lse")
+
+
+def test_v3_bf16_output_dtype_bf16():
+    say("v3 bf16 out bf16")
+    case = inputs.decode_case(22, B=4, seq_lens=np.array([700, 64, 5, 2049]), **V3)
+    g, gl = run_decode(case, out_dtype=torch.bfloat16)
+    o, ol = oracle.mqa_decode_case(case)
+    assert_bf16_close(g, o, "o_lat bf16")
+    assert_lse_close(gl, ol, "lse")
+
+
+@pytest.mark.parametrize("s_q", [2, 3])
+def test_v3_bf16_multi_token_causal(s_q):
+    say(f"v3 bf16 s_q={s_q}")
+    lens = np.array([s_q, 40, 64, 65, 300], dtype=np.int32)
+    case = inputs.decode_case(23, B=len(lens), seq_lens=lens, s_q=s_q, tail_fill="nan", **V3)
+    for splits in (0, 2):
+        g, gl = run_decode(case, num_splits=splits)
+        o, ol = oracle.mqa_decode_case(case)
+        assert_bf16_close(g, o, f"o_lat s_q={s_q} splits={splits}")
+        assert_lse_close(gl, ol, "lse")
+
+
+@pytest.mark.parametrize("force_generic", [False, True])
+def test_v3_fp8_cache_sq2(force_generic):
+    say(f"v3 fp8 s_q=2 generic={force_generic}")
+    lens = np.array([2, 33, 64, 129, 1500], dtype=np.int32)
+    case = inputs.decode_case(24, B=len(lens), seq_lens=lens, s_q=2, kv_dtype="fp8", **V3)
+    for splits in (0, 3):
+        g, gl = run_decode(case, num_splits=splits, force_generic=force_generic)
+        o, ol = oracle.mqa_decode_case(case)
+        assert_bf16_close(g, o, f"fp8 splits={splits}")
+        assert_lse_close(gl, ol, "lse")
+
+
+def test_mfma_matches_generic_kernel():
+    """The two kernels agree closely with each other (both fp32 accumulation)."""
+    say("mfma vs generic")
+    case = inputs.decode_case(25, B=3, seq_lens=np.array([333, 2048, 17]), **V3)
+    a, al = run_decode(case)
+    b, bl = run_decode(case, force_generic=True)
+    assert np.abs(a - b).max() <= 2e-3
+    assert np.abs(al - bl).max() <= 1e-4
+
+
+def test_split_count_invariance():
+    say("split invariance")
+    case = inputs.decode_case(26, B=2, seq_lens=np.array([4096, 1234]), **V3)
+    base, bl = run_decode(case, num_splits=1)
+    for k in (2, 5, 16, 64):
+        g, gl = run_decode(case, num_splits=k)
+        assert np.abs(g - base).max() <= 2e-3, k
+        assert np.abs(gl - bl).max() <= 1e-4, k
+
+
+def test_determinism_and_paging_invariance():
+    say("determinism + paging")
+    case = inputs.decode_case(27, B=3, seq_lens=np.array([900, 64, 3000]), **V3)
+    a, al = run_decode(case)
+    b, bl = run_decode(case)
+    assert np.array_equal(a, b) and np.array_equal(al, bl)
+    # same logical rows behind a different physical permutation: bit-identical
+    perm = np.random.default_rng(5).permutation(case.num_blocks)
+    c2 = inputs.decode_case(27, B=3, seq_lens=np.array([900, 64, 3000]), **V3)
+    newc = np.empty_like(c2.cache)
+    newc[perm] = c2.cache
+    c2.cache = newc
+    c2.block_table = np.where(c2.block_table >= 0, perm[np.maximum(c2.block_table, 0)], -1).astype(np.int32)
+    c, cl = run_decode(c2)
+    assert np.array_equal(a, c) and np.array_equal(al, cl)
+
+
+def test_long_sequence_many_splits():
+    say("long sequence 40000 tokens")
+    case = inputs.decode_case(28, B=1, seq_lens=np.array([40000]), **V3)
+    g, gl = run_decode(case)
+    o, ol = oracle.mqa_decode_case(case)
+    assert_bf16_close(g, o, "long")
+    assert_lse_close(gl, ol, "lse")
+
+
+# ------------------------------------------------------------------ full workload sizes (sampled)
+
+@pytest.mark.parametrize("name,seqs", [
+    ("v3_bf16_B64_ctx8192", [0, 37, 63]),
+    ("v3_bf16_B128_ctxlogU128-32768", None),
+    ("v3_bf16_B4_ctx131072", [2]),
+    ("v3_fp8_B64_ctx16384_sq2", [0, 63]),
+])
+def test_full_size_workloads_sampled(name, seqs):
+    """Full workload shape in the automatic split configuration the benchmark
+    times; the oracle checks sampled sequences one by one."""
+    say(f"full size {name}")
+    case = inputs.workload_case(name)
+    if seqs is None:  # variable lengths: shortest, longest and a middle one
+        order = np.argsort(case.seq_lens)
+        seqs = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+    g, gl = run_decode(case, out_dtype=torch.bfloat16)
+    o, ol = oracle.mqa_decode_case(case, seqs)
+    assert np.all(np.isfinite(g))
+    assert_bf16_close(g[seqs], o, name)
+    assert_lse_close(gl[seqs], ol, name)
+
+
+# ------------------------------------------------------------------ combine, projections
+
+@pytest.mark.parametrize("N,S,D", [(1, 1, 4), (37, 5, 512), (256, 64, 512), (5, 3, 132)])
+def test_combine_lse(N, S, D):
+    say(f"combine N={N} S={S} D={D}")
+    rng = np.random.default_rng(N * 1000 + S)
+    o = rng.standard_normal((N, S, D)).astype(np.float32)
+    l = (rng.standard_normal((N, S)) * 3).astype(np.float32)
+    splits = rng.integers(0, S + 1, size=N).astype(np.int32)
+    if N > 2:
+        l[1, :] = -np.inf          # a row with only empty splits
+        l[2, 0] = -np.inf          # one empty split
+        splits[1] = S
+    for use_splits in (False, True):
+        out, lse = binding.combine_lse(f32_dev(o), f32_dev(l),
+                                       torch.from_numpy(splits).cuda() if use_splits else None)
+        torch.cuda.synchronize()
+        out, lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+        for n in range(N):
+            k = splits[n] if use_splits else S
+            if k == 0:
+                ro, rl = np.zeros(D), -np.inf
+            else:
+                ro, rl = oracle.combine_lse(o[n, :k].astype(np.float64), l[n, :k].astype(np.float64))
+            assert np.abs(out[n] - ro).max() <= 1e-5 * max(1, np.abs(ro).max()), (n, use_splits)
+            if np.isfinite(rl):
+                assert abs(lse[n] - rl) <= 1e-5, (n, use_splits)
+            else:
+                assert np.isneginf(lse[n])
+
+
+@pytest.mark.parametrize("T", [1, 4, 64, 100])
+def test_absorb_and_up_proj_bf16_v3(T):
+    say(f"projections bf16 T={T}")
+    P = inputs.projection_weights(31 + T, T_q=T)
+    qc, wuk, wuv, ol = (bf16_dev(P[k]) for k in ("q_c", "w_uk", "w_uv", "o_lat"))
+    q_lat = binding.absorb_q(qc, wuk, out_dtype=torch.float32)
+    o = binding.up_proj_v(ol, wuv, 128, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_q = oracle.absorb_q(oracle.bf16_to_f64(P["q_c"]), oracle.bf16_to_f64(P["w_uk"]), 128, 128)
+    ref_o = oracle.up_proj_v(oracle.bf16_to_f64(P["o_lat"]), oracle.bf16_to_f64(P["w_uv"]), 128, 128)
+    # bf16 inputs, fp32 accumulation over 128 / 512 terms
+    assert_f32_close(q_lat.cpu().numpy().astype(np.float64), ref_q, "q_lat", tol=1e-5)
+    assert_f32_close(o.cpu().numpy().astype(np.float64), ref_o, "o", tol=1e-5)
+    q16 = binding.absorb_q(qc, wuk)            # bf16 output
+    torch.cuda.synchronize()
+    assert_bf16_close(q16.float().cpu().numpy().astype(np.float64), ref_q, "q_lat bf16")
+
+
+def test_absorb_strided_tokens():
+    """q_nope rows with a token stride larger than n_h*d_h (a slice of a wider buffer)."""
+    say("absorb strided")
+    P = inputs.projection_weights(41, T_q=5)
+    wide = torch.zeros((5, 128 * 128 + 64), dtype=torch.bfloat16, device="cuda")
+    wide[:, :128 * 128] = bf16_dev(P["q_c"]).view(5, -1)
+    q = wide[:, :128 * 128].view(5, 128, 128)
+    out = binding.absorb_q(q, bf16_dev(P["w_uk"]), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.absorb_q(oracle.bf16_to_f64(P["q_c"]), oracle.bf16_to_f64(P["w_uk"]), 128, 128)
+    assert_f32_close(out.cpu().numpy().astype(np.float64), ref, "strided")
