@@ -1,0 +1,229 @@
+#!/usr/bin/env python
+"""Absorbed-MLA decode benchmark on one MI355X.
+
+One step = the whole hot path for one batch: W^UK absorption into the query
+(mla_absorb_q) -> paged split-KV decode over the latent cache with the
+log-sum-exp combine (mla_decode_absorbed) -> W^UV up-projection
+(mla_up_proj_v).  Inputs are seeded synthetic tensors already resident in HBM;
+the timed region rotates through several physically distinct copies of the
+latent cache so repeated steps cannot be served from the 256 MB last-level
+cache.
+
+Prints one JSON line.  Metric: latent-cache bytes read per second (TB/s) of
+the whole step, with decode tokens/s and the roofline fraction alongside.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "latent-KV TB/s + decode tok/s, absorbed MLA n_h=128 B=64 ctx 8K, % roofline"
+HEADLINE = "v3_bf16_B64_ctx8192"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+KERNEL_SRC = os.path.join(ROOT, "mla_latent_kv_05_amd", "csrc", "decode_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_bf16_B64_ctx8192_traffic.md")
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode call from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    if workload != HEADLINE or not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("traffic:"):
+            for kv in line.split()[1:]:
+                k, _, v = kv.partition("=")
+                fields[k] = v
+    if fields.get("kernel_sha256_16") != kernel_hash():
+        return None
+    try:
+        return int(fields["bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(case, P, seconds: float) -> dict:
+    """The float64 oracle on a bounded sample of the same workload: whole
+    sequences (gather pages, absorb, decode, up-project) until `seconds` of
+    CPU time have been spent; reported in the GPU's unit."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    qc = oracle.bf16_to_f64(P["q_c"]).reshape(case.B, case.s_q, case.n_h, case.d_h)
+    wuk = oracle.bf16_to_f64(P["w_uk"])
+    wuv = oracle.bf16_to_f64(P["w_uv"])
+    done, nbytes, t0 = 0, 0, time.perf_counter()
+    while True:
+        b = done % case.B
+        _, qr, c, kr = oracle.decode_case_rows(case, b)
+        ql = oracle.absorb_q(qc[b], wuk, case.n_h, case.d_h)
+        o_lat, _ = oracle.mqa_decode_rows(ql, qr, c, kr, case.softmax_scale)
+        oracle.up_proj_v(o_lat, wuv, case.n_h, case.d_h)
+        done += 1
+        nbytes += int(case.seq_lens[b]) * case.row_bytes
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= case.B:
+            break
+    return {"value": nbytes / el / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {case.B} sequences of the workload, whole step (page gather, W^UK absorb, "
+                      f"decode, W^UV) in float64 numpy, {el:.1f} s, rate scaled by latent bytes",
+            "tok_s": done * case.s_q / el, "seconds": el}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--copies", type=int, default=4, help="physically distinct cache copies rotated per step")
+    ap.add_argument("--splits", type=int, default=0, help="0 = automatic split planning")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from mla_latent_kv_05_amd import binding, inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    binding.lib()
+
+    w = inputs.WORKLOADS[args.workload]
+    assert w["kind"] == "decode", "bench.py times the decode workloads"
+    case = inputs.workload_case(args.workload)
+    B, s_q, n_h, d_c, d_r, d_h = case.B, case.s_q, case.n_h, case.d_c, case.d_r, case.d_h
+    T_q = B * s_q
+    P = inputs.projection_weights(w["seed"] + 100, T_q=T_q, n_h=n_h, d_h=d_h, d_c=d_c)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if case.kv_dtype == "bf16":
+        base = bf(case.cache)
+        kv_dtype = binding.MLA_BF16
+    else:
+        base = torch.from_numpy(np.ascontiguousarray(case.cache)).to(dev)
+        kv_dtype = binding.MLA_FP8_E4M3
+    caches = [base] + [base.clone() for _ in range(max(0, args.copies - 1))]
+    table = torch.from_numpy(np.maximum(case.block_table, 0).astype(np.int32)).to(dev)
+    lens = torch.from_numpy(case.seq_lens.astype(np.int32)).to(dev)
+    q_c, w_uk, w_uv = bf(P["q_c"]), bf(P["w_uk"]), bf(P["w_uv"])
+    q_rope = bf(case.q_rope)
+    q_lat = torch.empty((T_q, n_h, d_c), dtype=torch.bfloat16, device=dev)
+    o_lat = torch.empty((B, s_q, n_h, d_c), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, s_q, n_h), dtype=torch.float32, device=dev)
+    o = torch.empty((T_q, n_h, d_h), dtype=torch.bfloat16, device=dev)
+    ws = binding.alloc_workspace(B, s_q, n_h, d_c, table.shape[1], args.splits, device=dev)
+    scale = 1.0 / math.sqrt(d_h + d_r)
+
+    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)] for k in ("a", "b", "c", "d")}
+
+    def step(i, timed=False):
+        if timed:
+            ev["a"][i].record()
+        binding.absorb_q(q_c, w_uk, out=q_lat)
+        if timed:
+            ev["b"][i].record()
+        binding.decode(q_lat.view(B, s_q, n_h, d_c), q_rope, caches[i % len(caches)], table, lens, scale,
+                       kv_dtype=kv_dtype, d_r=d_r, out=o_lat, lse=lse, workspace=ws, num_splits=args.splits)
+        if timed:
+            ev["c"][i].record()
+        binding.up_proj_v(o_lat.view(T_q, n_h, d_c), w_uv, d_h, out=o)
+        if timed:
+            ev["d"][i].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i, timed=True)
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    absorb_ms = float(np.mean([ev["a"][i].elapsed_time(ev["b"][i]) for i in range(args.steps)]))
+    decode_ms = float(np.mean([ev["b"][i].elapsed_time(ev["c"][i]) for i in range(args.steps)]))
+    up_ms = float(np.mean([ev["c"][i].elapsed_time(ev["d"][i]) for i in range(args.steps)]))
+
+    latent_bytes = case.latent_bytes
+    value = latent_bytes / (ms_step * 1e-3) / 1e12
+    tok_s = T_q / (ms_step * 1e-3)
+    flops = 0
+    for b in range(B):
+        L = int(case.seq_lens[b])
+        for i in range(s_q):
+            vis = L - s_q + i + 1
+            flops += vis * (2 * n_h * (d_c + d_r) + 2 * n_h * d_c)
+    if case.kv_dtype == "bf16":
+        achieved = latent_bytes / (decode_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        achieved = flops / (decode_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_MFMA_PEAK_TFLOPS}
+    roof["traffic"] = measured_traffic(args.workload)
+    roof["kernel"] = "mla_decode_absorbed (split planner + decode_mfma_kernel + combine), one call"
+    roof["units_per_launch"] = {"tokens": int(case.seq_lens.sum()), "bytes_per_token": case.row_bytes,
+                                "flops": flops}
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if case.kv_dtype == "bf16" else "fp8e4m3+bf16",
+        "data": "synthetic: seeded PCG64 N(0,1) latent cache rounded to bf16 (fp8: per-token amax/448 e4m3fn), "
+                "q_lat N(0,1/512) from W^UK absorption, shuffled 64-token pages",
+        "config": {"workload": args.workload, "n_h": n_h, "d_c": d_c, "d_r": d_r, "d_h": d_h, "B": B,
+                   "s_q": s_q, "ctx": int(case.seq_lens.max()) if w["lens"][0] == "fixed" else "log-uniform",
+                   "page_tokens": case.block_size, "kv_dtype": case.kv_dtype, "splits": args.splits or "auto",
+                   "cache_copies": len(caches)},
+        "decode_tok_s": tok_s, "latent_bytes": latent_bytes,
+        "roofline_frac_step": value * 1e3 / HBM_PEAK_GBS if case.kv_dtype == "bf16" else None,
+        "absorb_ms": absorb_ms, "decode_ms": decode_ms, "up_proj_ms": up_ms, "wall_s": t_wall,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(case, P, args.cpu_seconds)
+        rec["cpu_baseline"]["cpu_model"] = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                                                 if l.startswith("model name")), platform.processor())
+        rec["cpu_baseline"]["affinity_cores"] = len(os.sched_getaffinity(0))
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

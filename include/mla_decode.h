@@ -112,7 +112,7 @@ size_t mla_decode_workspace_bytes(int B, int s_q, int n_h, int d_c, int max_bloc
  *  num_splits  0 = automatic split-KV planning from the lengths and the
  *           device's compute-unit count; k > 0 = each sequence is cut into
  *           min(k, its block count) contiguous partitions, raised where a
- *           partition would exceed 2048 blocks.
+ *           partition would exceed 512 blocks.
  *  workspace   device buffer of at least mla_decode_workspace_bytes(...)
  *           bytes; its contents need no initialisation and are clobbered.
  *  flags    0 or MLA_FLAG_FORCE_GENERIC.
@@ -162,9 +162,9 @@ int mla_combine_lse(const float* o_part, const float* lse_part, const int32_t* s
  *  o_lat [T_q, n_h, d_c], token stride olat_stride_t, dtype act_dtype
  *  w_uv  [n_h*d_h, d_c], dtype w_dtype
  *  o     [T_q, n_h, d_h], token stride o_stride_t, dtype out_dtype
- *  bf16 activations and weights take the MFMA kernel (needs d_c % 16 == 0,
- *  d_h % 32 == 0, 16-byte aligned rows); other combinations a plain fp32
- *  kernel.  Accumulation is fp32.  T_q == 0 is a no-op.
+ *  bf16 activations and weights take the MFMA kernel (needs d_c % 64 == 0,
+ *  d_c <= 512, d_h % 32 == 0, 16-byte aligned rows); other combinations a
+ *  plain fp32 kernel.  Accumulation is fp32.  T_q == 0 is a no-op.
  */
 int mla_up_proj_v(const void* o_lat, int64_t olat_stride_t, const void* w_uv, void* o,
                   int64_t o_stride_t, int T_q, int n_h, int d_c, int d_h, int act_dtype,

@@ -101,7 +101,7 @@ int mla_up_proj_v(const void* o_lat, int64_t olat_stride_t, const void* w_uv, vo
   if (olat_stride_t < (int64_t)n_h * d_c || o_stride_t < (int64_t)n_h * d_h) return MLA_ERR_INVALID_ARG;
   const bool mfma = act_dtype == MLA_BF16 && w_dtype == MLA_BF16;
   if (mfma) {
-    if (d_c % 16 != 0 || d_h % 32 != 0) return MLA_ERR_UNSUPPORTED;
+    if (d_c % 64 != 0 || d_c > 512 || d_h % 32 != 0) return MLA_ERR_UNSUPPORTED;
     if (!aligned16(o_lat) || !aligned16(w_uv) || olat_stride_t % 8 != 0) return MLA_ERR_MISALIGNED;
   }
   return launch_status(launch_up_proj(o_lat, olat_stride_t, w_uv, o, o_stride_t, T_q, n_h, d_c, d_h,

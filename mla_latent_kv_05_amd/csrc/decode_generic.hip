@@ -19,30 +19,7 @@ namespace mla {
 // partial-result write and merge of a split sequence.
 
 constexpr int kPlanThreads = 1024;
-
-__device__ int block_sum(int v, int* red) {
-  int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  __syncthreads();
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  int t = 0;
-  for (int i = 0; i < kPlanThreads / 64; ++i) t += red[i];
-  return t;
-}
-
-__device__ int block_max(int v, int* red) {
-  int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-  __syncthreads();
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  int t = 0;
-  for (int i = 0; i < kPlanThreads / 64; ++i) t = max(t, red[i]);
-  return t;
-}
+constexpr int kPlanLdsSeqs = 8192;  // sequence block counts cached in LDS up to this batch
 
 __device__ __forceinline__ int nblocks_of(const PlanArgs& a, int b) {
   int L = a.seq_lens[b];
@@ -50,10 +27,13 @@ __device__ __forceinline__ int nblocks_of(const PlanArgs& a, int b) {
   return n < 1 ? 1 : n;
 }
 
-__device__ int units_for_chunk(const PlanArgs& a, int c, int* red) {
-  int cnt = 0;
-  for (int b = threadIdx.x; b < a.B; b += kPlanThreads) cnt += (nblocks_of(a, b) + c - 1) / c;
-  return block_sum(cnt, red);
+// ceil(n / c) for 0 < n, c < 2^23 through a float reciprocal plus one correction
+__device__ __forceinline__ int ceil_div_small(int n, int c, float rc) {
+  int q = (int)((float)(n + c - 1) * rc);
+  const int num = n + c - 1;
+  if ((q + 1) * c <= num) ++q;
+  if (q * c > num) --q;
+  return q;
 }
 
 // partitions of a sequence with n blocks: explicit count (raised where a
@@ -67,44 +47,77 @@ __device__ __forceinline__ int units_of(const PlanArgs& a, int n, int chunk) {
   return (n + chunk - 1) / chunk;
 }
 
+// Every candidate partition length c in [lo, hi] (at most 2048 of them) is
+// scored in parallel: units(c) = sum_b ceil(n_b / c), waves = ceil(units /
+// slots), cost = waves * (c + overhead), overhead charged when any sequence
+// is split.  The cheapest c with waves <= kMaxAutoWaves wins (ties: larger c,
+// i.e. fewer partial results); if none fits, c = hi.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  __shared__ int red[kPlanThreads / 64];
+  __shared__ int nb[kPlanLdsSeqs];
+  __shared__ unsigned long long red[kPlanThreads / 64];
   __shared__ int scan[kPlanThreads];
-  const int tid = threadIdx.x;
+  __shared__ int s_chunk, s_waves;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool in_lds = a.B <= kPlanLdsSeqs;
 
-  int chunk = 0, waves = 1;
-  if (a.num_splits <= 0) {
-    int max_n = 0;
-    for (int b = tid; b < a.B; b += kPlanThreads) max_n = max(max_n, nblocks_of(a, b));
-    max_n = block_max(max_n, red);
-    const int overhead = 4;
-    long long best_cost = -1;
-    for (int k = 1; k <= kMaxAutoWaves; ++k) {
-      int target = k * a.slots_per_wave;
-      int hi = min(max_n, a.max_chunk);
-      int lo = min(a.min_chunk, hi);
-      if (lo < 1) lo = 1;
-      // smallest c in [lo, hi] with units(c) <= target (hi always qualifies or is the floor)
-      while (lo < hi) {
-        int mid = (lo + hi) >> 1;
-        if (units_for_chunk(a, mid, red) <= target) hi = mid; else lo = mid + 1;
-      }
-      int c = lo;
-      int u = units_for_chunk(a, c, red);
-      int w = (u + a.slots_per_wave - 1) / a.slots_per_wave;
-      long long cost = (long long)w * (c + (u > a.B ? overhead : 0));
-      if (best_cost < 0 || cost < best_cost) { best_cost = cost; chunk = c; waves = w; }
-    }
+  int max_n = 0;
+  for (int b = tid; b < a.B; b += kPlanThreads) {
+    const int n = nblocks_of(a, b);
+    if (in_lds) nb[b] = n;
+    max_n = max(max_n, n);
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) max_n = max(max_n, __shfl_xor(max_n, o, 64));
+  if (lane == 0) red[wv] = (unsigned long long)max_n;
+  __syncthreads();
+  max_n = 0;
+  for (int i = 0; i < kPlanThreads / 64; ++i) max_n = max(max_n, (int)red[i]);
+  __syncthreads();
+
+  if (a.num_splits <= 0) {
+    const int hi = min(max_n, a.max_chunk);
+    const int lo = max(1, min(a.min_chunk, hi));
+    const int overhead = 4;
+    unsigned long long best = ~0ull;  // key = cost << 32 | (0xffffffff - c)
+    for (int c = lo + tid; c <= hi; c += kPlanThreads) {
+      const float rc = 1.0f / (float)c;
+      int u = 0;
+      for (int b = 0; b < a.B; ++b) u += ceil_div_small(in_lds ? nb[b] : nblocks_of(a, b), c, rc);
+      const int waves = (u + a.slots_per_wave - 1) / a.slots_per_wave;
+      if (waves > kMaxAutoWaves && c != hi) continue;
+      const unsigned long long cost = (unsigned long long)waves * (unsigned)(c + (u > a.B ? overhead : 0));
+      const unsigned long long key = (cost << 32) | (0xffffffffu - (unsigned)c);
+      best = key < best ? key : best;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const unsigned long long other = __shfl_xor(best, o, 64);
+      best = other < best ? other : best;
+    }
+    if (lane == 0) red[wv] = best;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long m = ~0ull;
+      for (int i = 0; i < kPlanThreads / 64; ++i) m = red[i] < m ? red[i] : m;
+      const int c = (int)(0xffffffffu - (unsigned)(m & 0xffffffffu));
+      int u = 0;
+      for (int b = 0; b < a.B; ++b) u += ((in_lds ? nb[b] : nblocks_of(a, b)) + c - 1) / c;
+      s_chunk = c;
+      s_waves = (u + a.slots_per_wave - 1) / a.slots_per_wave;
+    }
+    __syncthreads();
+  } else if (tid == 0) {
+    s_chunk = 0;
+    s_waves = 0;
+  }
+  __syncthreads();
+  const int chunk = s_chunk;
 
   // per-thread run of consecutive sequences for the prefix sum
   const int per = (a.B + kPlanThreads - 1) / kPlanThreads;
   const int b0 = tid * per, b1 = min(a.B, b0 + per);
   int local = 0;
-  for (int b = b0; b < b1; ++b) {
-    int n = nblocks_of(a, b);
-    local += units_of(a, n, chunk);
-  }
+  for (int b = b0; b < b1; ++b) local += units_of(a, in_lds ? nb[b] : nblocks_of(a, b), chunk);
   scan[tid] = local;
   __syncthreads();
   for (int o = 1; o < kPlanThreads; o <<= 1) {
@@ -115,12 +128,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   int first = scan[tid] - local;
   for (int b = b0; b < b1; ++b) {
-    int n = nblocks_of(a, b);
-    int u = units_of(a, n, chunk);
-    int len = (n + u - 1) / u;
+    const int n = in_lds ? nb[b] : nblocks_of(a, b);
+    const int u = units_of(a, n, chunk);
+    const int len = (n + u - 1) / u;
     a.seq[b] = make_int2(first, u);
     for (int k = 0; k < u; ++k) {
-      int s0 = k * len, s1 = min(n, s0 + len);
+      const int s0 = k * len, s1 = min(n, s0 + len);
       a.work[first + k] = make_int4(b, s0, s1, u > 1 ? first + k : -1);
     }
     first += u;
@@ -129,7 +142,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     WsHeader* h = (WsHeader*)a.ws_header;
     h->n_units = scan[tid];
     h->chunk_blocks = chunk;
-    h->waves = waves;
+    h->waves = s_waves;
   }
 }
 

@@ -30,121 +30,9 @@
 // c is stored at chunk (c & ~7) | ((c ^ f(t)) & 7), f(t) = ((t&3)<<1)|((t>>2)&1),
 // which keeps both the 8-row b128 reads of the QK step and the 4-row
 // transposed reads of the PV step free of bank conflicts.
-#include "device_util.h"
-#include "mla_internal.h"
+#include "mfma_common.h"
 
 namespace mla {
-
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __attribute__((address_space(3))) int lds_i32;
-
-constexpr int kHeads = 128;
-constexpr int kDc = 512;
-constexpr int kDr = 64;
-constexpr int kBlk = 64;                          // tokens per page
-constexpr int kSub = 32;                          // tokens per subtile
-constexpr int kRowB = (kDc + kDr) * 2;            // 1152
-constexpr int kTileB = kSub * kRowB;              // 36864
-constexpr int kStages = 4;
-constexpr int kBf16Dma = kTileB / (4 * 1024);     // 9 DMA instructions per wave per subtile
-// fp8 staging per subtile: codes | k^R | scales
-constexpr int kF8Codes = kSub * kDc;              // 16384
-constexpr int kF8Kr = kSub * kDr * 2;             // 4096
-constexpr int kF8Stage = kF8Codes + kF8Kr + 256;  // 20736 (scales + pad)
-constexpr int kF8Dma = 6;                         // 4 code + 1 k^R + 1 scale instruction per wave
-constexpr float kTau = 8.0f;                      // lazy-rescale threshold (log2 units)
-constexpr int kMaxUnitPages = 2048;               // page ids cached in LDS per unit
-
-constexpr int kQrStride = kDr * 2 + 16;            // padded bytes per head of the LDS q_rope copy (fp8)
-constexpr int kTabOff(bool fp8) { return fp8 ? kStages * kF8Stage + kTileB : kStages * kTileB; }
-constexpr int kQrOff(bool fp8) { return kTabOff(fp8) + kMaxUnitPages * 4; }
-constexpr int kLdsBytes(bool fp8) { return kQrOff(fp8) + (fp8 ? kHeads * kQrStride : 0); }
-
-__device__ __forceinline__ int swz_f(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
-
-typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
-
-__device__ __forceinline__ i32x4_t make_rsrc(const void* base) {
-  const uint64_t a = (uint64_t)base;
-  i32x4_t r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));  // stride 0
-  r[2] = -1;                                                        // num_records: no clamping
-  r[3] = 0x00020000;                                                // gfx9 raw buffer config
-  return r;
-}
-
-// 16-byte global -> LDS DMA (buffer_load_dwordx4 ... lds): lane l's 16 bytes
-// from rsrc.base + voff land at LDS address m0 + 16*l.  Issued as inline asm so
-// that the compiler does not add its own vmcnt waits in front of later LDS
-// reads; completion is tracked explicitly with wait_vm<>() + a barrier.  The
-// leading s_nop covers the VALU-writes-SGPR -> VMEM-reads-SGPR hazard on the
-// resource, the one after the M0 write the SALU-writes-M0 -> LDS-DMA hazard.
-__device__ __forceinline__ void dma16(i32x4_t rsrc, int voff, lds_u8* l) {
-  const int m0v = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)l);
-  asm volatile(
-      "s_nop 4\n\t"
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v),
-      "v"(voff), "s"(rsrc)
-      : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(n) only (gfx9 encoding: expcnt/lgkmcnt at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-template <int G>
-__device__ __forceinline__ void wait_groups(int outstanding) {
-  static_assert(kStages == 4, "wait table assumes 4 stages");
-  if (outstanding >= 2)
-    wait_vm<2 * G>();
-  else if (outstanding == 1)
-    wait_vm<G>();
-  else
-    wait_vm<0>();
-}
-
-__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// P.V accumulation with the accumulator pinned to AGPRs (the 16 blocks fill
-// the whole AGPR file, leaving every VGPR for queries and temporaries).  The
-// s_nop provides the 2 wait states a VALU-written VGPR needs before an MFMA
-// reads it as A/B; back-to-back accumulation into the same AGPRs with the same
-// opcode needs none.
-__device__ __forceinline__ void mfma_acc(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// Orders VALU/accvgpr access to the AGPR accumulator after (or before) the
-// asm MFMAs above: 24 wait states cover the MFMA-writes-AGPR ->
-// v_accvgpr_read and v_accvgpr_write -> MFMA-reads-SrcC hazards.
-__device__ __forceinline__ void acc_fence(f32x16_t* acc) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-               : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]), "+a"(acc[5]),
-                 "+a"(acc[6]), "+a"(acc[7]), "+a"(acc[8]), "+a"(acc[9]), "+a"(acc[10]), "+a"(acc[11]),
-                 "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]), "+a"(acc[15]));
-}
-
-__device__ __forceinline__ bf16x8_t lds_b128(const lds_u8* p) {
-  return *(const __attribute__((address_space(3))) bf16x8_t*)p;
-}
-__device__ __forceinline__ bf16x4_t lds_tr16(const lds_u8* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p);
-}
-
-// two e4m3fn codes (bytes 0,1 or 2,3 of w) -> packed bf16 pair (exact)
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
-  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
-}
 
 template <bool FP8>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -165,13 +53,19 @@ void decode_mfma_kernel(DecodeArgs a) {
   int off_qk[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) off_qk[j] = l32 * kRowB + (((2 * j + g) ^ swz_f(l32)) << 4);
-  int off_pv[2];
+  // transposed V reads: rows ta (first 4 k-slots) and ta + 8 (last 4), for
+  // even / odd 32-dim blocks
+  int off_pv[2][2];
   {
     const int ta = 4 * g + (j16 >> 2);
-    const int fa = ((j16 >> 2) << 1) | g;
     const int clo = 2 * (G & 1) + ((j16 & 3) >> 1);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) off_pv[p] = ta * kRowB + (((4 * p + clo) ^ fa) << 4) + (j16 & 1) * 8;
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = ta + 8 * h;
+        off_pv[p][h] = t * kRowB + (((4 * p + clo) ^ swz_f(t)) << 4) + (j16 & 1) * 8;
+      }
   }
   // DMA source offsets of this lane within a bf16 subtile (LDS chunk -> global chunk)
   // (16-bit pairs: offsets are < 36864)
@@ -393,9 +287,9 @@ void decode_mfma_kernel(DecodeArgs a) {
       // ---- O^T += V^T . P^T  (rolling prefetch of the transposed value reads)
       {
         auto load_v = [&](int db, int ks) {
-          const lds_u8* pv = tile + off_pv[db & 1] + (db >> 1) * 128 + ks * 16 * kRowB;
-          const bf16x4_t lo = lds_tr16(pv);
-          const bf16x4_t hi = lds_tr16(pv + 8 * kRowB);
+          const int kofs = (db >> 1) * 128 + ks * 16 * kRowB;
+          const bf16x4_t lo = lds_tr16(tile + off_pv[db & 1][0] + kofs);
+          const bf16x4_t hi = lds_tr16(tile + off_pv[db & 1][1] + kofs);
           bf16x8_t v;
           v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
           v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
@@ -455,20 +349,15 @@ void decode_mfma_kernel(DecodeArgs a) {
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t s) {
-  static bool attr_set[2] = {false, false};
-  const bool fp8 = a.kv_dtype == 2;
-  hipError_t e;
-  if (!attr_set[fp8]) {
-    e = hipFuncSetAttribute(fp8 ? (const void*)decode_mfma_kernel<true> : (const void*)decode_mfma_kernel<false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes(fp8));
+  if (a.kv_dtype != 2) return launch_decode_bf16(a, grid_x, s);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)decode_mfma_kernel<true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes(true));
     if (e != hipSuccess) return e;
-    attr_set[fp8] = true;
+    attr_set = true;
   }
-  dim3 grid(grid_x, a.s_q);
-  if (fp8)
-    hipLaunchKernelGGL(decode_mfma_kernel<true>, grid, dim3(256), kLdsBytes(true), s, a);
-  else
-    hipLaunchKernelGGL(decode_mfma_kernel<false>, grid, dim3(256), kLdsBytes(false), s, a);
+  hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(grid_x, a.s_q), dim3(256), kLdsBytes(true), s, a);
   return hipGetLastError();
 }
 

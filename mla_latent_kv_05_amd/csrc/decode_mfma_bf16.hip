@@ -1,0 +1,371 @@
+// Software-pipelined MFMA decode kernel for a bf16 latent cache at the
+// DeepSeek-V2/V3 shape (n_h = 128, d_c = 512, d_h^R = 64, 64-token pages).
+// Same work decomposition, LDS tile layout and operand mapping as the fp8
+// kernel in decode_mfma.hip (see the notes there); this variant overlaps the
+// stages of consecutive 32-token subtiles so the matrix pipe stays busy:
+//
+//   iteration i   (A) wait for subtile i+1, barrier, DMA subtile i+3
+//                 (B) S(i+1) = K(i+1).Q^T on MFMA   ||  p = exp2(s(i) - m), P(i) in bf16
+//                 (C) O += V(i)^T.P(i)^T on MFMA   ||  s(i+1) = scale * S(i+1), mask, row max
+//                 (D) rare: rescale O when the row max grew by more than kTau
+//
+// Only (D) runs without MFMA work beside it.  The unit's partial (or final)
+// output is staged through LDS so each store instruction writes whole rows.
+#include "mfma_common.h"
+
+namespace mla {
+
+constexpr int kB16Stages = 4;                               // tiles i, i+1 in use, i+2, i+3 in flight
+constexpr int kB16TabOff = kB16Stages * kTileB;             // 147456
+constexpr int kB16Pages = kMaxUnitPages;                    // page ids cached in LDS per unit
+constexpr int kB16GoffOff = kB16TabOff + kB16Pages * 4;     // 149504: per-thread DMA offsets
+constexpr int kB16Lds = kB16GoffOff + 256 * 20;             // 154624
+constexpr int kOutRowF = kDc + 4;                           // padded fp32 row of the output staging
+
+// s_waitcnt vmcnt for "at most n DMA groups of this kernel still in flight"
+__device__ __forceinline__ void wait_b16_groups(int n) {
+  if (n >= 2)
+    wait_vm<2 * kBf16Dma>();
+  else if (n == 1)
+    wait_vm<kBf16Dma>();
+  else
+    wait_vm<0>();
+}
+
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_bf16_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
+  lds_u8* smem = (lds_u8*)smem_raw;
+  lds_i32* tab = (lds_i32*)(smem + kB16TabOff);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31, j16 = lane & 15, G = lane >> 4;
+  const int qi = blockIdx.y;
+  const int R = a.s_q * kHeads;
+  const int head = w * 32 + l32;
+  const int n_units = ((const WsHeader*)a.ws_header)->n_units;
+  const float scale2 = a.scale * kLog2e;
+
+  int off_qk[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) off_qk[j] = l32 * kRowB + (((2 * j + g) ^ swz_f(l32)) << 4);
+  // transposed V reads: rows ta (first 4 k-slots) and ta + 8 (last 4), for
+  // even / odd 32-dim blocks
+  int off_pv[2][2];
+  {
+    const int ta = 4 * g + (j16 >> 2);
+    const int clo = 2 * (G & 1) + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = ta + 8 * h;
+        off_pv[p][h] = t * kRowB + (((4 * p + clo) ^ swz_f(t)) << 4) + (j16 & 1) * 8;
+      }
+  }
+  // DMA source offset of each of this thread's 9 LDS chunks within a subtile
+  // (LDS chunk -> global chunk through the swizzle), kept in LDS as 16-bit
+  // pairs: 5 dwords per thread, written once
+  lds_u8* goff_lds = smem + kB16GoffOff + tid * 20;
+#pragma unroll
+  for (int i2 = 0; i2 < 5; ++i2) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 2 * i2 + h;
+      if (i < kBf16Dma) {
+        const int p = (i * 4 + w) * 64 + lane;
+        const int t = p / 72;
+        v |= (uint32_t)((t * 72 + ((p - t * 72) ^ swz_f(t))) * 16) << (16 * h);
+      }
+    }
+    *(__attribute__((address_space(3))) uint32_t*)(goff_lds + 4 * i2) = v;
+  }
+
+  for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+    const int4 wk = a.work[unit];
+    const int b = wk.x;
+    const int L = a.seq_lens[b];
+    const int vis = L - a.s_q + qi + 1;
+    const int tok0 = wk.y * kBlk;
+    const int tok1 = min(wk.z * kBlk, vis);
+    const int ntok = tok1 - tok0;
+    const int n_sub = ntok > 0 ? (ntok + kSub - 1) / kSub : 0;
+    const int n_last = ntok - (n_sub - 1) * kSub;  // valid rows of the last subtile
+    auto nvalid_of = [&](int t) { return t == n_sub - 1 ? n_last : kSub; };
+
+    __syncthreads();  // the previous unit is done with LDS
+    {
+      const int npg = (n_sub * kSub + kBlk - 1) / kBlk;
+      const int32_t* trow = a.table + (long long)b * a.max_blocks + wk.y;
+      for (int i = tid; i < npg; i += 256) tab[i] = trow[i];
+    }
+    wait_vm<0>();
+    __syncthreads();  // page ids visible
+    auto issue = [&](int s) {
+      const int pg = __builtin_amdgcn_readfirstlane(tab[s >> 1]);
+      const uint8_t* blk = (const uint8_t*)a.kv + (long long)pg * a.block_bytes;
+      lds_u8* dst = smem + (s % kB16Stages) * kTileB + w * 1024;
+      const i32x4_t rs = make_rsrc(blk + (s & 1) * kTileB);
+      const u32x4_t o4 = *(const __attribute__((address_space(3))) u32x4_t*)goff_lds;
+      const uint32_t o5 = *(const __attribute__((address_space(3))) uint32_t*)(goff_lds + 16);
+      const uint32_t ow[5] = {o4[0], o4[1], o4[2], o4[3], o5};
+#pragma unroll
+      for (int i = 0; i < kBf16Dma; ++i) dma16(rs, (int)((ow[i >> 1] >> (16 * (i & 1))) & 0xffffu), dst + i * 4096);
+    };
+    auto tile_of = [&](int s) { return smem + (s % kB16Stages) * kTileB; };
+    // zero the value rows of a ragged last subtile (they may hold NaN); all threads
+    auto zero_tail = [&](int s) {
+      lds_u8* t_ = tile_of(s);
+      const int nv = nvalid_of(s);
+      for (int e = tid; e < (kSub - nv) * 72; e += 256) {
+        const int t = nv + e / 72, c = e % 72;
+        *(__attribute__((address_space(3))) u32x4_t*)(t_ + t * kRowB + c * 16) = u32x4_t{0, 0, 0, 0};
+      }
+    };
+
+    f32x16_t acc[16];
+#pragma unroll
+    for (int d = 0; d < 16; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
+    acc_fence(acc);
+    float m_run = -INFINITY, l_run = 0.f;
+
+    if (n_sub > 0) {
+#pragma unroll
+      for (int s = 0; s < kB16Stages - 1; ++s)
+        if (s < n_sub) issue(s);
+    }
+    // queries (issued after the first DMA groups so the two latencies overlap)
+    bf16x8_t q[36];
+    {
+      const long long qrow = ((long long)b * a.s_q + qi) * kHeads + head;
+      const bf16x8_t* ql = (const bf16x8_t*)((const uint16_t*)a.q_lat + qrow * kDc);
+      const bf16x8_t* qr = (const bf16x8_t*)((const uint16_t*)a.q_rope + qrow * kDr);
+#pragma unroll
+      for (int kb = 0; kb < 32; ++kb) q[kb] = ql[2 * kb + g];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) q[32 + kb] = qr[2 * kb + g];
+    }
+    if (n_sub > 0) {
+      // the query loads are the newest: waiting for the groups after tile 0
+      // to be the only ones left would not cover them, so wait for all here
+      wait_vm<0>();
+      __syncthreads();
+      if (n_last < kSub && n_sub == 1) {
+        zero_tail(0);
+        __syncthreads();
+      }
+    }
+
+    // ---- helpers on LDS tiles
+    // QK A-operand fragment f (0..35) of a tile: k-block f, slot group g
+    auto kfrag = [&](const lds_u8* tile, int f) { return lds_b128(tile + off_qk[f & 3] + (f >> 2) * 128); };
+    // PV A-operand fragment of step (db, ks): V^T[dims db*32.., tokens 16ks + {4g..4g+3, 8+4g..}]
+    auto vfrag = [&](const lds_u8* tile, int step) {
+      const int db = step & 15, ks = step >> 4;  // ks-outer order
+      const int kofs = (db >> 1) * 128 + ks * 16 * kRowB;
+      const bf16x4_t lo = lds_tr16(tile + off_pv[db & 1][0] + kofs);
+      const bf16x4_t hi = lds_tr16(tile + off_pv[db & 1][1] + kofs);
+      bf16x8_t v;
+      v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+      v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+      return v;
+    };
+    // scaled, masked score of row value r of subtile t (in place) and its running max
+    auto score = [&](f32x16_t& sv, int r, int nv, float& mx) {
+      const int t = 8 * (r >> 2) + 4 * g + (r & 3);
+      sv[r] = t < nv ? sv[r] * scale2 : -INFINITY;
+      mx = fmaxf(mx, sv[r]);
+    };
+
+    f32x16_t sc;   // S of the subtile whose scores are being formed
+    bf16x8_t P[2]; // P of the subtile whose P.V is in flight
+    if (n_sub > 0) {
+      // S(0), its scores, the first reference max and P(0)
+      const lds_u8* tile = tile_of(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+      bf16x8_t ka[2] = {kfrag(tile, 0), kfrag(tile, 1)};
+#pragma unroll
+      for (int f = 0; f < 36; ++f) {
+        sc = mfma(ka[f & 1], q[f], sc);
+        if (f + 2 < 36) ka[f & 1] = kfrag(tile, f + 2);
+      }
+      float mx = -INFINITY;
+      const int nv = nvalid_of(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) score(sc, r, nv, mx);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      m_run = mx;
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(sc[r] - m_run);
+        ps += p;
+        P[r >> 3][r & 7] = (__bf16)p;
+      }
+      l_run = ps;
+    }
+
+    for (int it = 0; it + 1 < n_sub; ++it) {
+      // ---- (A) next subtile resident; refill the stage subtile it-1 used
+      wait_b16_groups(min(1, n_sub - 2 - it));
+      __syncthreads();
+      if (it + 3 < n_sub) issue(it + 3);
+      if (it + 1 == n_sub - 1 && n_last < kSub) {
+        zero_tail(it + 1);
+        __syncthreads();
+      }
+      const lds_u8* tile = tile_of(it);
+      const lds_u8* tile_n = tile_of(it + 1);
+
+      // ---- (X) S(it+1) (one dependent chain) interleaved with P.V steps 0..15
+      //      of subtile it (independent accumulators fill the chain's gaps)
+      bf16x8_t va[2] = {vfrag(tile, 0), vfrag(tile, 1)};
+      bf16x8_t ka[2] = {kfrag(tile_n, 0), kfrag(tile_n, 1)};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+      for (int k4 = 0; k4 < 9; ++k4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int f = 4 * k4 + j;
+          sc = mfma(ka[f & 1], q[f], sc);
+          if (f + 2 < 36) ka[f & 1] = kfrag(tile_n, f + 2);
+          if ((j & 1) && k4 < 8) {  // one P.V step after every second QK step
+            const int step = 2 * k4 + (j >> 1);
+            mfma_acc(acc[step & 15], va[step & 1], P[step >> 4]);
+            va[step & 1] = vfrag(tile, step + 2);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // ---- (Y) P.V steps 16..31 of subtile it, interleaved with the scores,
+      //      reference max and P of subtile it+1
+      bf16x8_t Pn[2];
+      float mx = -INFINITY, ps = 0.f, m_new = m_run;
+      const int nv_n = nvalid_of(it + 1);
+#pragma unroll
+      for (int h = 0; h < 16; ++h) {
+        const int step = 16 + h;
+        mfma_acc(acc[step & 15], va[step & 1], P[1]);
+        if (step + 2 < 32) va[step & 1] = vfrag(tile, step + 2);
+        if (h < 8) {
+          score(sc, 2 * h, nv_n, mx);
+          score(sc, 2 * h + 1, nv_n, mx);
+          if (h == 7) {
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            m_new = mx > m_run + kTau ? mx : m_run;  // lazy: keep the reference unless far behind
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 2 * (h - 8) + e;
+            const float p = __builtin_amdgcn_exp2f(sc[r] - m_new);
+            ps += p;
+            Pn[r >> 3][r & 7] = (__bf16)p;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // ---- (Z) rare: the reference max moved; rescale O and the row sum
+      if (m_new != m_run) {
+        const float f = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= f;
+        acc_fence(acc);
+#pragma unroll
+        for (int d = 0; d < 16; ++d) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[d][r] *= f;
+          asm volatile("" : "+a"(acc[d]));
+        }
+        acc_fence(acc);
+        m_run = m_new;
+      }
+      l_run += ps;
+      P[0] = Pn[0];
+      P[1] = Pn[1];
+    }
+    if (n_sub > 0) {  // the last subtile: P.V only
+      const lds_u8* tile = tile_of(n_sub - 1);
+      bf16x8_t va[2] = {vfrag(tile, 0), vfrag(tile, 1)};
+#pragma unroll
+      for (int step = 0; step < 32; ++step) {
+        mfma_acc(acc[step & 15], va[step & 1], P[step >> 4]);
+        if (step + 2 < 32) va[step & 1] = vfrag(tile, step + 2);
+      }
+    }
+
+    // ---- finalize: normalise, stage rows through LDS, store whole rows
+    acc_fence(acc);
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    const long long orow0 = ((long long)b * a.s_q + qi) * kHeads;  // first output row of this (b, qi)
+    const bool final_out = wk.w < 0;
+    const long long prow0 = (long long)wk.w * R + qi * kHeads;
+    const bool bf16_out = final_out && a.out_dtype != 0;
+    float* o32 = final_out ? (float*)a.out + orow0 * kDc : a.o_part + prow0 * kDc;
+    uint16_t* o16 = (uint16_t*)a.out + orow0 * kDc;
+    if (g == 0) {
+      if (!final_out)
+        a.lse_part[prow0 + head] = lse_v;
+      else if (a.lse)
+        a.lse[orow0 + head] = lse_v;
+    }
+    __syncthreads();  // every wave is done with the tiles
+    typedef __attribute__((address_space(3))) f32x4_t lds_f4;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if ((w >> 1) == pass) {
+        lds_u8* rowp = smem + (size_t)((w & 1) * 32 + l32) * kOutRowF * 4;
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+          asm volatile("" : "+a"(acc[db]));  // one block at a time
+          const f32x16_t t = acc[db];
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            f32x4_t v;
+            v[0] = t[4 * qd] * inv; v[1] = t[4 * qd + 1] * inv; v[2] = t[4 * qd + 2] * inv; v[3] = t[4 * qd + 3] * inv;
+            *(lds_f4*)(rowp + (db * 32 + 8 * qd + 4 * g) * 4) = v;
+          }
+        }
+      }
+      __syncthreads();
+      // 64 staged rows (heads 64*pass ..) x 512 floats: 128 threads per row, 16 B each
+#pragma unroll 4
+      for (int e = tid; e < 64 * (kDc / 4); e += 256) {
+        const int r = e / (kDc / 4), c4 = e % (kDc / 4);
+        const f32x4_t v = *(const lds_f4*)(smem + ((size_t)r * kOutRowF + 4 * c4) * 4);
+        const long long row = 64 * pass + r;
+        if (bf16_out) {
+          uint2 pk;
+          pk.x = f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+          pk.y = f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+          *(uint2*)(o16 + row * kDc + 4 * c4) = pk;
+        } else {
+          *(float4*)(o32 + row * kDc + 4 * c4) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, int grid_x, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)decode_bf16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       kB16Lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(decode_bf16_kernel, dim3(grid_x, a.s_q), dim3(256), kB16Lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

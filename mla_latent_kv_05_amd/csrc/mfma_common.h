@@ -1,0 +1,121 @@
+// Shared pieces of the MFMA decode kernels (bf16 and fp8 caches): tile
+// geometry, the LDS swizzle, global->LDS DMA, and the MFMA wrappers.
+#pragma once
+#include "device_util.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) int lds_i32;
+
+constexpr int kHeads = 128;
+constexpr int kDc = 512;
+constexpr int kDr = 64;
+constexpr int kBlk = 64;                          // tokens per page
+constexpr int kSub = 32;                          // tokens per subtile
+constexpr int kRowB = (kDc + kDr) * 2;            // 1152
+constexpr int kTileB = kSub * kRowB;              // 36864
+constexpr int kStages = 4;
+constexpr int kBf16Dma = kTileB / (4 * 1024);     // 9 DMA instructions per wave per subtile
+// fp8 staging per subtile: codes | k^R | scales
+constexpr int kF8Codes = kSub * kDc;              // 16384
+constexpr int kF8Kr = kSub * kDr * 2;             // 4096
+constexpr int kF8Stage = kF8Codes + kF8Kr + 256;  // 20736 (scales + pad)
+constexpr int kF8Dma = 6;                         // 4 code + 1 k^R + 1 scale instruction per wave
+constexpr float kTau = 8.0f;                      // lazy-rescale threshold (log2 units)
+constexpr int kMaxUnitPages = 512;                // page ids cached in LDS per unit (32768 tokens)
+
+constexpr int kQrStride = kDr * 2 + 16;            // padded bytes per head of the LDS q_rope copy (fp8)
+constexpr int kTabOff(bool fp8) { return fp8 ? kStages * kF8Stage + kTileB : kStages * kTileB; }
+constexpr int kQrOff(bool fp8) { return kTabOff(fp8) + kMaxUnitPages * 4; }
+constexpr int kLdsBytes(bool fp8) { return kQrOff(fp8) + (fp8 ? kHeads * kQrStride : 0); }
+
+__device__ __forceinline__ int swz_f(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
+
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base) {
+  const uint64_t a = (uint64_t)base;
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));  // stride 0
+  r[2] = -1;                                                        // num_records: no clamping
+  r[3] = 0x00020000;                                                // gfx9 raw buffer config
+  return r;
+}
+
+// 16-byte global -> LDS DMA (buffer_load_dwordx4 ... lds): lane l's 16 bytes
+// from rsrc.base + voff land at LDS address m0 + 16*l.  Issued as inline asm so
+// that the compiler does not add its own vmcnt waits in front of later LDS
+// reads; completion is tracked explicitly with wait_vm<>() + a barrier.  The
+// leading s_nop covers the VALU-writes-SGPR -> VMEM-reads-SGPR hazard on the
+// resource, the one after the M0 write the SALU-writes-M0 -> LDS-DMA hazard.
+__device__ __forceinline__ void dma16(i32x4_t rsrc, int voff, lds_u8* l) {
+  const int m0v = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)l);
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v),
+      "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) only (gfx9 encoding: expcnt/lgkmcnt at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int G>
+__device__ __forceinline__ void wait_groups(int outstanding) {
+  static_assert(kStages == 4, "wait table assumes 4 stages");
+  if (outstanding >= 2)
+    wait_vm<2 * G>();
+  else if (outstanding == 1)
+    wait_vm<G>();
+  else
+    wait_vm<0>();
+}
+
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// P.V accumulation with the accumulator pinned to AGPRs (the 16 blocks fill
+// the whole AGPR file, leaving every VGPR for queries and temporaries).  The
+// s_nop provides the 2 wait states a VALU-written VGPR needs before an MFMA
+// reads it as A/B; back-to-back accumulation into the same AGPRs with the same
+// opcode needs none.
+__device__ __forceinline__ void mfma_acc(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Orders VALU/accvgpr access to the AGPR accumulator after (or before) the
+// asm MFMAs above: 24 wait states cover the MFMA-writes-AGPR ->
+// v_accvgpr_read and v_accvgpr_write -> MFMA-reads-SrcC hazards.
+__device__ __forceinline__ void acc_fence(f32x16_t* acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]), "+a"(acc[5]),
+                 "+a"(acc[6]), "+a"(acc[7]), "+a"(acc[8]), "+a"(acc[9]), "+a"(acc[10]), "+a"(acc[11]),
+                 "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]), "+a"(acc[15]));
+}
+
+__device__ __forceinline__ bf16x8_t lds_b128(const lds_u8* p) {
+  return *(const __attribute__((address_space(3))) bf16x8_t*)p;
+}
+__device__ __forceinline__ bf16x4_t lds_tr16(const lds_u8* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p);
+}
+
+// two e4m3fn codes (bytes 0,1 or 2,3 of w) -> packed bf16 pair (exact)
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+
+
+}  // namespace mla

@@ -59,12 +59,22 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* q, lon
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31, j16 = lane & 15, G = lane >> 4;
   const int ncols = min(kAbsCols, d_c - c0);
-  // stage W rows k = 0..d_h-1, columns c0..c0+ncols (16-byte pieces)
+  // stage W rows k = 0..d_h-1, columns c0..c0+ncols (16-byte pieces); the
+  // loads of one batch are all issued before any LDS store
   const int pieces = ncols / 8;
-  for (int e = tid; e < d_h * pieces; e += 256) {
-    const int k = e / pieces, pc = e % pieces;
-    const u32x4_t v = *(const u32x4_t*)(w + ((long long)(h * d_h + k)) * d_c + c0 + pc * 8);
-    *(__attribute__((address_space(3))) u32x4_t*)(wl + (k * kAbsStride + pc * 8) * 2) = v;
+  const int total = d_h * pieces;
+  for (int e0 = 0; e0 < total; e0 += 256 * 8) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = e0 + j * 256 + tid;
+      if (e < total) v[j] = *(const u32x4_t*)(w + ((long long)(h * d_h + e / pieces)) * d_c + c0 + (e % pieces) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = e0 + j * 256 + tid;
+      if (e < total) *(__attribute__((address_space(3))) u32x4_t*)(wl + ((e / pieces) * kAbsStride + (e % pieces) * 8) * 2) = v[j];
+    }
   }
   __syncthreads();
   const int cw = 32 * wv;  // this wave's column offset within the block
@@ -101,38 +111,53 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* q, lon
 }
 
 // ------------------------------------------------------------ MFMA up-projection
-// Workgroup = head h; wave w covers output rows k = 32w .. 32w+31 of W^UV_h
-// (d_h = 128 -> 4 waves; larger d_h loops).  B[c][k] = W^UV[h*d_h + k][c] is
-// contiguous along c, so both operands load straight from global memory.
+// Workgroup = (head h, 32-row block k0 of W^UV_h).  The 4 waves split the d_c
+// reduction into quarters; each keeps its W slice (32 rows x d_c/4) in
+// registers for all T_q tiles, and the quarter sums are added through LDS.
+// B[c][k] = W^UV[h*d_h + k][c] is contiguous along c, so both operands load
+// straight from global memory.
+constexpr int kUpMaxCb = 8;  // d_c / 64 (16-wide k-steps per wave) up to d_c = 512
+
 __global__ __launch_bounds__(256) void up_mfma_kernel(const uint16_t* a, long long a_st, const uint16_t* w,
                                                       void* out, long long o_st, int T, int n_h, int d_c,
                                                       int d_h, int out_dt) {
-  const int h = blockIdx.y;
+  __shared__ float red[4][32 * 33];
+  const int h = blockIdx.y, k0 = blockIdx.x * 32;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  for (int k0 = (blockIdx.x * 4 + wv) * 32; k0 < d_h; k0 += gridDim.x * 4 * 32) {
-    const uint16_t* wrow = w + ((long long)(h * d_h + k0 + l32)) * d_c + g * 8;
-    for (int t0 = 0; t0 < T; t0 += 32) {
-      f32x16_t acc;
+  const int ncb = d_c / 64;                  // k-steps of this wave
+  const int cbase = wv * ncb * 16;           // first d_c column of this wave
+  const uint16_t* wrow = w + ((long long)(h * d_h + k0 + l32)) * d_c + cbase + g * 8;
+  bf16x8_t wf[kUpMaxCb];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-      const int tr = t0 + l32;
-      const bool tv = tr < T;
-      const uint16_t* arow = a + tr * a_st + (long long)h * d_c + g * 8;
-#pragma unroll 4
-      for (int cb = 0; cb < d_c / 16; ++cb) {
-        bf16x8_t av;
-        if (tv) av = *(const bf16x8_t*)(arow + cb * 16);
-        else for (int j = 0; j < 8; ++j) av[j] = (__bf16)0.f;
-        const bf16x8_t bv = *(const bf16x8_t*)(wrow + cb * 16);
-        acc = mfma16(av, bv, acc);
-      }
+  for (int cb = 0; cb < kUpMaxCb; ++cb)
+    if (cb < ncb) wf[cb] = *(const bf16x8_t*)(wrow + cb * 16);
+  for (int t0 = 0; t0 < T; t0 += 32) {
+    const int tr = t0 + l32;
+    const uint16_t* arow = a + (long long)tr * a_st + (long long)h * d_c + cbase + g * 8;
+    bf16x8_t af[kUpMaxCb];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = t0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (t < T) store_elem(out, t * o_st + (long long)h * d_h + k0 + l32, acc[r], out_dt);
-      }
+    for (int cb = 0; cb < kUpMaxCb; ++cb) {
+      if (cb < ncb && tr < T) af[cb] = *(const bf16x8_t*)(arow + cb * 16);
+      else for (int j = 0; j < 8; ++j) af[cb][j] = (__bf16)0.f;
     }
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < kUpMaxCb; ++cb)
+      if (cb < ncb) acc = mfma16(af[cb], wf[cb], acc);
+    // D[i = t][j = k]: lane column k0 + l32, rows 8(r/4) + 4g + r%4
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wv][(8 * (r >> 2) + 4 * g + (r & 3)) * 33 + l32] = acc[r];
+    __syncthreads();
+    for (int e = threadIdx.x; e < 32 * 32; e += 256) {
+      const int i = e >> 5, j = e & 31;
+      const int t = t0 + i;
+      const float v = red[0][i * 33 + j] + red[1][i * 33 + j] + red[2][i * 33 + j] + red[3][i * 33 + j];
+      if (t < T) store_elem(out, (long long)t * o_st + (long long)h * d_h + k0 + j, v, out_dt);
+    }
+    __syncthreads();
   }
 }
 
@@ -156,8 +181,7 @@ hipError_t launch_up_proj(const void* o_lat, long long a_st, const void* w, void
                           int T, int n_h, int d_c, int d_h, int act_dt, int w_dt, int out_dt, bool mfma,
                           hipStream_t s) {
   if (mfma) {
-    const int wgs = (d_h + 127) / 128;
-    hipLaunchKernelGGL(up_mfma_kernel, dim3(wgs, n_h), dim3(256), 0, s, (const uint16_t*)o_lat, a_st,
+    hipLaunchKernelGGL(up_mfma_kernel, dim3(d_h / 32, n_h), dim3(256), 0, s, (const uint16_t*)o_lat, a_st,
                        (const uint16_t*)w, out, o_st, T, n_h, d_c, d_h, out_dt);
   } else {
     const long long total = (long long)T * n_h * d_h;

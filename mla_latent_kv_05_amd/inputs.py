@@ -47,8 +47,10 @@ def f32_to_bf16_bits(x) -> np.ndarray:
 
     Returns the raw 16-bit patterns as uint16.  NaN stays NaN."""
     a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = a.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = a.view(np.uint32)
+    # finite values cannot wrap in uint32 (max 0xFF7FFFFF + 0x8000); NaNs are fixed below
+    with np.errstate(over="ignore"):
+        rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     out = rounded.astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
@@ -92,15 +94,23 @@ def encode_e4m3fn(x) -> np.ndarray:
     return (code | sign).astype(np.uint8)
 
 
+def encode_e4m3fn_fast(x32: np.ndarray) -> np.ndarray:
+    """encode_e4m3fn for float32 inputs via torch's round-to-nearest-even cast
+    (the two agree bit for bit on float32 values; see tests/test_inputs.py)."""
+    import torch
+    t = torch.from_numpy(np.clip(np.ascontiguousarray(x32, dtype=np.float32), -E4M3_MAX, E4M3_MAX))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
 def quantize_rows_e4m3(c) -> tuple[np.ndarray, np.ndarray]:
     """Per-token fp8 quantisation of content rows ``c`` [..., d_c].
 
     scale_t = amax_t / 448 in fp32 (1.0 for an all-zero row),
-    code = e4m3fn(c / scale_t)."""
+    code = e4m3fn(c / scale_t) with the quotient formed in fp32."""
     c = np.asarray(c, dtype=np.float32)
     amax = np.abs(c).max(axis=-1)
     scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    codes = encode_e4m3fn(c.astype(np.float64) / scale.astype(np.float64)[..., None])
+    codes = encode_e4m3fn_fast(c / scale[..., None])
     return codes, scale
 
 
@@ -214,23 +224,33 @@ def decode_case(seed: int, B: int, seq_lens, s_q: int = 1, n_h: int = 128,
         k += nblk[b]
     D = d_c + d_r
     kind = "f32" if (kv_dtype != "f32" and q_dtype != "f32") else "f64"
-    rows = _draw(rng, (num_blocks, block_size, D), 1.0, kind)
+    # the cache is drawn block-chunk by block-chunk (one continuous random
+    # stream) straight into its storage array
     if kv_dtype == "bf16":
-        cache = f32_to_bf16_bits(rows)
+        cache = np.empty((num_blocks, block_size, D), dtype=np.uint16)
     elif kv_dtype == "f32":
-        cache = rows.astype(np.float32)
+        cache = np.empty((num_blocks, block_size, D), dtype=np.float32)
     elif kv_dtype == "fp8":
-        codes, scale = quantize_rows_e4m3(rows[..., :d_c])
-        kr = f32_to_bf16_bits(rows[..., d_c:])
-        blk = np.empty((num_blocks, block_size * (d_c + 2 * d_r + 4)), dtype=np.uint8)
-        o1 = block_size * d_c
-        o2 = o1 + block_size * d_r * 2
-        blk[:, :o1] = codes.reshape(num_blocks, -1)
-        blk[:, o1:o2] = kr.reshape(num_blocks, -1).view(np.uint8).reshape(num_blocks, -1)
-        blk[:, o2:] = scale.reshape(num_blocks, -1).view(np.uint8).reshape(num_blocks, -1)
-        cache = blk
+        cache = np.empty((num_blocks, block_size * (d_c + 2 * d_r + 4)), dtype=np.uint8)
     else:
         raise ValueError(kv_dtype)
+    chunk = 32
+    for i0 in range(0, num_blocks, chunk):
+        i1 = min(num_blocks, i0 + chunk)
+        rows = _draw(rng, (i1 - i0, block_size, D), 1.0, kind)
+        if kv_dtype == "bf16":
+            cache[i0:i1] = f32_to_bf16_bits(rows)
+        elif kv_dtype == "f32":
+            cache[i0:i1] = rows
+        else:
+            n = i1 - i0
+            codes, scale = quantize_rows_e4m3(rows[..., :d_c])
+            kr = f32_to_bf16_bits(rows[..., d_c:])
+            o1 = block_size * d_c
+            o2 = o1 + block_size * d_r * 2
+            cache[i0:i1, :o1] = codes.reshape(n, -1)
+            cache[i0:i1, o1:o2] = kr.reshape(n, -1).view(np.uint8).reshape(n, -1)
+            cache[i0:i1, o2:] = scale.reshape(n, -1).view(np.uint8).reshape(n, -1)
     if tail_fill == "nan" and kv_dtype in ("bf16", "f32"):
         for b in range(B):
             used = lens[b] - (nblk[b] - 1) * block_size

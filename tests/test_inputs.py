@@ -45,6 +45,9 @@ def test_e4m3_encoder_matches_torch():
     # torch rounds from float32; compare where the float32 value is exact
     exact = x.astype(np.float32).astype(np.float64) == x
     assert np.array_equal(ours[exact], ref[exact])
+    # the bulk path used for large caches agrees on every float32 input
+    x32 = x.astype(np.float32)
+    assert np.array_equal(inputs.encode_e4m3fn_fast(x32), inputs.encode_e4m3fn(x32.astype(np.float64)))
 
 
 def test_workload_shapes():
