@@ -14,7 +14,8 @@
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *    never allocates, frees or retains memory; it keeps no state between calls
- *    apart from a per-device cache of kernel attributes.
+ *    apart from a per-device cache of kernel attributes and the profiling
+ *    events armed by mla_decode_kernel_events (per host thread).
  *  - Every call enqueues work on `stream` (a hipStream_t passed as void*; NULL
  *    is the default stream) and returns without synchronising.
  *  - Tensors are row-major with the last dimension contiguous.  Strides are
@@ -134,6 +135,18 @@ int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_ca
                         int block_size, float softmax_scale, int q_dtype, int kv_dtype,
                         int out_dtype, int num_splits, void* workspace, size_t workspace_bytes,
                         void* o_lat, float* lse, int flags, void* stream);
+
+/*
+ * mla_decode_kernel_events -- profiling aid.  Arms two caller-owned HIP
+ * events (hipEvent_t passed as void*) for the next mla_decode_absorbed call
+ * made by the calling host thread: that call records `before` on its stream
+ * just before it launches its attention kernel and `after` just after, so the
+ * elapsed time between them covers that one kernel (the split planner and the
+ * partial-result merge are outside), and then disarms.  NULL, NULL disarms.
+ * The events must stay valid until that call has returned; the library does
+ * not retain them afterwards.  Always returns MLA_OK.
+ */
+int mla_decode_kernel_events(void* before, void* after);
 
 /*
  * mla_combine_lse -- merge split-KV partial results (log-sum-exp combine):

@@ -37,6 +37,7 @@ _SIGS = {
                                        _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
     "mla_combine_lse": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int,
                                    _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
+    "mla_decode_kernel_events": (_c.c_int, [_c.c_void_p, _c.c_void_p]),
 }
 
 
@@ -179,6 +180,16 @@ def decode(q_lat: torch.Tensor, q_rope: torch.Tensor, kv_cache: torch.Tensor, bl
                                      workspace.numel(), _ptr(out), _ptr(lse) if with_lse else None, flags,
                                      _stream()), "mla_decode_absorbed")
     return out, (lse if with_lse else None)
+
+
+def decode_kernel_events(before: torch.cuda.Event, after: torch.cuda.Event) -> None:
+    """Arm two timing events for the attention kernel of the next decode()
+    call on this thread (see mla_decode_kernel_events).  The events must
+    already exist on the device: record each once beforehand."""
+    h0, h1 = before.cuda_event, after.cuda_event
+    if not h0 or not h1:
+        raise RuntimeError("record the events once before arming them")
+    _check(lib().mla_decode_kernel_events(h0, h1), "mla_decode_kernel_events")
 
 
 def combine_lse(o_part: torch.Tensor, lse_part: torch.Tensor, splits_per_row: torch.Tensor | None = None,

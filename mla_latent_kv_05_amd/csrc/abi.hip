@@ -116,6 +116,17 @@ size_t mla_decode_workspace_bytes(int B, int s_q, int n_h, int d_c, int max_bloc
   return layout_for(s, n_cu).total;
 }
 
+namespace {
+thread_local hipEvent_t g_kernel_ev_before = nullptr;
+thread_local hipEvent_t g_kernel_ev_after = nullptr;
+}  // namespace
+
+int mla_decode_kernel_events(void* before, void* after) {
+  g_kernel_ev_before = (hipEvent_t)before;
+  g_kernel_ev_after = (hipEvent_t)after;
+  return MLA_OK;
+}
+
 int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_cache, const int32_t* block_table,
                         int max_blocks_per_seq, const int32_t* seq_lens, int B, int s_q, int n_h, int d_c,
                         int d_r, int block_size, float softmax_scale, int q_dtype, int kv_dtype, int out_dtype,
@@ -165,6 +176,9 @@ int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_ca
   a.B = B; a.s_q = s_q; a.n_h = n_h; a.d_c = d_c; a.d_r = d_r; a.block_size = block_size;
   a.scale = softmax_scale;
   a.q_dtype = q_dtype; a.kv_dtype = kv_dtype; a.out_dtype = out_dtype;
+  // the bf16-cache MFMA kernel writes bf16 partial rows when the merged
+  // output is bf16 anyway (half the partial-result traffic)
+  a.part_bf16 = (fast && kv_dtype == MLA_BF16 && out_dtype == MLA_BF16) ? 1 : 0;
 
   hipStream_t st = (hipStream_t)stream;
   const int grid_x = fast ? (n_cu / s_q > 0 ? n_cu / s_q : 1) : (L.units_max < n_cu ? L.units_max : n_cu);
@@ -183,8 +197,12 @@ int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_ca
   p.units_max = L.units_max;
   hipError_t e = launch_plan(p, st);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  hipEvent_t ev0 = g_kernel_ev_before, ev1 = g_kernel_ev_after;
+  g_kernel_ev_before = g_kernel_ev_after = nullptr;
+  if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return MLA_ERR_LAUNCH;
   e = fast ? launch_decode_mfma(a, grid_x, st) : launch_decode_generic(a, grid_x, st);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return MLA_ERR_LAUNCH;
   e = launch_combine_units(a, st);
   return launch_status(e);
 }

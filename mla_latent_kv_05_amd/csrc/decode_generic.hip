@@ -55,7 +55,7 @@ __device__ __forceinline__ int units_of(const PlanArgs& a, int n, int chunk) {
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int nb[kPlanLdsSeqs];
   __shared__ unsigned long long red[kPlanThreads / 64];
-  __shared__ int scan[kPlanThreads];
+  __shared__ int scan[kPlanThreads / 64];
   __shared__ int s_chunk, s_waves;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const bool in_lds = a.B <= kPlanLdsSeqs;
@@ -66,8 +66,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (in_lds) nb[b] = n;
     max_n = max(max_n, n);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) max_n = max(max_n, __shfl_xor(max_n, o, 64));
+  max_n = __reduce_max_sync(~0ull, max_n);
   if (lane == 0) red[wv] = (unsigned long long)max_n;
   __syncthreads();
   max_n = 0;
@@ -78,34 +77,54 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int hi = min(max_n, a.max_chunk);
     const int lo = max(1, min(a.min_chunk, hi));
     const int overhead = 4;
-    unsigned long long best = ~0ull;  // key = cost << 32 | (0xffffffff - c)
-    for (int c = lo + tid; c <= hi; c += kPlanThreads) {
+    // waves(c) does not grow with c and the cost grows with c inside each
+    // interval of equal waves, except where the split overhead drops (c >=
+    // the longest sequence).  So the cheapest c is the smallest c reaching
+    // waves <= w for some w in 1..kMaxAutoWaves (a binary search each, one
+    // wave per w), or c = min(hi, max_n), or the forced fallback c = hi.
+    unsigned long long best = ~0ull;  // key = cost << 32 | (0xffff - c) << 8 | waves
+    const int nb_lane = (in_lds && lane < a.B) ? nb[lane] : 0;
+    auto units_at = [&](int c) {
       const float rc = 1.0f / (float)c;
-      int u = 0;
-      for (int b = 0; b < a.B; ++b) u += ceil_div_small(in_lds ? nb[b] : nblocks_of(a, b), c, rc);
+      int v = 0;
+      if (a.B <= 64)
+        v = lane < a.B ? ceil_div_small(nb_lane, c, rc) : 0;
+      else
+        for (int b = lane; b < a.B; b += 64) v += ceil_div_small(in_lds ? nb[b] : nblocks_of(a, b), c, rc);
+      return __reduce_add_sync(~0ull, v);  // DPP wave sum, uniform result
+    };
+    auto consider = [&](int c, int u) {
       const int waves = (u + a.slots_per_wave - 1) / a.slots_per_wave;
-      if (waves > kMaxAutoWaves && c != hi) continue;
+      if (waves > kMaxAutoWaves && c != hi) return;
       const unsigned long long cost = (unsigned long long)waves * (unsigned)(c + (u > a.B ? overhead : 0));
-      const unsigned long long key = (cost << 32) | (0xffffffffu - (unsigned)c);
+      // ties on cost go to the larger c; the low byte carries waves (diagnostic)
+      const unsigned long long key = (cost << 32) | ((unsigned long long)(0xffffu - (unsigned)c) << 8) |
+                                     (unsigned)min(waves, 255);
       best = key < best ? key : best;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const unsigned long long other = __shfl_xor(best, o, 64);
-      best = other < best ? other : best;
+    };
+    if (wv < kMaxAutoWaves) {
+      const long long cap = (long long)(wv + 1) * a.slots_per_wave;
+      int l = lo, h = hi;  // smallest c in [l, h] with units(c) <= cap, if units(hi) <= cap
+      if (units_at(hi) <= cap) {
+        while (l < h) {
+          const int mid = (l + h) >> 1;
+          if (units_at(mid) <= cap) h = mid; else l = mid + 1;
+        }
+        consider(l, units_at(l));
+      }
+    } else if (wv == kMaxAutoWaves) {
+      const int c1 = min(hi, max_n);
+      consider(c1, units_at(c1));
+      consider(hi, units_at(hi));
     }
     if (lane == 0) red[wv] = best;
     __syncthreads();
     if (tid == 0) {
       unsigned long long m = ~0ull;
       for (int i = 0; i < kPlanThreads / 64; ++i) m = red[i] < m ? red[i] : m;
-      const int c = (int)(0xffffffffu - (unsigned)(m & 0xffffffffu));
-      int u = 0;
-      for (int b = 0; b < a.B; ++b) u += ((in_lds ? nb[b] : nblocks_of(a, b)) + c - 1) / c;
-      s_chunk = c;
-      s_waves = (u + a.slots_per_wave - 1) / a.slots_per_wave;
+      s_chunk = (int)(0xffffu - (unsigned)((m >> 8) & 0xffffu));
+      s_waves = (int)(m & 0xffu);
     }
-    __syncthreads();
   } else if (tid == 0) {
     s_chunk = 0;
     s_waves = 0;
@@ -118,15 +137,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int b0 = tid * per, b1 = min(a.B, b0 + per);
   int local = 0;
   for (int b = b0; b < b1; ++b) local += units_of(a, in_lds ? nb[b] : nblocks_of(a, b), chunk);
-  scan[tid] = local;
-  __syncthreads();
-  for (int o = 1; o < kPlanThreads; o <<= 1) {
-    int v = tid >= o ? scan[tid - o] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
+  // inclusive scan: within each wave by shuffles, then across the waves
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
   }
-  int first = scan[tid] - local;
+  if (lane == 63) scan[wv] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < wv; ++i) before += scan[i];
+  const int total = [&] { int t = 0; for (int i = 0; i < kPlanThreads / 64; ++i) t += scan[i]; return t; }();
+  incl += before;
+  int first = incl - local;
   for (int b = b0; b < b1; ++b) {
     const int n = in_lds ? nb[b] : nblocks_of(a, b);
     const int u = units_of(a, n, chunk);
@@ -140,7 +164,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   if (tid == kPlanThreads - 1) {
     WsHeader* h = (WsHeader*)a.ws_header;
-    h->n_units = scan[tid];
+    h->n_units = total;
     h->chunk_blocks = chunk;
     h->waves = s_waves;
   }
@@ -303,6 +327,31 @@ __device__ __forceinline__ void merge_row(const float* o_base, long long o_strid
   lse_out = z > 0.f ? m + logf(z) : -INFINITY;
 }
 
+// the same merge over bf16 partial rows
+__device__ __forceinline__ void merge_row_bf16(const uint16_t* o_base, long long o_stride,
+                                               const float* l_base, long long l_stride, int S,
+                                               int c4, float4& out, float& lse_out) {
+  float m = -INFINITY;
+  for (int k = 0; k < S; ++k) m = fmaxf(m, l_base[k * l_stride]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float z = 0.f;
+  if (m != -INFINITY) {
+    for (int k = 0; k < S; ++k) {
+      const float w = expf(l_base[k * l_stride] - m);
+      if (w == 0.f) continue;
+      const uint2 pk = ((const uint2*)(o_base + k * o_stride))[c4];
+      acc.x += w * bf16_bits_to_f32((uint16_t)(pk.x & 0xffffu));
+      acc.y += w * bf16_bits_to_f32((uint16_t)(pk.x >> 16));
+      acc.z += w * bf16_bits_to_f32((uint16_t)(pk.y & 0xffffu));
+      acc.w += w * bf16_bits_to_f32((uint16_t)(pk.y >> 16));
+      z += w;
+    }
+  }
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  out = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  lse_out = z > 0.f ? m + logf(z) : -INFINITY;
+}
+
 __device__ __forceinline__ void store4(void* out, long long base, float4 v, int dt) {
   if (dt == 0) {
     *(float4*)((float*)out + base) = v;
@@ -329,8 +378,11 @@ __global__ __launch_bounds__(256) void combine_units_kernel(DecodeArgs a) {
   const long long prow = (long long)sq.x * R + r;
   float4 o;
   float lse_v;
-  merge_row(a.o_part + prow * a.d_c, (long long)R * a.d_c, a.lse_part + prow, R, sq.y, c4, o,
-            lse_v);
+  if (a.part_bf16)
+    merge_row_bf16((const uint16_t*)a.o_part + prow * a.d_c, (long long)R * a.d_c, a.lse_part + prow, R, sq.y,
+                   c4, o, lse_v);
+  else
+    merge_row(a.o_part + prow * a.d_c, (long long)R * a.d_c, a.lse_part + prow, R, sq.y, c4, o, lse_v);
   const long long orow = ((long long)b * a.s_q + qi) * a.n_h + h;
   store4(a.out, orow * a.d_c + 4 * c4, o, a.out_dtype);
   if (c4 == 0 && a.lse) a.lse[orow] = lse_v;

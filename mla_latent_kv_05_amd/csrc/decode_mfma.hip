@@ -80,7 +80,7 @@ void decode_mfma_kernel(DecodeArgs a) {
     goff2[i >> 1] |= (uint32_t)(t * kRowB + c * 16) << (16 * (i & 1));
   }
 
-  for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+  for (int unit = xcd_slot(blockIdx.x, gridDim.x); unit < n_units; unit += gridDim.x) {
     const int4 wk = a.work[unit];
     const int b = wk.x;
     const int L = a.seq_lens[b];

@@ -18,9 +18,9 @@ namespace mla {
 constexpr int kB16Stages = 4;                               // tiles i, i+1 in use, i+2, i+3 in flight
 constexpr int kB16TabOff = kB16Stages * kTileB;             // 147456
 constexpr int kB16Pages = kMaxUnitPages;                    // page ids cached in LDS per unit
-constexpr int kB16GoffOff = kB16TabOff + kB16Pages * 4;     // 149504: per-thread DMA offsets
-constexpr int kB16Lds = kB16GoffOff + 256 * 20;             // 154624
+constexpr int kB16Lds = kB16TabOff + kB16Pages * 4;         // 149504
 constexpr int kOutRowF = kDc + 4;                           // padded fp32 row of the output staging
+constexpr int kOutRowH = kDc * 2 + 16;                      // padded bf16 row (bytes)
 
 // s_waitcnt vmcnt for "at most n DMA groups of this kernel still in flight"
 __device__ __forceinline__ void wait_b16_groups(int n) {
@@ -63,26 +63,8 @@ void decode_bf16_kernel(DecodeArgs a) {
         off_pv[p][h] = t * kRowB + (((4 * p + clo) ^ swz_f(t)) << 4) + (j16 & 1) * 8;
       }
   }
-  // DMA source offset of each of this thread's 9 LDS chunks within a subtile
-  // (LDS chunk -> global chunk through the swizzle), kept in LDS as 16-bit
-  // pairs: 5 dwords per thread, written once
-  lds_u8* goff_lds = smem + kB16GoffOff + tid * 20;
-#pragma unroll
-  for (int i2 = 0; i2 < 5; ++i2) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = 2 * i2 + h;
-      if (i < kBf16Dma) {
-        const int p = (i * 4 + w) * 64 + lane;
-        const int t = p / 72;
-        v |= (uint32_t)((t * 72 + ((p - t * 72) ^ swz_f(t))) * 16) << (16 * h);
-      }
-    }
-    *(__attribute__((address_space(3))) uint32_t*)(goff_lds + 4 * i2) = v;
-  }
-
-  for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+  const int w_s = __builtin_amdgcn_readfirstlane(w);  // wave index as a scalar
+  for (int unit = xcd_slot(blockIdx.x, gridDim.x); unit < n_units; unit += gridDim.x) {
     const int4 wk = a.work[unit];
     const int b = wk.x;
     const int L = a.seq_lens[b];
@@ -105,13 +87,10 @@ void decode_bf16_kernel(DecodeArgs a) {
     auto issue = [&](int s) {
       const int pg = __builtin_amdgcn_readfirstlane(tab[s >> 1]);
       const uint8_t* blk = (const uint8_t*)a.kv + (long long)pg * a.block_bytes;
-      lds_u8* dst = smem + (s % kB16Stages) * kTileB + w * 1024;
+      lds_u8* dst = smem + (s % kB16Stages) * kTileB + w_s * 1024;
       const i32x4_t rs = make_rsrc(blk + (s & 1) * kTileB);
-      const u32x4_t o4 = *(const __attribute__((address_space(3))) u32x4_t*)goff_lds;
-      const uint32_t o5 = *(const __attribute__((address_space(3))) uint32_t*)(goff_lds + 16);
-      const uint32_t ow[5] = {o4[0], o4[1], o4[2], o4[3], o5};
 #pragma unroll
-      for (int i = 0; i < kBf16Dma; ++i) dma16(rs, (int)((ow[i >> 1] >> (16 * (i & 1))) & 0xffffu), dst + i * 4096);
+      for (int i = 0; i < kBf16Dma; ++i) dma16(rs, dma_src_offset(i * 256 + tid), dst + i * 4096);
     };
     auto tile_of = [&](int s) { return smem + (s % kB16Stages) * kTileB; };
     // zero the value rows of a ragged last subtile (they may hold NaN); all threads
@@ -125,33 +104,34 @@ void decode_bf16_kernel(DecodeArgs a) {
     };
 
     f32x16_t acc[16];
-#pragma unroll
-    for (int d = 0; d < 16; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
+    zero_acc(acc);
     acc_fence(acc);
     float m_run = -INFINITY, l_run = 0.f;
 
+    // queries first, then the first three subtiles: loads complete in issue
+    // order, so "at most the later subtiles' groups in flight" covers both
+    // the queries and subtile 0 (36 + 27 loads fit the 6-bit vmcnt)
+    bf16x8_t q[36];
+    {
+      // uniform row base + 32-bit per-lane offset (scalar base addressing)
+      const long long row0 = ((long long)b * a.s_q + qi) * kHeads;
+      const uint8_t* ql = (const uint8_t*)a.q_lat + row0 * (kDc * 2);
+      const uint8_t* qr = (const uint8_t*)a.q_rope + row0 * (kDr * 2);
+      // recomputed here rather than kept live across the unit loop
+      int hl = threadIdx.x;
+      asm volatile("" : "+v"(hl));
+      const int hd = (hl >> 6) * 32 + (hl & 31), gg = (hl >> 5) & 1;
+      const int ol = hd * (kDc * 2) + gg * 16, orp = hd * (kDr * 2) + gg * 16;
+#pragma unroll
+      for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8_t*)(ql + ol + kb * 32);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) q[32 + kb] = *(const bf16x8_t*)(qr + orp + kb * 32);
+    }
     if (n_sub > 0) {
 #pragma unroll
       for (int s = 0; s < kB16Stages - 1; ++s)
         if (s < n_sub) issue(s);
-    }
-    // queries (issued after the first DMA groups so the two latencies overlap)
-    bf16x8_t q[36];
-    {
-      const long long qrow = ((long long)b * a.s_q + qi) * kHeads + head;
-      const bf16x8_t* ql = (const bf16x8_t*)((const uint16_t*)a.q_lat + qrow * kDc);
-      const bf16x8_t* qr = (const bf16x8_t*)((const uint16_t*)a.q_rope + qrow * kDr);
-#pragma unroll
-      for (int kb = 0; kb < 32; ++kb) q[kb] = ql[2 * kb + g];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) q[32 + kb] = qr[2 * kb + g];
-    }
-    if (n_sub > 0) {
-      // the query loads are the newest: waiting for the groups after tile 0
-      // to be the only ones left would not cover them, so wait for all here
-      wait_vm<0>();
+      wait_b16_groups(min(2, n_sub - 1));
       __syncthreads();
       if (n_last < kSub && n_sub == 1) {
         zero_tail(0);
@@ -213,7 +193,19 @@ void decode_bf16_kernel(DecodeArgs a) {
       // ---- (A) next subtile resident; refill the stage subtile it-1 used
       wait_b16_groups(min(1, n_sub - 2 - it));
       __syncthreads();
-      if (it + 3 < n_sub) issue(it + 3);
+      // subtile it+3 goes to the stage subtile it-1 used; its 9 DMA
+      // instructions are spread over the QK steps below
+      const bool dma_on = it + 3 < n_sub;
+      i32x4_t dma_rs = {0, 0, 0, 0};
+      int dma_m0 = 0;
+      if (dma_on) {
+        const int s3 = it + 3;
+        const int pg = __builtin_amdgcn_readfirstlane(tab[s3 >> 1]);
+        dma_rs = make_rsrc((const uint8_t*)a.kv + (long long)pg * a.block_bytes + (s3 & 1) * kTileB);
+        dma_m0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(smem + (s3 % kB16Stages) * kTileB)) +
+                 w_s * 1024;
+        dma_fence();
+      }
       if (it + 1 == n_sub - 1 && n_last < kSub) {
         zero_tail(it + 1);
         __syncthreads();
@@ -234,6 +226,7 @@ void decode_bf16_kernel(DecodeArgs a) {
           const int f = 4 * k4 + j;
           sc = mfma(ka[f & 1], q[f], sc);
           if (f + 2 < 36) ka[f & 1] = kfrag(tile_n, f + 2);
+          if (j == 0 && dma_on) dma16_m0(dma_rs, dma_src_offset(k4 * 256 + tid), dma_m0 + k4 * 4096);
           if ((j & 1) && k4 < 8) {  // one P.V step after every second QK step
             const int step = 2 * k4 + (j >> 1);
             mfma_acc(acc[step & 15], va[step & 1], P[step >> 4]);
@@ -308,9 +301,9 @@ void decode_bf16_kernel(DecodeArgs a) {
     const long long orow0 = ((long long)b * a.s_q + qi) * kHeads;  // first output row of this (b, qi)
     const bool final_out = wk.w < 0;
     const long long prow0 = (long long)wk.w * R + qi * kHeads;
-    const bool bf16_out = final_out && a.out_dtype != 0;
+    const bool bf16_out = final_out ? a.out_dtype != 0 : a.part_bf16 != 0;
     float* o32 = final_out ? (float*)a.out + orow0 * kDc : a.o_part + prow0 * kDc;
-    uint16_t* o16 = (uint16_t*)a.out + orow0 * kDc;
+    uint16_t* o16 = final_out ? (uint16_t*)a.out + orow0 * kDc : (uint16_t*)a.o_part + prow0 * kDc;
     if (g == 0) {
       if (!final_out)
         a.lse_part[prow0 + head] = lse_v;
@@ -319,6 +312,32 @@ void decode_bf16_kernel(DecodeArgs a) {
     }
     __syncthreads();  // every wave is done with the tiles
     typedef __attribute__((address_space(3))) f32x4_t lds_f4;
+    typedef __attribute__((address_space(3))) u32x2_t lds_u2;
+    typedef __attribute__((address_space(3))) u32x4_t lds_u4;
+    if (bf16_out) {
+      // all 128 rows at once in bf16, then 16-byte stores of whole rows
+      lds_u8* rowp = smem + (size_t)(w * 32 + l32) * kOutRowH;
+#pragma unroll
+      for (int db = 0; db < 16; ++db) {
+        asm volatile("" : "+a"(acc[db]));  // one block at a time
+        const f32x16_t t = acc[db];
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          u32x2_t pk;
+          pk[0] = f32_to_bf16_bits(t[4 * qd] * inv) | ((uint32_t)f32_to_bf16_bits(t[4 * qd + 1] * inv) << 16);
+          pk[1] = f32_to_bf16_bits(t[4 * qd + 2] * inv) | ((uint32_t)f32_to_bf16_bits(t[4 * qd + 3] * inv) << 16);
+          *(lds_u2*)(rowp + (db * 32 + 8 * qd + 4 * g) * 2) = pk;
+        }
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int e = tid; e < kHeads * (kDc / 8); e += 256) {
+        const int r = e / (kDc / 8), c8 = e % (kDc / 8);
+        const u32x4_t v = *(const lds_u4*)(smem + (size_t)r * kOutRowH + c8 * 16);
+        *(u32x4_t*)(o16 + (long long)r * kDc + 8 * c8) = v;
+      }
+      continue;  // the next unit starts with a barrier before touching LDS
+    }
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
       if ((w >> 1) == pass) {
@@ -342,14 +361,7 @@ void decode_bf16_kernel(DecodeArgs a) {
         const int r = e / (kDc / 4), c4 = e % (kDc / 4);
         const f32x4_t v = *(const lds_f4*)(smem + ((size_t)r * kOutRowF + 4 * c4) * 4);
         const long long row = 64 * pass + r;
-        if (bf16_out) {
-          uint2 pk;
-          pk.x = f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-          pk.y = f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-          *(uint2*)(o16 + row * kDc + 4 * c4) = pk;
-        } else {
-          *(float4*)(o32 + row * kDc + 4 * c4) = make_float4(v[0], v[1], v[2], v[3]);
-        }
+        *(float4*)(o32 + row * kDc + 4 * c4) = make_float4(v[0], v[1], v[2], v[3]);
       }
       __syncthreads();
     }

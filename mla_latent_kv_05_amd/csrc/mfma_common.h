@@ -31,7 +31,9 @@ constexpr int kTabOff(bool fp8) { return fp8 ? kStages * kF8Stage + kTileB : kSt
 constexpr int kQrOff(bool fp8) { return kTabOff(fp8) + kMaxUnitPages * 4; }
 constexpr int kLdsBytes(bool fp8) { return kQrOff(fp8) + (fp8 ? kHeads * kQrStride : 0); }
 
-__device__ __forceinline__ int swz_f(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+// chunk swizzle of token row t (bits 2, 3, 1 of t -> bits 0, 1, 2): chosen by
+// measuring both LDS read patterns of the tile on gfx950
+__device__ __forceinline__ int swz_f(int t) { return ((t >> 2) & 1) | (((t >> 3) & 1) << 1) | (((t >> 1) & 1) << 2); }
 
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
 
@@ -61,6 +63,28 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, int voff, lds_u8* l) {
       "v"(voff), "s"(rsrc)
       : "memory", "m0");
 }
+
+// The same DMA with the LDS address already in an SGPR (computed with scalar
+// arithmetic from a wave-uniform base).  The caller issues dma_fence() once
+// after its resource descriptor was formed and before the first of these.
+__device__ __forceinline__ void dma16_m0(i32x4_t rsrc, int voff, int m0v) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v),
+      "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+// wait states between a VALU write of an SGPR (readfirstlane into the
+// resource descriptor) and a VMEM instruction that reads it
+__device__ __forceinline__ void dma_fence() { asm volatile("s_nop 4" ::: "memory"); }
+
+// byte offset, within a 32-token subtile of a page, of the 16-byte chunk that
+// thread slot p (0..2303) of the DMA deposits at LDS chunk p of the tile: the
+// swizzle only permutes the low 3 bits of the chunk index inside a row, and a
+// row is 72 chunks (a multiple of 8), so the source is p with those bits
+// flipped by the row's swizzle
+__device__ __forceinline__ int dma_src_offset(int p) { return (p ^ swz_f(p / 72)) << 4; }
 
 // s_waitcnt vmcnt(n) only (gfx9 encoding: expcnt/lgkmcnt at their maxima)
 template <int N>
@@ -101,6 +125,24 @@ __device__ __forceinline__ void acc_fence(f32x16_t* acc) {
                : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]), "+a"(acc[5]),
                  "+a"(acc[6]), "+a"(acc[7]), "+a"(acc[8]), "+a"(acc[9]), "+a"(acc[10]), "+a"(acc[11]),
                  "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]), "+a"(acc[15]));
+}
+
+// Zero the 16 accumulator blocks with MFMAs whose inputs are zero (AGPR
+// destinations, no VALU traffic through the accumulator file)
+__device__ __forceinline__ void zero_acc(f32x16_t* acc) {
+  bf16x8_t z = {};
+  asm volatile("" : "+v"(z));
+#pragma unroll
+  for (int d = 0; d < 16; ++d) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc[d]) : "v"(z));
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.
+// Renumber them so that consecutive work units (the partitions of one
+// sequence, which read the same query rows) run on one XCD.
+__device__ __forceinline__ int xcd_slot(int bid, int grid) {
+  constexpr int kXcd = 8;
+  if (grid % kXcd != 0) return bid;
+  return (bid % kXcd) * (grid / kXcd) + bid / kXcd;
 }
 
 __device__ __forceinline__ bf16x8_t lds_b128(const lds_u8* p) {

@@ -11,7 +11,8 @@ namespace mla {
 //   work          int4[units_max]    (b, first_block, end_block, slot)
 //   seq           int2[B]            (first unit, unit count)
 //   lse_part      float[units_max * R]
-//   o_part        float[units_max * R * d_c]
+//   o_part        float[units_max * R * d_c]  (bf16 rows when the decode kernel
+//                 writes bf16 partials; the space is sized for fp32)
 // with R = s_q * n_h rows per sequence.  slot = -1 marks a sequence that has
 // a single unit: that unit writes the final output directly.
 struct WsHeader {
@@ -63,7 +64,8 @@ struct DecodeArgs {
   const int4* work;
   const int2* seq;
   float* lse_part;
-  float* o_part;
+  float* o_part;       // fp32 rows, or bf16 rows when part_bf16
+  int part_bf16;
   long long block_bytes;
   int max_blocks;
   int B, s_q, n_h, d_c, d_r, block_size;

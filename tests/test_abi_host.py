@@ -19,7 +19,7 @@ OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE = 0, -1, -2, -3, -4
 def test_header_functions_exported():
     names = binding.header_functions()
     assert set(names) == {"mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_absorbed",
-                          "mla_combine_lse", "mla_up_proj_v", "mla_status_string"}
+                          "mla_combine_lse", "mla_up_proj_v", "mla_status_string", "mla_decode_kernel_events"}
     L = binding.lib()
     for n in names:
         assert hasattr(L, n), n
