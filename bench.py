@@ -97,6 +97,22 @@ def cpu_baseline(case, P, seconds: float) -> dict:
             "tok_s": done * case.s_q / el, "seconds": el}
 
 
+def copy_probe(mib: int) -> int:
+    """A plain copy of known size: HBM counters (FETCH_SIZE / WRITE_SIZE) read
+    on it give the bytes-per-count scale used for the decode kernel."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,7 +123,12 @@ def main() -> int:
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic split planning")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (the reference kernel "
+                         "for scaling HBM traffic counters) and exit")
     args = ap.parse_args()
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

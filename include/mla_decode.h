@@ -66,9 +66,10 @@ extern "C" {
  *  w_uk    [n_h*d_h, d_c],  dtype w_dtype
  *  q_lat   [T_q, n_h, d_c], token stride qlat_stride_t (>= n_h*d_c), dtype out_dtype
  *  act_dtype, w_dtype in {MLA_F32, MLA_BF16}; out_dtype in {MLA_F32, MLA_BF16}.
- *  Accumulation is fp32.  bf16 activations and weights take the MFMA kernel
- *  (needs d_h % 16 == 0, d_c % 32 == 0, 16-byte aligned rows); other
- *  combinations take a plain fp32 kernel.  T_q == 0 is a no-op.
+ *  Accumulation is fp32.  bf16 activations and weights with d_h <= 128 take
+ *  the MFMA kernel (which then needs d_h % 16 == 0, d_c % 32 == 0, 16-byte
+ *  aligned rows); other combinations take a plain fp32 kernel.  T_q == 0 is
+ *  a no-op.
  */
 int mla_absorb_q(const void* q_nope, int64_t q_stride_t, const void* w_uk, void* q_lat,
                  int64_t qlat_stride_t, int T_q, int n_h, int d_h, int d_c, int act_dtype,

@@ -82,7 +82,7 @@ int mla_absorb_q(const void* q_nope, int64_t q_stride_t, const void* w_uk, void*
   if (T_q == 0) return MLA_OK;
   if (!q_nope || !w_uk || !q_lat) return MLA_ERR_INVALID_ARG;
   if (q_stride_t < (int64_t)n_h * d_h || qlat_stride_t < (int64_t)n_h * d_c) return MLA_ERR_INVALID_ARG;
-  const bool mfma = act_dtype == MLA_BF16 && w_dtype == MLA_BF16;
+  const bool mfma = act_dtype == MLA_BF16 && w_dtype == MLA_BF16 && d_h <= 128;
   if (mfma) {
     if (d_h % 16 != 0 || d_c % 32 != 0) return MLA_ERR_UNSUPPORTED;
     if (!aligned16(q_nope) || !aligned16(w_uk) || q_stride_t % 8 != 0) return MLA_ERR_MISALIGNED;

@@ -364,6 +364,81 @@ __device__ __forceinline__ void store4(void* out, long long base, float4 v, int 
   }
 }
 
+// Merge of a decode call's own partial rows: one thread per 8 consecutive
+// elements of a row (16-byte loads of bf16 partials, two of fp32), the loads
+// of all partitions issued before they are consumed.
+__global__ __launch_bounds__(256) void combine_units8_kernel(DecodeArgs a) {
+  const int bq = blockIdx.y;
+  const int b = bq / a.s_q, qi = bq % a.s_q;
+  const int2 sq = a.seq[b];
+  if (sq.y <= 1) return;
+  const int d8 = a.d_c / 8;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int h = idx / d8, c8 = idx % d8;
+  if (h >= a.n_h) return;
+  const int R = a.s_q * a.n_h;
+  const long long prow = (long long)sq.x * R + qi * a.n_h + h;
+  const float* lp = a.lse_part + prow;
+  float m = -INFINITY;
+  for (int k = 0; k < sq.y; ++k) m = fmaxf(m, lp[(long long)k * R]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float z = 0.f;
+  if (m != -INFINITY) {
+    constexpr int kU = 4;
+    for (int k0 = 0; k0 < sq.y; k0 += kU) {
+      float wk[kU];
+      u32x4_t v16[kU];
+      f32x4_t v32[kU][2];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int k = k0 + u;
+        wk[u] = k < sq.y ? expf(lp[(long long)k * R] - m) : 0.f;
+        if (k < sq.y) {
+          const long long e = (prow + (long long)k * R) * a.d_c + 8 * c8;
+          if (a.part_bf16) {
+            v16[u] = *(const u32x4_t*)((const uint16_t*)a.o_part + e);
+          } else {
+            v32[u][0] = *(const f32x4_t*)(a.o_part + e);
+            v32[u][1] = *(const f32x4_t*)(a.o_part + e + 4);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (wk[u] == 0.f) continue;  // an empty partition may hold anything
+        z += wk[u];
+        if (a.part_bf16) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[2 * j] += wk[u] * bf16_bits_to_f32((uint16_t)(v16[u][j] & 0xffffu));
+            acc[2 * j + 1] += wk[u] * bf16_bits_to_f32((uint16_t)(v16[u][j] >> 16));
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[j] += wk[u] * v32[u][0][j];
+            acc[4 + j] += wk[u] * v32[u][1][j];
+          }
+        }
+      }
+    }
+  }
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  const long long orow = ((long long)b * a.s_q + qi) * a.n_h + h;
+  const long long ob = orow * a.d_c + 8 * c8;
+  if (a.out_dtype == 0) {
+    *(f32x4_t*)((float*)a.out + ob) = f32x4_t{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    *(f32x4_t*)((float*)a.out + ob + 4) = f32x4_t{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+  } else {
+    u32x4_t pk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      pk[j] = (uint32_t)f32_to_bf16_bits(acc[2 * j] * inv) | ((uint32_t)f32_to_bf16_bits(acc[2 * j + 1] * inv) << 16);
+    *(u32x4_t*)((uint16_t*)a.out + ob) = pk;
+  }
+  if (c8 == 0 && a.lse) a.lse[orow] = z > 0.f ? m + logf(z) : -INFINITY;
+}
+
 __global__ __launch_bounds__(256) void combine_units_kernel(DecodeArgs a) {
   const int bq = blockIdx.y;
   const int b = bq / a.s_q, qi = bq % a.s_q;
@@ -389,6 +464,14 @@ __global__ __launch_bounds__(256) void combine_units_kernel(DecodeArgs a) {
 }
 
 hipError_t launch_combine_units(const DecodeArgs& a, hipStream_t s) {
+  // 8-wide path when rows split into 16-byte pieces (d_c % 8 == 0 keeps every
+  // fp32 / bf16 row start 16-byte aligned given 256-byte aligned buffers)
+  if (a.d_c % 8 == 0) {
+    const int per = a.n_h * (a.d_c / 8);
+    dim3 grid((per + 255) / 256, a.B * a.s_q);
+    hipLaunchKernelGGL(combine_units8_kernel, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const int per = a.n_h * (a.d_c / 4);
   dim3 grid((per + 255) / 256, a.B * a.s_q);
   hipLaunchKernelGGL(combine_units_kernel, grid, dim3(256), 0, s, a);

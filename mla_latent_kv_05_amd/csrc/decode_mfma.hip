@@ -247,7 +247,7 @@ void decode_mfma_kernel(DecodeArgs a) {
           mx = fmaxf(mx, v);
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = half_swap_max(mx);
       if (m_run == -INFINITY) {
         m_run = mx;  // first subtile: the accumulator is still zero
       } else if (mx > m_run + kTau) {
@@ -310,7 +310,7 @@ void decode_mfma_kernel(DecodeArgs a) {
 
     // ---- finalize this unit
     acc_fence(acc);
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = half_swap_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     const long long orow = ((long long)b * a.s_q + qi) * kHeads + head;

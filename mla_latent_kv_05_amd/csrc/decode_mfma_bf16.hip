@@ -153,42 +153,97 @@ void decode_bf16_kernel(DecodeArgs a) {
       v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
       return v;
     };
-    // scaled, masked score of row value r of subtile t (in place) and its running max
-    auto score = [&](f32x16_t& sv, int r, int nv, float& mx) {
-      const int t = 8 * (r >> 2) + 4 * g + (r & 3);
-      sv[r] = t < nv ? sv[r] * scale2 : -INFINITY;
-      mx = fmaxf(mx, sv[r]);
+    // raw scores of the token rows past the end of a ragged subtile -> -inf
+    // (a uniform branch; full subtiles skip it)
+    auto mask_tail = [&](f32x16_t& sv, int nv) {
+      if (nv < kSub) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 8 * (r >> 2) + 4 * g + (r & 3);
+          sv[r] = t < nv ? sv[r] : -INFINITY;
+        }
+      }
+    };
+    // max of the 16 raw scores of a lane (tree), then of the two wave halves
+    // holding the same head, in the exp2 domain (the scale is positive)
+    auto row_max = [&](const f32x16_t& sv) {
+      float m8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m8[i] = fmaxf(sv[2 * i], sv[2 * i + 1]);
+#pragma unroll
+      for (int w2 = 4; w2 >= 1; w2 >>= 1)
+#pragma unroll
+        for (int i = 0; i < w2; ++i) m8[i] = fmaxf(m8[i], m8[i + w2]);
+      return half_swap_max(m8[0]) * scale2;
     };
 
-    f32x16_t sc;   // S of the subtile whose scores are being formed
-    bf16x8_t P[2]; // P of the subtile whose P.V is in flight
+    // softmax of the raw scores sp of one subtile against the running max:
+    // lazy new reference, exp2 weights in bf16 (P) and their row sum.  The
+    // VALU work is split in pieces so it can sit between MFMAs.
+    f32x16_t sp;    // raw S of the subtile whose P.V comes next
+    f32x16_t sc;    // S of the following subtile, accumulating
+    bf16x8_t P[2];  // P of subtile sp
+    float m_new = -INFINITY, ps0 = 0.f, ps1 = 0.f;
+    float m8[8];
+    auto sm_max = [&](int piece) {  // pieces 0..3
+      if (piece == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m8[i] = fmaxf(sp[2 * i], sp[2 * i + 1]);
+      } else if (piece == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m8[i] = fmaxf(m8[i], m8[i + 4]);
+      } else if (piece == 2) {
+        m8[0] = fmaxf(m8[0], m8[2]);
+        m8[1] = fmaxf(m8[1], m8[3]);
+        m8[0] = fmaxf(m8[0], m8[1]);
+      } else {
+        const float mx = half_swap_max(m8[0]) * scale2;
+        m_new = mx > m_run + kTau ? mx : m_run;  // lazy: keep the reference unless far behind
+        ps0 = ps1 = 0.f;
+      }
+    };
+    auto sm_exp = [&](int r) {  // rows r, r+1
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[r], scale2, -m_new));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[r + 1], scale2, -m_new));
+      ps0 += p0;
+      ps1 += p1;
+      P[r >> 3][r & 7] = (__bf16)p0;
+      P[r >> 3][(r & 7) + 1] = (__bf16)p1;
+    };
+    // the reference moved (rare): rescale O and the row sum before new P.V
+    auto sm_commit = [&]() {
+      if (m_new != m_run) {
+        const float f = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= f;
+        acc_fence(acc);
+#pragma unroll
+        for (int d = 0; d < 16; ++d) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[d][r] *= f;
+          asm volatile("" : "+a"(acc[d]));
+        }
+        acc_fence(acc);
+        m_run = m_new;
+      }
+      l_run += ps0 + ps1;
+    };
+
     if (n_sub > 0) {
-      // S(0), its scores, the first reference max and P(0)
+      // S(0) -> sp, its first reference max
       const lds_u8* tile = tile_of(0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+      for (int r = 0; r < 16; ++r) sp[r] = 0.f;
       bf16x8_t ka[2] = {kfrag(tile, 0), kfrag(tile, 1)};
 #pragma unroll
       for (int f = 0; f < 36; ++f) {
-        sc = mfma(ka[f & 1], q[f], sc);
+        sp = mfma(ka[f & 1], q[f], sp);
         if (f + 2 < 36) ka[f & 1] = kfrag(tile, f + 2);
       }
-      float mx = -INFINITY;
-      const int nv = nvalid_of(0);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) score(sc, r, nv, mx);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      m_run = mx;
-      float ps = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sc[r] - m_run);
-        ps += p;
-        P[r >> 3][r & 7] = (__bf16)p;
-      }
-      l_run = ps;
+      mask_tail(sp, nvalid_of(0));
+      m_run = row_max(sp);
     }
 
+    constexpr int kQkA = 16;  // QK steps overlapped with the softmax
     for (int it = 0; it + 1 < n_sub; ++it) {
       // ---- (A) next subtile resident; refill the stage subtile it-1 used
       wait_b16_groups(min(1, n_sub - 2 - it));
@@ -213,78 +268,55 @@ void decode_bf16_kernel(DecodeArgs a) {
       const lds_u8* tile = tile_of(it);
       const lds_u8* tile_n = tile_of(it + 1);
 
-      // ---- (X) S(it+1) (one dependent chain) interleaved with P.V steps 0..15
-      //      of subtile it (independent accumulators fill the chain's gaps)
-      bf16x8_t va[2] = {vfrag(tile, 0), vfrag(tile, 1)};
-      bf16x8_t ka[2] = {kfrag(tile_n, 0), kfrag(tile_n, 1)};
+      // ---- phase 1: QK(it+1) steps 0..15 (one dependent chain) with the
+      //      softmax of subtile it in the gaps
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+      bf16x8_t ka[2] = {kfrag(tile_n, 0), kfrag(tile_n, 1)};
 #pragma unroll
-      for (int k4 = 0; k4 < 9; ++k4) {
+      for (int f = 0; f < kQkA; ++f) {
+        sc = mfma(ka[f & 1], q[f], sc);
+        ka[f & 1] = kfrag(tile_n, f + 2);
+        if (f < 4) sm_max(f);
+        else if (f < 12) sm_exp(2 * (f - 4));
+        if (f == 7) asm volatile("" : "+v"(P[0]));  // keep the conversions in place
+        if (f == 11) asm volatile("" : "+v"(P[1]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sm_commit();
+
+      // ---- phase 2: QK(it+1) steps 16..35 interleaved with the 32 P.V
+      //      steps of subtile it (12 x [QK, PV, PV] + 8 x [QK, PV]); the
+      //      DMA of subtile it+3 rides along
+      bf16x8_t va[2] = {vfrag(tile, 0), vfrag(tile, 1)};
+      int step = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int f = 4 * k4 + j;
-          sc = mfma(ka[f & 1], q[f], sc);
-          if (f + 2 < 36) ka[f & 1] = kfrag(tile_n, f + 2);
-          if (j == 0 && dma_on) dma16_m0(dma_rs, dma_src_offset(k4 * 256 + tid), dma_m0 + k4 * 4096);
-          if ((j & 1) && k4 < 8) {  // one P.V step after every second QK step
-            const int step = 2 * k4 + (j >> 1);
-            mfma_acc(acc[step & 15], va[step & 1], P[step >> 4]);
-            va[step & 1] = vfrag(tile, step + 2);
-          }
+      for (int f = kQkA; f < 36; ++f) {
+        sc = mfma(ka[f & 1], q[f], sc);
+        if (f + 2 < 36) ka[f & 1] = kfrag(tile_n, f + 2);
+        const int npv = (f - kQkA) < 12 ? 2 : 1;
+#pragma unroll
+        for (int u = 0; u < npv; ++u) {
+          mfma_acc(acc[step & 15], va[step & 1], P[step >> 4]);
+          if (step + 2 < 32) va[step & 1] = vfrag(tile, step + 2);
+          ++step;
+        }
+        if (((f - kQkA) & 1) == 0 && (f - kQkA) / 2 < kBf16Dma && dma_on) {
+          const int k4 = (f - kQkA) / 2;
+          dma16_m0(dma_rs, dma_src_offset(k4 * 256 + tid), dma_m0 + k4 * 4096);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-
-      // ---- (Y) P.V steps 16..31 of subtile it, interleaved with the scores,
-      //      reference max and P of subtile it+1
-      bf16x8_t Pn[2];
-      float mx = -INFINITY, ps = 0.f, m_new = m_run;
-      const int nv_n = nvalid_of(it + 1);
-#pragma unroll
-      for (int h = 0; h < 16; ++h) {
-        const int step = 16 + h;
-        mfma_acc(acc[step & 15], va[step & 1], P[1]);
-        if (step + 2 < 32) va[step & 1] = vfrag(tile, step + 2);
-        if (h < 8) {
-          score(sc, 2 * h, nv_n, mx);
-          score(sc, 2 * h + 1, nv_n, mx);
-          if (h == 7) {
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            m_new = mx > m_run + kTau ? mx : m_run;  // lazy: keep the reference unless far behind
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int r = 2 * (h - 8) + e;
-            const float p = __builtin_amdgcn_exp2f(sc[r] - m_new);
-            ps += p;
-            Pn[r >> 3][r & 7] = (__bf16)p;
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-
-      // ---- (Z) rare: the reference max moved; rescale O and the row sum
-      if (m_new != m_run) {
-        const float f = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= f;
-        acc_fence(acc);
-#pragma unroll
-        for (int d = 0; d < 16; ++d) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[d][r] *= f;
-          asm volatile("" : "+a"(acc[d]));
-        }
-        acc_fence(acc);
-        m_run = m_new;
-      }
-      l_run += ps;
-      P[0] = Pn[0];
-      P[1] = Pn[1];
+      sp = sc;
+      mask_tail(sp, nvalid_of(it + 1));
     }
-    if (n_sub > 0) {  // the last subtile: P.V only
+    if (n_sub > 0) {  // the last subtile: softmax and P.V only
       const lds_u8* tile = tile_of(n_sub - 1);
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) sm_max(pc);
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) sm_exp(r);
+      sm_commit();
       bf16x8_t va[2] = {vfrag(tile, 0), vfrag(tile, 1)};
 #pragma unroll
       for (int step = 0; step < 32; ++step) {
@@ -295,7 +327,7 @@ void decode_bf16_kernel(DecodeArgs a) {
 
     // ---- finalize: normalise, stage rows through LDS, store whole rows
     acc_fence(acc);
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = half_swap_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     const long long orow0 = ((long long)b * a.s_q + qi) * kHeads;  // first output row of this (b, qi)
@@ -324,8 +356,8 @@ void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           u32x2_t pk;
-          pk[0] = f32_to_bf16_bits(t[4 * qd] * inv) | ((uint32_t)f32_to_bf16_bits(t[4 * qd + 1] * inv) << 16);
-          pk[1] = f32_to_bf16_bits(t[4 * qd + 2] * inv) | ((uint32_t)f32_to_bf16_bits(t[4 * qd + 3] * inv) << 16);
+          pk[0] = pack_bf16x2(t[4 * qd] * inv, t[4 * qd + 1] * inv);
+          pk[1] = pack_bf16x2(t[4 * qd + 2] * inv, t[4 * qd + 3] * inv);
           *(lds_u2*)(rowp + (db * 32 + 8 * qd + 4 * g) * 2) = pk;
         }
       }

@@ -127,6 +127,17 @@ __device__ __forceinline__ void acc_fence(f32x16_t* acc) {
                  "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]), "+a"(acc[15]));
 }
 
+// max / sum of a value with the lane 32 apart (the other half of the wave):
+// one VALU permlane swap instead of an LDS-routed shuffle
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Zero the 16 accumulator blocks with MFMAs whose inputs are zero (AGPR
 // destinations, no VALU traffic through the accumulator file)
 __device__ __forceinline__ void zero_acc(f32x16_t* acc) {

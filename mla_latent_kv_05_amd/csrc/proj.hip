@@ -48,6 +48,7 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(const void* A, long l
 // columns c0 + 32w .. +31 for all T_q rows (32-row tiles).
 constexpr int kAbsCols = 128;
 constexpr int kAbsStride = 144;  // bf16 elements per staged weight row
+constexpr int kAbsMaxKb = 8;     // d_h / 16 up to d_h = 128
 
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* q, long long q_st,
                                                           const uint16_t* w, void* out, long long o_st,
@@ -59,6 +60,21 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* q, lon
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31, j16 = lane & 15, G = lane >> 4;
   const int ncols = min(kAbsCols, d_c - c0);
+  const int cw = 32 * wv;  // this wave's column offset within the block
+  const int nkb = d_h / 16;
+  // A fragments (query rows t0 + l32) of one 32-row tile; the first tile's
+  // loads are issued before the weight staging so the two latencies overlap
+  bf16x8_t av[kAbsMaxKb];
+  auto load_q = [&](int t0) {
+    const int tr = t0 + l32;
+#pragma unroll
+    for (int kb = 0; kb < kAbsMaxKb; ++kb) {
+      if (kb >= nkb) break;
+      if (tr < T) av[kb] = *(const bf16x8_t*)(q + tr * q_st + (long long)h * d_h + kb * 16 + g * 8);
+      else for (int j = 0; j < 8; ++j) av[kb][j] = (__bf16)0.f;
+    }
+  };
+  load_q(0);
   // stage W rows k = 0..d_h-1, columns c0..c0+ncols (16-byte pieces); the
   // loads of one batch are all issued before any LDS store
   const int pieces = ncols / 8;
@@ -77,30 +93,32 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* q, lon
     }
   }
   __syncthreads();
-  const int cw = 32 * wv;  // this wave's column offset within the block
   if (cw >= ncols) return;
+  // B fragments (this wave's 32 columns, all of K) once from LDS
+  bf16x8_t bf[kAbsMaxKb];
+#pragma unroll
+  for (int kb = 0; kb < kAbsMaxKb; ++kb) {
+    if (kb >= nkb) break;
+    // B[k][n]: k = kb*16 + g*8 + {0..3 | 4..7}, n = cw + l32 -> two transposed reads
+    const int krow = kb * 16 + g * 8 + (j16 >> 2);
+    const int col = cw + 16 * (G & 1) + (j16 & 3) * 4;
+    const lds_u8* p = wl + (krow * kAbsStride + col) * 2;
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p);
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4_t*)(p + 4 * kAbsStride * 2));
+    bf[kb][0] = lo[0]; bf[kb][1] = lo[1]; bf[kb][2] = lo[2]; bf[kb][3] = lo[3];
+    bf[kb][4] = hi[0]; bf[kb][5] = hi[1]; bf[kb][6] = hi[2]; bf[kb][7] = hi[3];
+  }
   for (int t0 = 0; t0 < T; t0 += 32) {
     f32x16_t acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    const int tr = t0 + l32;
-    const bool tv = tr < T;
-    for (int kb = 0; kb < d_h / 16; ++kb) {
-      bf16x8_t av;
-      if (tv) av = *(const bf16x8_t*)(q + tr * q_st + (long long)h * d_h + kb * 16 + g * 8);
-      else for (int j = 0; j < 8; ++j) av[j] = (__bf16)0.f;
-      // B[k][n]: k = kb*16 + g*8 + {0..3 | 4..7}, n = cw + l32 -> two transposed reads
-      const int krow = kb * 16 + g * 8 + (j16 >> 2);
-      const int col = cw + 16 * (G & 1) + (j16 & 3) * 4;
-      const lds_u8* p = wl + (krow * kAbsStride + col) * 2;
-      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p);
-      const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4_t*)(p + 4 * kAbsStride * 2));
-      bf16x8_t bv;
-      bv[0] = lo[0]; bv[1] = lo[1]; bv[2] = lo[2]; bv[3] = lo[3];
-      bv[4] = hi[0]; bv[5] = hi[1]; bv[6] = hi[2]; bv[7] = hi[3];
-      acc = mfma16(av, bv, acc);
+#pragma unroll
+    for (int kb = 0; kb < kAbsMaxKb; ++kb) {
+      if (kb >= nkb) break;
+      acc = mfma16(av[kb], bf[kb], acc);
     }
+    if (t0 + 32 < T) load_q(t0 + 32);  // next tile in flight during these stores
     // D[i = t][j = column]: lane column cw + l32, rows 8(r/4) + 4g + r%4
 #pragma unroll
     for (int r = 0; r < 16; ++r) {

@@ -44,9 +44,11 @@ layout) are written here from the formats' definitions.
 Parity status: every function below is pinned by tests/test_oracle.py
 (absorbed vs materialised agreement, closed forms, torch's CPU
 scaled_dot_product_attention, complex-number rotation, the cache arithmetic
-the pages print).  The fp8 *scheme* (per-token amax/448 scale) is a reading of
-"FP8 content cache, BF16 RoPE key" and is pinned only by self-consistency and
-the e4m3fn format facts.
+the pages print).  The fp8 *scheme* (per-token amax/448 scale on e4m3fn
+content codes, bf16 RoPE key) is a reading: the pages name only an fp8
+content cache beside a bf16 RoPE key, so with respect to the pages it is
+parity unpinned -- it is pinned only by self-consistency (the oracle decodes
+exactly the codes and scales the GPU reads) and by the e4m3fn format facts.
 """
 
 from __future__ import annotations
