@@ -367,6 +367,7 @@ __device__ __forceinline__ void store4(void* out, long long base, float4 v, int 
 // Merge of a decode call's own partial rows: one thread per 8 consecutive
 // elements of a row (16-byte loads of bf16 partials, two of fp32), the loads
 // of all partitions issued before they are consumed.
+template <bool PBF16>
 __global__ __launch_bounds__(256) void combine_units8_kernel(DecodeArgs a) {
   const int bq = blockIdx.y;
   const int b = bq / a.s_q, qi = bq % a.s_q;
@@ -379,47 +380,69 @@ __global__ __launch_bounds__(256) void combine_units8_kernel(DecodeArgs a) {
   const int R = a.s_q * a.n_h;
   const long long prow = (long long)sq.x * R + qi * a.n_h + h;
   const float* lp = a.lse_part + prow;
-  float m = -INFINITY;
-  for (int k = 0; k < sq.y; ++k) m = fmaxf(m, lp[(long long)k * R]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float z = 0.f;
-  if (m != -INFINITY) {
-    constexpr int kU = 4;
-    for (int k0 = 0; k0 < sq.y; k0 += kU) {
-      float wk[kU];
-      u32x4_t v16[kU];
-      f32x4_t v32[kU][2];
+  float z = 0.f, m = -INFINITY;
+  auto add = [&](float wk, const u32x4_t& v16, const f32x4_t& lo, const f32x4_t& hi) {
+    if (wk == 0.f) return;  // an empty partition may hold anything
+    z += wk;
+    if constexpr (PBF16) {
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int k = k0 + u;
-        wk[u] = k < sq.y ? expf(lp[(long long)k * R] - m) : 0.f;
-        if (k < sq.y) {
-          const long long e = (prow + (long long)k * R) * a.d_c + 8 * c8;
-          if (a.part_bf16) {
-            v16[u] = *(const u32x4_t*)((const uint16_t*)a.o_part + e);
-          } else {
-            v32[u][0] = *(const f32x4_t*)(a.o_part + e);
-            v32[u][1] = *(const f32x4_t*)(a.o_part + e + 4);
-          }
-        }
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += wk * bf16_bits_to_f32((uint16_t)(v16[j] & 0xffffu));
+        acc[2 * j + 1] += wk * bf16_bits_to_f32((uint16_t)(v16[j] >> 16));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] += wk * lo[j];
+        acc[4 + j] += wk * hi[j];
+      }
+    }
+  };
+  auto load = [&](int k, u32x4_t& v16, f32x4_t& lo, f32x4_t& hi) {
+    const long long e = (prow + (long long)k * R) * a.d_c + 8 * c8;
+    if constexpr (PBF16) {
+      v16 = *(const u32x4_t*)((const uint16_t*)a.o_part + e);
+    } else {
+      lo = *(const f32x4_t*)(a.o_part + e);
+      hi = *(const f32x4_t*)(a.o_part + e + 4);
+    }
+  };
+  constexpr int kU = 8;
+  if (sq.y <= kU) {
+    // every load (log-sum-exps and rows) in flight at once: one round trip
+    float l[kU];
+    u32x4_t v16[kU];
+    f32x4_t lo[kU], hi[kU];
+#pragma unroll
+    for (int k = 0; k < kU; ++k)
+      if (k < sq.y) {
+        l[k] = lp[(long long)k * R];
+        load(k, v16[k], lo[k], hi[k]);
       }
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if (wk[u] == 0.f) continue;  // an empty partition may hold anything
-        z += wk[u];
-        if (a.part_bf16) {
+    for (int k = 0; k < kU; ++k)
+      if (k < sq.y) m = fmaxf(m, l[k]);
+    if (m != -INFINITY) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            acc[2 * j] += wk[u] * bf16_bits_to_f32((uint16_t)(v16[u][j] & 0xffffu));
-            acc[2 * j + 1] += wk[u] * bf16_bits_to_f32((uint16_t)(v16[u][j] >> 16));
-          }
-        } else {
+      for (int k = 0; k < kU; ++k)
+        if (k < sq.y) add(expf(l[k] - m), v16[k], lo[k], hi[k]);
+    }
+  } else {
+    for (int k = 0; k < sq.y; ++k) m = fmaxf(m, lp[(long long)k * R]);
+    if (m != -INFINITY) {
+      for (int k0 = 0; k0 < sq.y; k0 += 4) {
+        float wk[4];
+        u32x4_t v16[4];
+        f32x4_t lo[4], hi[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            acc[j] += wk[u] * v32[u][0][j];
-            acc[4 + j] += wk[u] * v32[u][1][j];
-          }
+        for (int u = 0; u < 4; ++u) {
+          const int k = k0 + u;
+          wk[u] = k < sq.y ? expf(lp[(long long)k * R] - m) : 0.f;
+          if (k < sq.y) load(k, v16[u], lo[u], hi[u]);
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) add(wk[u], v16[u], lo[u], hi[u]);
       }
     }
   }
@@ -469,7 +492,10 @@ hipError_t launch_combine_units(const DecodeArgs& a, hipStream_t s) {
   if (a.d_c % 8 == 0) {
     const int per = a.n_h * (a.d_c / 8);
     dim3 grid((per + 255) / 256, a.B * a.s_q);
-    hipLaunchKernelGGL(combine_units8_kernel, grid, dim3(256), 0, s, a);
+    if (a.part_bf16)
+      hipLaunchKernelGGL(combine_units8_kernel<true>, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(combine_units8_kernel<false>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
   }
   const int per = a.n_h * (a.d_c / 4);
