@@ -67,9 +67,9 @@ extern "C" {
  *  q_lat   [T_q, n_h, d_c], token stride qlat_stride_t (>= n_h*d_c), dtype out_dtype
  *  act_dtype, w_dtype in {MLA_F32, MLA_BF16}; out_dtype in {MLA_F32, MLA_BF16}.
  *  Accumulation is fp32.  bf16 activations and weights with d_h <= 128 take
- *  the MFMA kernel (which then needs d_h % 16 == 0, d_c % 32 == 0, 16-byte
- *  aligned rows); other combinations take a plain fp32 kernel.  T_q == 0 is
- *  a no-op.
+ *  the MFMA kernel (which then needs d_h % 16 == 0, d_c % 32 == 0, and
+ *  16-byte aligned rows of q_nope, w_uk and q_lat, else MLA_ERR_MISALIGNED);
+ *  other combinations take a plain fp32 kernel.  T_q == 0 is a no-op.
  */
 int mla_absorb_q(const void* q_nope, int64_t q_stride_t, const void* w_uk, void* q_lat,
                  int64_t qlat_stride_t, int T_q, int n_h, int d_h, int d_c, int act_dtype,
@@ -177,8 +177,10 @@ int mla_combine_lse(const float* o_part, const float* lse_part, const int32_t* s
  *  w_uv  [n_h*d_h, d_c], dtype w_dtype
  *  o     [T_q, n_h, d_h], token stride o_stride_t, dtype out_dtype
  *  bf16 activations and weights take the MFMA kernel (needs d_c % 64 == 0,
- *  d_c <= 512, d_h % 32 == 0, 16-byte aligned rows); other combinations a
- *  plain fp32 kernel.  Accumulation is fp32.  T_q == 0 is a no-op.
+ *  d_c <= 512, d_h % 32 == 0, 16-byte aligned o_lat/w_uv rows, and o
+ *  aligned to two elements with an even o_stride_t, else
+ *  MLA_ERR_MISALIGNED); other combinations a plain fp32 kernel.
+ *  Accumulation is fp32.  T_q == 0 is a no-op.
  */
 int mla_up_proj_v(const void* o_lat, int64_t olat_stride_t, const void* w_uv, void* o,
                   int64_t o_stride_t, int T_q, int n_h, int d_c, int d_h, int act_dtype,

@@ -86,6 +86,9 @@ int mla_absorb_q(const void* q_nope, int64_t q_stride_t, const void* w_uk, void*
   if (mfma) {
     if (d_h % 16 != 0 || d_c % 32 != 0) return MLA_ERR_UNSUPPORTED;
     if (!aligned16(q_nope) || !aligned16(w_uk) || q_stride_t % 8 != 0) return MLA_ERR_MISALIGNED;
+    // output rows are written in 16-byte pieces
+    const int64_t oe = out_dtype == MLA_F32 ? 4 : 2;
+    if (!aligned16(q_lat) || (qlat_stride_t * oe) % 16 != 0) return MLA_ERR_MISALIGNED;
   }
   return launch_status(launch_absorb(q_nope, q_stride_t, w_uk, q_lat, qlat_stride_t, T_q, n_h, d_h, d_c,
                                      act_dtype, w_dtype, out_dtype, mfma, (hipStream_t)stream));
@@ -103,6 +106,8 @@ int mla_up_proj_v(const void* o_lat, int64_t olat_stride_t, const void* w_uv, vo
   if (mfma) {
     if (d_c % 64 != 0 || d_c > 512 || d_h % 32 != 0) return MLA_ERR_UNSUPPORTED;
     if (!aligned16(o_lat) || !aligned16(w_uv) || olat_stride_t % 8 != 0) return MLA_ERR_MISALIGNED;
+    // outputs are written two adjacent elements at a time
+    if (((uintptr_t)o % (out_dtype == MLA_F32 ? 8 : 4)) != 0 || o_stride_t % 2 != 0) return MLA_ERR_MISALIGNED;
   }
   return launch_status(launch_up_proj(o_lat, olat_stride_t, w_uv, o, o_stride_t, T_q, n_h, d_c, d_h,
                                       act_dtype, w_dtype, out_dtype, mfma, (hipStream_t)stream));
