@@ -2,6 +2,7 @@
 // Declarations and contracts: include/mla_decode.h.
 #include "mla_decode.h"
 #include "mla_internal.h"
+#include <algorithm>
 
 #include <atomic>
 
@@ -208,7 +209,10 @@ int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_ca
   e = fast ? launch_decode_mfma(a, grid_x, st) : launch_decode_generic(a, grid_x, st);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return MLA_ERR_LAUNCH;
-  e = launch_combine_units(a, st);
+  // partitions per sequence are planned on the device; the host expects about
+  // slots / B of them (equal lengths) or the explicit count
+  const int expect_splits = num_splits > 0 ? num_splits : (grid_x + B - 1) / B;
+  e = launch_combine_units(a, st, expect_splits);
   return launch_status(e);
 }
 

@@ -486,7 +486,98 @@ __global__ __launch_bounds__(256) void combine_units_kernel(DecodeArgs a) {
   if (c4 == 0 && a.lse) a.lse[orow] = lse_v;
 }
 
-hipError_t launch_combine_units(const DecodeArgs& a, hipStream_t s) {
+// Merge for sequences cut into many partitions (long contexts): one
+// workgroup per output row; its four wavefronts take every fourth partition
+// (one 8-element piece of the row per lane) and add their sums through LDS.
+constexpr int kWideMaxS = 1024;
+template <bool PBF16>
+__global__ __launch_bounds__(256) void combine_units_wide_kernel(DecodeArgs a) {
+  __shared__ float wsh[kWideMaxS];
+  __shared__ float part[4][64][9];
+  __shared__ float rsh[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int R = a.s_q * a.n_h;
+  const int row = blockIdx.x;                 // (b, qi, h)
+  const int b = row / R, r = row % R;
+  const int2 sq = a.seq[b];
+  if (sq.y <= 1) return;
+  const int S = sq.y;
+  const long long prow = (long long)sq.x * R + r;
+  // partition weights exp(lse_s - max) and their sum
+  float m = -INFINITY;
+  for (int k = tid; k < S; k += 256) m = fmaxf(m, a.lse_part[prow + (long long)k * R]);
+  m = wave_max(m);
+  if (lane == 0) rsh[wv] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(rsh[0], rsh[1]), fmaxf(rsh[2], rsh[3]));
+  const bool cached = S <= kWideMaxS;  // weights kept in LDS, else recomputed
+  float zl = 0.f;
+  for (int k = tid; k < S; k += 256) {
+    const float wk = m == -INFINITY ? 0.f : expf(a.lse_part[prow + (long long)k * R] - m);
+    if (cached) wsh[k] = wk;
+    zl += wk;
+  }
+  zl = wave_sum(zl);
+  __syncthreads();  // wsh complete; rsh reads done
+  if (lane == 0) rsh[wv] = zl;
+  // this lane's 8 elements, partitions wv, wv+4, ...
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int pieces = a.d_c / 8;
+  if (lane < pieces) {
+    for (int k = wv; k < S; k += 4) {
+      const float wk = cached ? wsh[k] : (m == -INFINITY ? 0.f : expf(a.lse_part[prow + (long long)k * R] - m));
+      if (wk == 0.f) continue;  // an empty partition may hold anything
+      const long long e = (prow + (long long)k * R) * a.d_c + 8 * lane;
+      if constexpr (PBF16) {
+        const u32x4_t v = *(const u32x4_t*)((const uint16_t*)a.o_part + e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[2 * j] += wk * bf16_bits_to_f32((uint16_t)(v[j] & 0xffffu));
+          acc[2 * j + 1] += wk * bf16_bits_to_f32((uint16_t)(v[j] >> 16));
+        }
+      } else {
+        const f32x4_t lo = *(const f32x4_t*)(a.o_part + e), hi = *(const f32x4_t*)(a.o_part + e + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[j] += wk * lo[j];
+          acc[4 + j] += wk * hi[j];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) part[wv][lane][j] = acc[j];
+  __syncthreads();
+  if (wv == 0 && lane < pieces) {
+    const float z = rsh[0] + rsh[1] + rsh[2] + rsh[3];
+    const float inv = z > 0.f ? 1.f / z : 0.f;
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = (part[0][lane][j] + part[1][lane][j] + part[2][lane][j] + part[3][lane][j]) * inv;
+    const long long orow = (long long)b * R + r;
+    const long long ob = orow * a.d_c + 8 * lane;
+    if (a.out_dtype == 0) {
+      *(f32x4_t*)((float*)a.out + ob) = f32x4_t{o[0], o[1], o[2], o[3]};
+      *(f32x4_t*)((float*)a.out + ob + 4) = f32x4_t{o[4], o[5], o[6], o[7]};
+    } else {
+      *(u32x4_t*)((uint16_t*)a.out + ob) =
+          u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+    }
+    if (lane == 0 && a.lse) a.lse[orow] = z > 0.f ? m + logf(z) : -INFINITY;
+  }
+}
+
+hipError_t launch_combine_units(const DecodeArgs& a, hipStream_t s, int expect_splits) {
+  // many partitions per sequence: spread each row's partitions over a
+  // workgroup (the kernel itself handles up to kWideMaxS partitions)
+  if (expect_splits > 8 && a.d_c % 8 == 0 && a.d_c <= 512) {
+    dim3 grid(a.B * a.s_q * a.n_h);
+    if (a.part_bf16)
+      hipLaunchKernelGGL(combine_units_wide_kernel<true>, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(combine_units_wide_kernel<false>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   // 8-wide path when rows split into 16-byte pieces (d_c % 8 == 0 keeps every
   // fp32 / bf16 row start 16-byte aligned given 256-byte aligned buffers)
   if (a.d_c % 8 == 0) {

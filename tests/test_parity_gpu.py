@@ -155,12 +155,26 @@ def test_determinism_and_paging_invariance():
     assert np.array_equal(a, c) and np.array_equal(al, cl)
 
 
-def test_long_sequence_many_splits():
-    say("long sequence 40000 tokens")
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_long_sequence_many_splits(out_dtype):
+    """One long sequence over the whole device: many partitions, merged by the
+    one-workgroup-per-row merge (fp32 or bf16 partial rows)."""
+    say(f"long sequence 40000 tokens, out {out_dtype}")
     case = inputs.decode_case(28, B=1, seq_lens=np.array([40000]), **V3)
-    g, gl = run_decode(case)
+    g, gl = run_decode(case, out_dtype=out_dtype)
     o, ol = oracle.mqa_decode_case(case)
     assert_bf16_close(g, o, "long")
+    assert_lse_close(gl, ol, "lse")
+
+
+def test_more_partitions_than_the_merge_caches():
+    """1032 one-page partitions of one sequence: the merge recomputes weights
+    instead of caching them in LDS (more than 1024 partitions)."""
+    say("1032 partitions")
+    case = inputs.decode_case(29, B=1, seq_lens=np.array([66000]), **V3)
+    g, gl = run_decode(case, num_splits=1032)
+    o, ol = oracle.mqa_decode_case(case)
+    assert_bf16_close(g, o, "1032 partitions")
     assert_lse_close(gl, ol, "lse")
 
 
