@@ -182,9 +182,9 @@ int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_ca
   a.B = B; a.s_q = s_q; a.n_h = n_h; a.d_c = d_c; a.d_r = d_r; a.block_size = block_size;
   a.scale = softmax_scale;
   a.q_dtype = q_dtype; a.kv_dtype = kv_dtype; a.out_dtype = out_dtype;
-  // the bf16-cache MFMA kernel writes bf16 partial rows when the merged
-  // output is bf16 anyway (half the partial-result traffic)
-  a.part_bf16 = (fast && kv_dtype == MLA_BF16 && out_dtype == MLA_BF16) ? 1 : 0;
+  // the MFMA kernels write bf16 partial rows when the merged output is bf16
+  // anyway (half the partial-result traffic)
+  a.part_bf16 = (fast && out_dtype == MLA_BF16) ? 1 : 0;
 
   hipStream_t st = (hipStream_t)stream;
   const int grid_x = fast ? (n_cu / s_q > 0 ? n_cu / s_q : 1) : (L.units_max < n_cu ? L.units_max : n_cu);

@@ -350,6 +350,7 @@ void decode_mfma_kernel(DecodeArgs a) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t s) {
   if (a.kv_dtype != 2) return launch_decode_bf16(a, grid_x, s);
+  if (a.kv_dtype == 2) return launch_decode_fp8(a, grid_x, s);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)decode_mfma_kernel<true>,

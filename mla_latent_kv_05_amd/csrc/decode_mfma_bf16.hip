@@ -1,42 +1,85 @@
-// Software-pipelined MFMA decode kernel for a bf16 latent cache at the
-// DeepSeek-V2/V3 shape (n_h = 128, d_c = 512, d_h^R = 64, 64-token pages).
-// Same work decomposition, LDS tile layout and operand mapping as the fp8
-// kernel in decode_mfma.hip (see the notes there); this variant overlaps the
-// stages of consecutive 32-token subtiles so the matrix pipe stays busy:
+// Software-pipelined MFMA decode kernel for the DeepSeek-V2/V3 shape of
+// absorbed MLA (itwiki "Multi-head latent attention": sections "Decoupled
+// RoPE", "Matrix absorption" and the V2/V3 dimension table): n_h = 128 heads
+// sharing one latent row [c^KV 512 | k^R 64] per token, 64-token pages, bf16
+// or fp8-e4m3 content.
 //
-//   iteration i   (A) wait for subtile i+1, barrier, DMA subtile i+3
-//                 (B) S(i+1) = K(i+1).Q^T on MFMA   ||  p = exp2(s(i) - m), P(i) in bf16
-//                 (C) O += V(i)^T.P(i)^T on MFMA   ||  s(i+1) = scale * S(i+1), mask, row max
-//                 (D) rare: rescale O when the row max grew by more than kTau
+// Work decomposition
+//   * grid.x = persistent workgroups looping over planned units (sequence,
+//     contiguous page range); grid.y = query token i of the sequence.
+//   * 4 wavefronts, one per SIMD; wavefront w owns heads 32w .. 32w+31 for
+//     both contractions: its queries stay in VGPRs, its P.V accumulator
+//     (32 heads x 512 dims fp32) fills the AGPRs.
+//   * Keys stream through LDS in 32-token subtiles of bf16 rows (36,864 B):
+//     16-byte global->LDS DMA straight into a 4-stage ring (bf16 cache), or
+//     into an fp8 staging ring that the workgroup expands into one of two
+//     bf16 tile slots (fp8 cache; e4m3 -> bf16 is exact).
+//   * S^T[token, head] = K[token, 0:576] . Q^T on v_mfma_f32_32x32x16_bf16
+//     (A = key rows from LDS via ds_read_b128, B = queries from registers).
+//   * O^T[dim, head] += V^T[dim, token] . P^T[token, head]: A = c^KV columns
+//     fetched transposed with ds_read_b64_tr_b16, B = P taken straight from
+//     the S^T accumulator layout (the lane is the head in both products).
+//   * fp8: the per-token scale multiplies the content score (the RoPE part
+//     accumulates separately) and P before the P.V product.
+//   * Online softmax in the exp2 domain with a lazy reference max: the
+//     reference only moves when a subtile's max exceeds it by 2^kTau, so the
+//     accumulator is rarely touched outside the MFMAs (numerator and
+//     denominator share the reference, so the result is exact).
 //
-// Only (D) runs without MFMA work beside it.  The unit's partial (or final)
-// output is staged through LDS so each store instruction writes whole rows.
+// Pipeline (iteration i; subtile i+1 resident before it starts)
+//   phase 1: QK(i+1) steps 0..15  ||  softmax of subtile i (max, exp2, P)
+//   phase 2: QK(i+1) steps 16..35 interleaved with the 32 P.V steps of
+//            subtile i; the DMA of a later subtile rides along
+//
+// LDS tile layout: row t (token) is 1152 B = 72 chunks of 16 B; logical chunk
+// c is stored at chunk (c & ~7) | ((c ^ f(t)) & 7), f(t) = bits 2, 3, 1 of t
+// (swz_f), chosen by measuring both read patterns.  The unit's partial (or
+// final) output is staged through LDS so each store writes whole rows.
 #include "mfma_common.h"
 
 namespace mla {
 
-constexpr int kB16Stages = 4;                               // tiles i, i+1 in use, i+2, i+3 in flight
+// bf16 cache: 4 tile stages (tiles i, i+1 in use, i+2, i+3 in flight)
+constexpr int kB16Stages = 4;
 constexpr int kB16TabOff = kB16Stages * kTileB;             // 147456
-constexpr int kB16Pages = kMaxUnitPages;                    // page ids cached in LDS per unit
-constexpr int kB16Lds = kB16TabOff + kB16Pages * 4;         // 149504
+// fp8 cache: 3 staging stages (codes + k^R; subtile i+1 being expanded,
+// i+2 and i+3 in flight), a ring of per-token scales, two bf16 tile slots,
+// and the queries' RoPE part (its own score accumulator takes those registers)
+constexpr int kF8StageB = kF8Codes + kF8Kr;                 // 20480 per subtile
+constexpr int kF8Stages3 = 3;
+constexpr int kF8ScaleSlots = 8;                            // scales of subtile s at slot s % 8
+constexpr int kF8ScaleOff = kF8Stages3 * kF8StageB;         // 61440
+constexpr int kF8SlotOff = kF8ScaleOff + kF8ScaleSlots * 128;  // 62464
+constexpr int kF8QrOff = kF8SlotOff + 2 * kTileB;           // 136192
+constexpr int kF8TabOff = kF8QrOff + kHeads * kQrStride;    // 154624
+constexpr int kPipeTabOff(bool fp8) { return fp8 ? kF8TabOff : kB16TabOff; }
+constexpr int kPipeLds(bool fp8) { return kPipeTabOff(fp8) + kMaxUnitPages * 4; }  // 149504 / 156672
 constexpr int kOutRowF = kDc + 4;                           // padded fp32 row of the output staging
 constexpr int kOutRowH = kDc * 2 + 16;                      // padded bf16 row (bytes)
+static_assert(kPipeLds(true) <= 160 * 1024, "LDS budget");
 
-// s_waitcnt vmcnt for "at most n DMA groups of this kernel still in flight"
-__device__ __forceinline__ void wait_b16_groups(int n) {
-  if (n >= 2)
-    wait_vm<2 * kBf16Dma>();
+// s_waitcnt vmcnt for "at most n DMA groups of G instructions still in flight"
+template <int G>
+__device__ __forceinline__ void wait_dma_groups(int n) {
+  if (n >= 3)
+    wait_vm<3 * G>();
+  else if (n == 2)
+    wait_vm<2 * G>();
   else if (n == 1)
-    wait_vm<kBf16Dma>();
+    wait_vm<G>();
   else
     wait_vm<0>();
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void decode_bf16_kernel(DecodeArgs a) {
+void decode_pipe_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
-  lds_i32* tab = (lds_i32*)(smem + kB16TabOff);
+  lds_i32* tab = (lds_i32*)(smem + kPipeTabOff(FP8));
+  constexpr int kDma = FP8 ? kF8Dma : kBf16Dma;       // DMA instructions per wave per subtile
+  constexpr int kAhead = 2;                           // subtiles in flight beyond the next one
+  constexpr int kQReg = FP8 ? 32 : 36;                // query fragments held in registers
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31, j16 = lane & 15, G = lane >> 4;
@@ -84,15 +127,85 @@ void decode_bf16_kernel(DecodeArgs a) {
     }
     wait_vm<0>();
     __syncthreads();  // page ids visible
-    auto issue = [&](int s) {
+    // DMA instruction i (0 .. kDma-1) of subtile s for this wave; the bf16
+    // tile lands swizzled, the fp8 staging (codes, k^R, scales) linear
+    auto page_rsrc = [&](int s) {
       const int pg = __builtin_amdgcn_readfirstlane(tab[s >> 1]);
       const uint8_t* blk = (const uint8_t*)a.kv + (long long)pg * a.block_bytes;
-      lds_u8* dst = smem + (s % kB16Stages) * kTileB + w_s * 1024;
-      const i32x4_t rs = make_rsrc(blk + (s & 1) * kTileB);
-#pragma unroll
-      for (int i = 0; i < kBf16Dma; ++i) dma16(rs, dma_src_offset(i * 256 + tid), dst + i * 4096);
+      return make_rsrc(FP8 ? blk : blk + (s & 1) * kTileB);
     };
-    auto tile_of = [&](int s) { return smem + (s % kB16Stages) * kTileB; };
+    auto dma_dst = [&](int s) {  // LDS base (scalar) of subtile s's DMA landing area for this wave
+      return __builtin_amdgcn_readfirstlane(
+          (int)(uint32_t)(uintptr_t)(smem + (FP8 ? (s % kF8Stages3) * kF8StageB : (s % kB16Stages) * kTileB)));
+    };
+    auto dma_one = [&](const i32x4_t& rs, int m0b, int s, int i) {
+      if (!FP8) {
+        dma16_m0(rs, dma_src_offset(i * 256 + tid), m0b + i * 4096 + w_s * 1024);
+      } else {
+        const int half = s & 1;
+        if (i < 4) {         // content codes: 16 KB, 4 x 1 KB per wave
+          dma16_m0(rs, half * kF8Codes + ((i * 4 + w) * 64 + lane) * 16, m0b + (i * 4 + w_s) * 1024);
+        } else if (i == 4) {  // RoPE keys: 4 KB
+          dma16_m0(rs, kBlk * kDc + half * kF8Kr + (w * 64 + lane) * 16, m0b + kF8Codes + w_s * 1024);
+        } else if (lane < 8) {  // scales: 128 B to the scale ring (every wave, same bytes)
+          const int ring = __builtin_amdgcn_readfirstlane(
+              (int)(uint32_t)(uintptr_t)(smem + kF8ScaleOff + (s % kF8ScaleSlots) * 128));
+          dma16_m0(rs, kBlk * (kDc + 2 * kDr) + half * (kSub * 4) + lane * 16, ring);
+        }
+      }
+    };
+    auto issue = [&](int s) {
+      const i32x4_t rs = page_rsrc(s);
+      const int m0b = dma_dst(s);
+      dma_fence();
+#pragma unroll
+      for (int i = 0; i < kDma; ++i) dma_one(rs, m0b, s, i);
+    };
+    auto tile_of = [&](int s) { return smem + (FP8 ? kF8SlotOff + (s & 1) * kTileB : (s % kB16Stages) * kTileB); };
+    // per-token scales of subtile s for this lane's rows 8qd + 4g + 0..3
+    auto scales_of = [&](int s, int qd) {
+      return *(const __attribute__((address_space(3))) f32x4_t*)(smem + kF8ScaleOff + (s % kF8ScaleSlots) * 128 +
+                                                                  16 * g + 32 * qd);
+    };
+    // fp8: expand staged subtile s into its bf16 tile slot (rows past nv -> 0).
+    // Each lane takes 16 codes (one 16-byte read) of row t = 8i + 2w + g per
+    // step i and writes the two swizzled 16-byte bf16 chunks; the four reads
+    // are issued before any conversion.  e4m3 -> bf16 with a unit scale is
+    // exact.
+    auto convert = [&](int s, int nv) {
+      const lds_u8* st = smem + (s % kF8Stages3) * kF8StageB;
+      lds_u8* tl = smem + kF8SlotOff + (s & 1) * kTileB;
+      const int c0 = 2 * l32;  // first of the lane's two 8-code chunks
+      u32x4_t cv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 8 * i + 2 * w + g;
+        cv[i] = *(const __attribute__((address_space(3))) u32x4_t*)(st + t * kDc + c0 * 8);
+      }
+      u32x4_t kr = {0, 0, 0, 0};
+      const int tr = tid >> 3, cr = tid & 7;  // RoPE: one 16-byte chunk per thread
+      if (tr < nv) kr = *(const __attribute__((address_space(3))) u32x4_t*)(st + kF8Codes + tr * 128 + cr * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 8 * i + 2 * w + g;
+        const bool ok = t < nv;
+        const int f = swz_f(t);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          u32x4_t o;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const uint32_t word = ok ? cv[i][2 * h + j] : 0u;
+            const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
+            const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true);
+            o[2 * j] = __builtin_bit_cast(uint32_t, lo);
+            o[2 * j + 1] = __builtin_bit_cast(uint32_t, hi);
+          }
+          *(__attribute__((address_space(3))) u32x4_t*)(tl + t * kRowB + (((c0 + h) ^ f) << 4)) = o;
+        }
+      }
+      *(__attribute__((address_space(3))) u32x4_t*)(tl + tr * kRowB + ((64 + (cr ^ swz_f(tr))) << 4)) = kr;
+    };
     // zero the value rows of a ragged last subtile (they may hold NaN); all threads
     auto zero_tail = [&](int s) {
       lds_u8* t_ = tile_of(s);
@@ -111,7 +224,8 @@ void decode_bf16_kernel(DecodeArgs a) {
     // queries first, then the first three subtiles: loads complete in issue
     // order, so "at most the later subtiles' groups in flight" covers both
     // the queries and subtile 0 (36 + 27 loads fit the 6-bit vmcnt)
-    bf16x8_t q[36];
+    bf16x8_t q[kQReg];
+    lds_u8* qr_lds = smem + kF8QrOff;  // fp8: RoPE query rows, kQrStride bytes per head
     {
       // uniform row base + 32-bit per-lane offset (scalar base addressing)
       const long long row0 = ((long long)b * a.s_q + qi) * kHeads;
@@ -125,20 +239,39 @@ void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8_t*)(ql + ol + kb * 32);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) q[32 + kb] = *(const bf16x8_t*)(qr + orp + kb * 32);
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8_t v = *(const bf16x8_t*)(qr + orp + kb * 32);
+        if (FP8)
+          *(__attribute__((address_space(3))) bf16x8_t*)(qr_lds + hd * kQrStride + (2 * kb + gg) * 16) = v;
+        else
+          q[(32 + kb) % kQReg] = v;
+      }
     }
+    // fp8: the q_rope copy to LDS already waits for the query loads; making
+    // that wait explicit on every path keeps the compiler from carrying
+    // them as outstanding into the subtile loop (where its own vmcnt waits
+    // would then also wait for the DMA)
+    if (FP8) wait_vm<0>();
     if (n_sub > 0) {
 #pragma unroll
-      for (int s = 0; s < kB16Stages - 1; ++s)
+      for (int s = 0; s <= kAhead; ++s)
         if (s < n_sub) issue(s);
-      wait_b16_groups(min(2, n_sub - 1));
+      wait_dma_groups<kDma>(min(kAhead, n_sub - 1));
       __syncthreads();
-      if (n_last < kSub && n_sub == 1) {
+      if (FP8) {
+        convert(0, nvalid_of(0));
+        __syncthreads();
+      } else if (n_last < kSub && n_sub == 1) {
         zero_tail(0);
         __syncthreads();
       }
     }
 
+    // B operand of QK step f: the query fragment (fp8: RoPE steps from LDS)
+    auto qfrag = [&](int f) {
+      if (FP8 && f >= 32) return lds_b128(qr_lds + head * kQrStride + (2 * (f - 32) + g) * 16);
+      return q[f % kQReg];
+    };
     // ---- helpers on LDS tiles
     // QK A-operand fragment f (0..35) of a tile: k-block f, slot group g
     auto kfrag = [&](const lds_u8* tile, int f) { return lds_b128(tile + off_qk[f & 3] + (f >> 2) * 128); };
@@ -181,8 +314,21 @@ void decode_bf16_kernel(DecodeArgs a) {
     // lazy new reference, exp2 weights in bf16 (P) and their row sum.  The
     // VALU work is split in pieces so it can sit between MFMAs.
     f32x16_t sp;    // raw S of the subtile whose P.V comes next
-    f32x16_t sc;    // S of the following subtile, accumulating
+    f32x16_t sc;    // S of the following subtile, accumulating (content part for fp8)
+    f32x16_t sr;    // fp8: its RoPE part
     bf16x8_t P[2];  // P of subtile sp
+    int sp_sub = 0; // subtile index of sp (fp8: scales of P)
+    // fp8: S = scale_t * content + RoPE for the 16 rows of a lane
+    auto form_scores = [&](int s) {
+      if (FP8) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x4_t ts = scales_of(s, qd);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[4 * qd + e] = __builtin_fmaf(sc[4 * qd + e], ts[e], sr[4 * qd + e]);
+        }
+      }
+    };
     float m_new = -INFINITY, ps0 = 0.f, ps1 = 0.f;
     float m8[8];
     auto sm_max = [&](int piece) {  // pieces 0..3
@@ -207,8 +353,16 @@ void decode_bf16_kernel(DecodeArgs a) {
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[r + 1], scale2, -m_new));
       ps0 += p0;
       ps1 += p1;
-      P[r >> 3][r & 7] = (__bf16)p0;
-      P[r >> 3][(r & 7) + 1] = (__bf16)p1;
+      if (FP8) {  // the value rows hold raw codes: their scale goes into P
+        const f32x4_t ts = scales_of(sp_sub, r >> 2);
+        const int t0 = 8 * (r >> 2) + 4 * g + (r & 3);  // masked rows may hold any scale
+        const int nv = nvalid_of(sp_sub);
+        P[r >> 3][r & 7] = (__bf16)(t0 < nv ? p0 * ts[r & 3] : 0.f);
+        P[r >> 3][(r & 7) + 1] = (__bf16)(t0 + 1 < nv ? p1 * ts[(r & 3) + 1] : 0.f);
+      } else {
+        P[r >> 3][r & 7] = (__bf16)p0;
+        P[r >> 3][(r & 7) + 1] = (__bf16)p1;
+      }
     };
     // the reference moved (rare): rescale O and the row sum before new P.V
     auto sm_commit = [&]() {
@@ -232,13 +386,16 @@ void decode_bf16_kernel(DecodeArgs a) {
       // S(0) -> sp, its first reference max
       const lds_u8* tile = tile_of(0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sp[r] = 0.f;
+      for (int r = 0; r < 16; ++r) { sc[r] = 0.f; sr[r] = 0.f; }
       bf16x8_t ka[2] = {kfrag(tile, 0), kfrag(tile, 1)};
 #pragma unroll
       for (int f = 0; f < 36; ++f) {
-        sp = mfma(ka[f & 1], q[f], sp);
+        if (FP8 && f >= 32) sr = mfma(ka[f & 1], qfrag(f), sr); else sc = mfma(ka[f & 1], qfrag(f), sc);
         if (f + 2 < 36) ka[f & 1] = kfrag(tile, f + 2);
       }
+      form_scores(0);
+      sp = sc;
+      sp_sub = 0;
       mask_tail(sp, nvalid_of(0));
       m_run = row_max(sp);
     }
@@ -246,24 +403,25 @@ void decode_bf16_kernel(DecodeArgs a) {
     constexpr int kQkA = 16;  // QK steps overlapped with the softmax
     for (int it = 0; it + 1 < n_sub; ++it) {
       // ---- (A) next subtile resident; refill the stage subtile it-1 used
-      wait_b16_groups(min(1, n_sub - 2 - it));
+      wait_dma_groups<kDma>(min(kAhead - 1, n_sub - 2 - it));
       __syncthreads();
-      // subtile it+3 goes to the stage subtile it-1 used; its 9 DMA
-      // instructions are spread over the QK steps below
-      const bool dma_on = it + 3 < n_sub;
+      if (FP8) {  // expand subtile it+1 into the slot subtile it-1 used
+        convert(it + 1, nvalid_of(it + 1));
+        __syncthreads();
+      } else if (it + 1 == n_sub - 1 && n_last < kSub) {
+        zero_tail(it + 1);
+        __syncthreads();
+      }
+      // subtile it+kAhead+1 goes to the stage subtile it-1 (bf16) / it (fp8)
+      // used; its DMA instructions are spread over the QK steps below
+      const int s_dma = it + kAhead + 1;
+      const bool dma_on = s_dma < n_sub;
       i32x4_t dma_rs = {0, 0, 0, 0};
       int dma_m0 = 0;
       if (dma_on) {
-        const int s3 = it + 3;
-        const int pg = __builtin_amdgcn_readfirstlane(tab[s3 >> 1]);
-        dma_rs = make_rsrc((const uint8_t*)a.kv + (long long)pg * a.block_bytes + (s3 & 1) * kTileB);
-        dma_m0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(smem + (s3 % kB16Stages) * kTileB)) +
-                 w_s * 1024;
+        dma_rs = page_rsrc(s_dma);
+        dma_m0 = dma_dst(s_dma);
         dma_fence();
-      }
-      if (it + 1 == n_sub - 1 && n_last < kSub) {
-        zero_tail(it + 1);
-        __syncthreads();
       }
       const lds_u8* tile = tile_of(it);
       const lds_u8* tile_n = tile_of(it + 1);
@@ -271,11 +429,11 @@ void decode_bf16_kernel(DecodeArgs a) {
       // ---- phase 1: QK(it+1) steps 0..15 (one dependent chain) with the
       //      softmax of subtile it in the gaps
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+      for (int r = 0; r < 16; ++r) { sc[r] = 0.f; sr[r] = 0.f; }
       bf16x8_t ka[2] = {kfrag(tile_n, 0), kfrag(tile_n, 1)};
 #pragma unroll
       for (int f = 0; f < kQkA; ++f) {
-        sc = mfma(ka[f & 1], q[f], sc);
+        sc = mfma(ka[f & 1], qfrag(f), sc);
         ka[f & 1] = kfrag(tile_n, f + 2);
         if (f < 4) sm_max(f);
         else if (f < 12) sm_exp(2 * (f - 4));
@@ -292,7 +450,7 @@ void decode_bf16_kernel(DecodeArgs a) {
       int step = 0;
 #pragma unroll
       for (int f = kQkA; f < 36; ++f) {
-        sc = mfma(ka[f & 1], q[f], sc);
+        if (FP8 && f >= 32) sr = mfma(ka[f & 1], qfrag(f), sr); else sc = mfma(ka[f & 1], qfrag(f), sc);
         if (f + 2 < 36) ka[f & 1] = kfrag(tile_n, f + 2);
         const int npv = (f - kQkA) < 12 ? 2 : 1;
 #pragma unroll
@@ -301,13 +459,12 @@ void decode_bf16_kernel(DecodeArgs a) {
           if (step + 2 < 32) va[step & 1] = vfrag(tile, step + 2);
           ++step;
         }
-        if (((f - kQkA) & 1) == 0 && (f - kQkA) / 2 < kBf16Dma && dma_on) {
-          const int k4 = (f - kQkA) / 2;
-          dma16_m0(dma_rs, dma_src_offset(k4 * 256 + tid), dma_m0 + k4 * 4096);
-        }
+        if (((f - kQkA) & 1) == 0 && (f - kQkA) / 2 < kDma && dma_on) dma_one(dma_rs, dma_m0, s_dma, (f - kQkA) / 2);
         __builtin_amdgcn_sched_barrier(0);
       }
+      form_scores(it + 1);
       sp = sc;
+      sp_sub = it + 1;
       mask_tail(sp, nvalid_of(it + 1));
     }
     if (n_sub > 0) {  // the last subtile: softmax and P.V only
@@ -400,16 +557,20 @@ void decode_bf16_kernel(DecodeArgs a) {
   }
 }
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, int grid_x, hipStream_t s) {
+template <bool FP8>
+static hipError_t launch_pipe(const DecodeArgs& a, int grid_x, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_bf16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       kB16Lds);
+    hipError_t e = hipFuncSetAttribute((const void*)decode_pipe_kernel<FP8>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kPipeLds(FP8));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(decode_bf16_kernel, dim3(grid_x, a.s_q), dim3(256), kB16Lds, s, a);
+  hipLaunchKernelGGL(decode_pipe_kernel<FP8>, dim3(grid_x, a.s_q), dim3(256), kPipeLds(FP8), s, a);
   return hipGetLastError();
 }
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, int grid_x, hipStream_t s) { return launch_pipe<false>(a, grid_x, s); }
+hipError_t launch_decode_fp8(const DecodeArgs& a, int grid_x, hipStream_t s) { return launch_pipe<true>(a, grid_x, s); }
 
 }  // namespace mla
