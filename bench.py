@@ -35,7 +35,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 CSRC = os.path.join(ROOT, "mla_latent_kv_05_amd", "csrc")
 # sources of the bf16-cache attention kernel (the traffic counters are tied to them)
-KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("decode_mfma_bf16.hip", "mfma_common.h", "device_util.h")]
+KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("decode_mfma.hip", "mfma_common.h", "device_util.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_kernel_B64_ctx8192_traffic.md")
 
 

@@ -1,45 +1,85 @@
-// Split-KV MFMA decode kernel for the DeepSeek-V2/V3 shape of absorbed MLA:
-// n_h = 128 query heads sharing one latent cache row [c^KV 512 | k^R 64]
-// (itwiki "Multi-head latent attention": sections "Decoupled RoPE", "Matrix
-// absorption", and the V2/V3 dimension table), 64-token pages, bf16 or
-// fp8-e4m3 content.  The itwiki page's "Implementation" section notes that
-// this shape (576-wide keys, 512-wide values shared by 128 heads) needs a
-// dedicated kernel.
+// Software-pipelined MFMA decode kernel for the DeepSeek-V2/V3 shape of
+// absorbed MLA (itwiki "Multi-head latent attention": sections "Decoupled
+// RoPE", "Matrix absorption" and the V2/V3 dimension table): n_h = 128 heads
+// sharing one latent row [c^KV 512 | k^R 64] per token, 64-token pages, bf16
+// or fp8-e4m3 content.
 //
 // Work decomposition
 //   * grid.x = persistent workgroups looping over planned units (sequence,
 //     contiguous page range); grid.y = query token i of the sequence.
 //   * 4 wavefronts, one per SIMD; wavefront w owns heads 32w .. 32w+31 for
-//     both contractions, so P never leaves registers.
-//   * The unit's keys stream through LDS in 32-token subtiles (36,864 B of
-//     bf16 rows), loaded with 16-byte global->LDS DMA into kStages buffers.
+//     both contractions: its queries stay in VGPRs, its P.V accumulator
+//     (32 heads x 512 dims fp32) fills the AGPRs.
+//   * Keys stream through LDS in 32-token subtiles of bf16 rows (36,864 B):
+//     16-byte global->LDS DMA straight into a 4-stage ring (bf16 cache), or
+//     into an fp8 staging ring that the workgroup expands into one of two
+//     bf16 tile slots (fp8 cache; e4m3 -> bf16 is exact).
 //   * S^T[token, head] = K[token, 0:576] . Q^T on v_mfma_f32_32x32x16_bf16
-//     (A = key rows from LDS via ds_read_b128, B = queries held in VGPRs).
+//     (A = key rows from LDS via ds_read_b128, B = queries from registers).
 //   * O^T[dim, head] += V^T[dim, token] . P^T[token, head]: A = c^KV columns
-//     fetched transposed with ds_read_tr16_b64, B = P taken straight from the
-//     S^T accumulator layout (each lane owns one head in both products).
-//   * Online softmax in base 2 with lazy rescaling: the running reference
-//     max only moves when a subtile's max exceeds it by more than kTau, so the
-//     256-register accumulator is rarely touched outside the MFMAs.  The
-//     result is exact: numerator and denominator share the reference.
-//   * fp8 content: codes are DMA'd to a staging area and expanded to the
-//     bf16 tile layout (e4m3 -> bf16 is exact); the per-token scale is folded
-//     into the content score and into P before the P.V product.
+//     fetched transposed with ds_read_b64_tr_b16, B = P taken straight from
+//     the S^T accumulator layout (the lane is the head in both products).
+//   * fp8: the per-token scale multiplies the content score (the RoPE part
+//     accumulates separately) and P before the P.V product.
+//   * Online softmax in the exp2 domain with a lazy reference max: the
+//     reference only moves when a subtile's max exceeds it by 2^kTau, so the
+//     accumulator is rarely touched outside the MFMAs (numerator and
+//     denominator share the reference, so the result is exact).
+//
+// Pipeline (iteration i; subtile i+1 resident before it starts)
+//   phase 1: QK(i+1) steps 0..15  ||  softmax of subtile i (max, exp2, P)
+//   phase 2: QK(i+1) steps 16..35 interleaved with the 32 P.V steps of
+//            subtile i; the DMA of a later subtile rides along
 //
 // LDS tile layout: row t (token) is 1152 B = 72 chunks of 16 B; logical chunk
-// c is stored at chunk (c & ~7) | ((c ^ f(t)) & 7), f(t) = ((t&3)<<1)|((t>>2)&1),
-// which keeps both the 8-row b128 reads of the QK step and the 4-row
-// transposed reads of the PV step free of bank conflicts.
+// c is stored at chunk (c & ~7) | ((c ^ f(t)) & 7), f(t) = bits 2, 3, 1 of t
+// (swz_f), chosen by measuring both read patterns.  The unit's partial (or
+// final) output is staged through LDS so each store writes whole rows.
 #include "mfma_common.h"
 
 namespace mla {
 
+// bf16 cache: 4 tile stages (tiles i, i+1 in use, i+2, i+3 in flight)
+constexpr int kB16Stages = 4;
+constexpr int kB16TabOff = kB16Stages * kTileB;             // 147456
+// fp8 cache: 3 staging stages (codes + k^R; subtile i+1 being expanded,
+// i+2 and i+3 in flight), a ring of per-token scales, two bf16 tile slots,
+// and the queries' RoPE part (its own score accumulator takes those registers)
+constexpr int kF8StageB = kF8Codes + kF8Kr;                 // 20480 per subtile
+constexpr int kF8Stages3 = 3;
+constexpr int kF8ScaleSlots = 8;                            // scales of subtile s at slot s % 8
+constexpr int kF8ScaleOff = kF8Stages3 * kF8StageB;         // 61440
+constexpr int kF8SlotOff = kF8ScaleOff + kF8ScaleSlots * 128;  // 62464
+constexpr int kF8QrOff = kF8SlotOff + 2 * kTileB;           // 136192
+constexpr int kF8TabOff = kF8QrOff + kHeads * kQrStride;    // 154624
+constexpr int kPipeTabOff(bool fp8) { return fp8 ? kF8TabOff : kB16TabOff; }
+constexpr int kPipeLds(bool fp8) { return kPipeTabOff(fp8) + kMaxUnitPages * 4; }  // 149504 / 156672
+constexpr int kOutRowF = kDc + 4;                           // padded fp32 row of the output staging
+constexpr int kOutRowH = kDc * 2 + 16;                      // padded bf16 row (bytes)
+static_assert(kPipeLds(true) <= 160 * 1024, "LDS budget");
+
+// s_waitcnt vmcnt for "at most n DMA groups of G instructions still in flight"
+template <int G>
+__device__ __forceinline__ void wait_dma_groups(int n) {
+  if (n >= 3)
+    wait_vm<3 * G>();
+  else if (n == 2)
+    wait_vm<2 * G>();
+  else if (n == 1)
+    wait_vm<G>();
+  else
+    wait_vm<0>();
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void decode_mfma_kernel(DecodeArgs a) {
+void decode_pipe_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
-  lds_i32* tab = (lds_i32*)(smem + kTabOff(FP8));
+  lds_i32* tab = (lds_i32*)(smem + kPipeTabOff(FP8));
+  constexpr int kDma = FP8 ? kF8Dma : kBf16Dma;       // DMA instructions per wave per subtile
+  constexpr int kAhead = 2;                           // subtiles in flight beyond the next one
+  constexpr int kQReg = FP8 ? 32 : 36;                // query fragments held in registers
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31, j16 = lane & 15, G = lane >> 4;
@@ -49,7 +89,6 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int n_units = ((const WsHeader*)a.ws_header)->n_units;
   const float scale2 = a.scale * kLog2e;
 
-  // ---- lane-constant LDS offsets
   int off_qk[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) off_qk[j] = l32 * kRowB + (((2 * j + g) ^ swz_f(l32)) << 4);
@@ -67,19 +106,7 @@ void decode_mfma_kernel(DecodeArgs a) {
         off_pv[p][h] = t * kRowB + (((4 * p + clo) ^ swz_f(t)) << 4) + (j16 & 1) * 8;
       }
   }
-  // DMA source offsets of this lane within a bf16 subtile (LDS chunk -> global chunk)
-  // (16-bit pairs: offsets are < 36864)
-  uint32_t goff2[(kBf16Dma + 1) / 2];
-#pragma unroll
-  for (int i = 0; i < (kBf16Dma + 1) / 2; ++i) goff2[i] = 0;
-#pragma unroll
-  for (int i = 0; i < kBf16Dma; ++i) {
-    const int p = (i * 4 + w) * 64 + lane;
-    const int t = p / 72, cp = p - t * 72;
-    const int c = (cp & ~7) | ((cp ^ swz_f(t)) & 7);
-    goff2[i >> 1] |= (uint32_t)(t * kRowB + c * 16) << (16 * (i & 1));
-  }
-
+  const int w_s = __builtin_amdgcn_readfirstlane(w);  // wave index as a scalar
   for (int unit = xcd_slot(blockIdx.x, gridDim.x); unit < n_units; unit += gridDim.x) {
     const int4 wk = a.work[unit];
     const int b = wk.x;
@@ -90,276 +117,461 @@ void decode_mfma_kernel(DecodeArgs a) {
     const int ntok = tok1 - tok0;
     const int n_sub = ntok > 0 ? (ntok + kSub - 1) / kSub : 0;
     const int n_last = ntok - (n_sub - 1) * kSub;  // valid rows of the last subtile
+    auto nvalid_of = [&](int t) { return t == n_sub - 1 ? n_last : kSub; };
 
-    __syncthreads();  // previous unit finished with LDS
+    __syncthreads();  // the previous unit is done with LDS
     {
       const int npg = (n_sub * kSub + kBlk - 1) / kBlk;
       const int32_t* trow = a.table + (long long)b * a.max_blocks + wk.y;
       for (int i = tid; i < npg; i += 256) tab[i] = trow[i];
     }
-    // queries of this lane's head: B operand slots (l/32)*8 .. +7 of each 16-dim k-block.
-    // The fp8 path keeps the RoPE slice in LDS (its extra score accumulator
-    // needs those registers).
-    constexpr int kQReg = FP8 ? 32 : 36;
-    bf16x8_t q[kQReg];
-    lds_u8* qr_lds = smem + kQrOff(FP8);
-    {
-      const long long qrow = ((long long)b * a.s_q + qi) * kHeads + head;
-      const bf16x8_t* ql = (const bf16x8_t*)((const uint16_t*)a.q_lat + qrow * kDc);
-      const bf16x8_t* qr = (const bf16x8_t*)((const uint16_t*)a.q_rope + qrow * kDr);
-#pragma unroll
-      for (int kb = 0; kb < 32; ++kb) q[kb] = ql[2 * kb + g];
-      if (FP8) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          *(__attribute__((address_space(3))) bf16x8_t*)(qr_lds + head * kQrStride + (2 * kb + g) * 16) =
-              qr[2 * kb + g];
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) q[kQReg - 4 + kb] = qr[2 * kb + g];
-      }
-    }
     wait_vm<0>();
     __syncthreads();  // page ids visible
-
-    auto issue = [&](int s) {
+    // DMA instruction i (0 .. kDma-1) of subtile s for this wave; the bf16
+    // tile lands swizzled, the fp8 staging (codes, k^R, scales) linear
+    auto page_rsrc = [&](int s) {
       const int pg = __builtin_amdgcn_readfirstlane(tab[s >> 1]);
       const uint8_t* blk = (const uint8_t*)a.kv + (long long)pg * a.block_bytes;
-      const int half = s & 1;
+      return make_rsrc(FP8 ? blk : blk + (s & 1) * kTileB);
+    };
+    auto dma_dst = [&](int s) {  // LDS base (scalar) of subtile s's DMA landing area for this wave
+      return __builtin_amdgcn_readfirstlane(
+          (int)(uint32_t)(uintptr_t)(smem + (FP8 ? (s % kF8Stages3) * kF8StageB : (s % kB16Stages) * kTileB)));
+    };
+    auto dma_one = [&](const i32x4_t& rs, int m0b, int s, int i) {
       if (!FP8) {
-        lds_u8* dst = smem + (s % kStages) * kTileB + w * 1024;
-        const i32x4_t rs = make_rsrc(blk + half * kTileB);
-#pragma unroll
-        for (int i = 0; i < kBf16Dma; ++i) dma16(rs, (int)((goff2[i >> 1] >> (16 * (i & 1))) & 0xffffu), dst + i * 4096);
+        dma16_m0(rs, dma_src_offset(i * 256 + tid), m0b + i * 4096 + w_s * 1024);
       } else {
-        lds_u8* dst = smem + (s % kStages) * kF8Stage;
-        const i32x4_t rs = make_rsrc(blk);
+        const int half = s & 1;
+        if (i < 4) {         // content codes: 16 KB, 4 x 1 KB per wave
+          dma16_m0(rs, half * kF8Codes + ((i * 4 + w) * 64 + lane) * 16, m0b + (i * 4 + w_s) * 1024);
+        } else if (i == 4) {  // RoPE keys: 4 KB
+          dma16_m0(rs, kBlk * kDc + half * kF8Kr + (w * 64 + lane) * 16, m0b + kF8Codes + w_s * 1024);
+        } else if (lane < 8) {  // scales: 128 B to the scale ring (every wave, same bytes)
+          const int ring = __builtin_amdgcn_readfirstlane(
+              (int)(uint32_t)(uintptr_t)(smem + kF8ScaleOff + (s % kF8ScaleSlots) * 128));
+          dma16_m0(rs, kBlk * (kDc + 2 * kDr) + half * (kSub * 4) + lane * 16, ring);
+        }
+      }
+    };
+    auto issue = [&](int s) {
+      const i32x4_t rs = page_rsrc(s);
+      const int m0b = dma_dst(s);
+      dma_fence();
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dma16(rs, half * kF8Codes + ((i * 4 + w) * 64 + lane) * 16, dst + (i * 4 + w) * 1024);
-        dma16(rs, kBlk * kDc + half * kF8Kr + (w * 64 + lane) * 16, dst + kF8Codes + w * 1024);
-        // every wave issues the (identical) scale load so all waves count kF8Dma per subtile
-        if (lane < 8)
-          dma16(rs, kBlk * (kDc + 2 * kDr) + half * (kSub * 4) + lane * 16, dst + kF8Codes + kF8Kr);
+      for (int i = 0; i < kDma; ++i) dma_one(rs, m0b, s, i);
+    };
+    auto tile_of = [&](int s) { return smem + (FP8 ? kF8SlotOff + (s & 1) * kTileB : (s % kB16Stages) * kTileB); };
+    // per-token scales of subtile s for this lane's rows 8qd + 4g + 0..3
+    auto scales_of = [&](int s, int qd) {
+      return *(const __attribute__((address_space(3))) f32x4_t*)(smem + kF8ScaleOff + (s % kF8ScaleSlots) * 128 +
+                                                                  16 * g + 32 * qd);
+    };
+    // fp8: expand staged subtile s into its bf16 tile slot (rows past nv -> 0).
+    // Each lane takes 16 codes (one 16-byte read) of row t = 8i + 2w + g per
+    // step i and writes the two swizzled 16-byte bf16 chunks; the four reads
+    // are issued before any conversion.  e4m3 -> bf16 with a unit scale is
+    // exact.
+    auto convert = [&](int s, int nv) {
+      const lds_u8* st = smem + (s % kF8Stages3) * kF8StageB;
+      lds_u8* tl = smem + kF8SlotOff + (s & 1) * kTileB;
+      const int c0 = 2 * l32;  // first of the lane's two 8-code chunks
+      u32x4_t cv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 8 * i + 2 * w + g;
+        cv[i] = *(const __attribute__((address_space(3))) u32x4_t*)(st + t * kDc + c0 * 8);
+      }
+      u32x4_t kr = {0, 0, 0, 0};
+      const int tr = tid >> 3, cr = tid & 7;  // RoPE: one 16-byte chunk per thread
+      if (tr < nv) kr = *(const __attribute__((address_space(3))) u32x4_t*)(st + kF8Codes + tr * 128 + cr * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 8 * i + 2 * w + g;
+        const bool ok = t < nv;
+        const int f = swz_f(t);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          u32x4_t o;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const uint32_t word = ok ? cv[i][2 * h + j] : 0u;
+            const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
+            const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true);
+            o[2 * j] = __builtin_bit_cast(uint32_t, lo);
+            o[2 * j + 1] = __builtin_bit_cast(uint32_t, hi);
+          }
+          *(__attribute__((address_space(3))) u32x4_t*)(tl + t * kRowB + (((c0 + h) ^ f) << 4)) = o;
+        }
+      }
+      *(__attribute__((address_space(3))) u32x4_t*)(tl + tr * kRowB + ((64 + (cr ^ swz_f(tr))) << 4)) = kr;
+    };
+    // zero the value rows of a ragged last subtile (they may hold NaN); all threads
+    auto zero_tail = [&](int s) {
+      lds_u8* t_ = tile_of(s);
+      const int nv = nvalid_of(s);
+      for (int e = tid; e < (kSub - nv) * 72; e += 256) {
+        const int t = nv + e / 72, c = e % 72;
+        *(__attribute__((address_space(3))) u32x4_t*)(t_ + t * kRowB + c * 16) = u32x4_t{0, 0, 0, 0};
       }
     };
 
     f32x16_t acc[16];
-#pragma unroll
-    for (int d = 0; d < 16; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
+    zero_acc(acc);
     acc_fence(acc);
     float m_run = -INFINITY, l_run = 0.f;
 
-    // prologue
+    // queries first, then the first three subtiles: loads complete in issue
+    // order, so "at most the later subtiles' groups in flight" covers both
+    // the queries and subtile 0 (36 + 27 loads fit the 6-bit vmcnt)
+    bf16x8_t q[kQReg];
+    lds_u8* qr_lds = smem + kF8QrOff;  // fp8: RoPE query rows, kQrStride bytes per head
+    {
+      // uniform row base + 32-bit per-lane offset (scalar base addressing)
+      const long long row0 = ((long long)b * a.s_q + qi) * kHeads;
+      const uint8_t* ql = (const uint8_t*)a.q_lat + row0 * (kDc * 2);
+      const uint8_t* qr = (const uint8_t*)a.q_rope + row0 * (kDr * 2);
+      // recomputed here rather than kept live across the unit loop
+      int hl = threadIdx.x;
+      asm volatile("" : "+v"(hl));
+      const int hd = (hl >> 6) * 32 + (hl & 31), gg = (hl >> 5) & 1;
+      const int ol = hd * (kDc * 2) + gg * 16, orp = hd * (kDr * 2) + gg * 16;
 #pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-      if (s < n_sub) issue(s);
-
-    for (int it = 0; it < n_sub; ++it) {
-      const int outstanding = min(kStages - 2, n_sub - 1 - it);
-      if (FP8) wait_groups<kF8Dma>(outstanding); else wait_groups<kBf16Dma>(outstanding);
+      for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8_t*)(ql + ol + kb * 32);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8_t v = *(const bf16x8_t*)(qr + orp + kb * 32);
+        if (FP8)
+          *(__attribute__((address_space(3))) bf16x8_t*)(qr_lds + hd * kQrStride + (2 * kb + gg) * 16) = v;
+        else
+          q[(32 + kb) % kQReg] = v;
+      }
+    }
+    // fp8: the q_rope copy to LDS already waits for the query loads; making
+    // that wait explicit on every path keeps the compiler from carrying
+    // them as outstanding into the subtile loop (where its own vmcnt waits
+    // would then also wait for the DMA)
+    if (FP8) wait_vm<0>();
+    if (n_sub > 0) {
+#pragma unroll
+      for (int s = 0; s <= kAhead; ++s)
+        if (s < n_sub) issue(s);
+      wait_dma_groups<kDma>(min(kAhead, n_sub - 1));
       __syncthreads();
-      if (it + kStages - 1 < n_sub) issue(it + kStages - 1);
-      const bool ragged = (it == n_sub - 1) && (n_last < kSub);
-      const int nvalid = ragged ? n_last : kSub;
-
-      lds_u8* tile;
-      if (!FP8) {
-        tile = smem + (it % kStages) * kTileB;
-        if (ragged) {  // zero the value rows past the end (they may hold NaN)
-          for (int e = tid; e < (kSub - nvalid) * 72; e += 256) {
-            const int t = nvalid + e / 72, c = e % 72;
-            *(__attribute__((address_space(3))) u32x4_t*)(tile + t * kRowB + c * 16) = u32x4_t{0, 0, 0, 0};
-          }
-          __syncthreads();
-        }
-      } else {
-        const lds_u8* st = smem + (it % kStages) * kF8Stage;
-        tile = smem + kStages * kF8Stage;
-#pragma unroll 1
-        for (int i = 0; i < 8; ++i) {
-          const int qd = tid + 256 * i;
-          const int t = qd >> 6, c = qd & 63;
-          u32x4_t o = {0, 0, 0, 0};
-          if (t < nvalid) {
-            const u32x2_t cw = *(const __attribute__((address_space(3))) u32x2_t*)(st + t * kDc + c * 8);
-            o[0] = fp8x2_to_bf16x2<false>(cw[0]);
-            o[1] = fp8x2_to_bf16x2<true>(cw[0]);
-            o[2] = fp8x2_to_bf16x2<false>(cw[1]);
-            o[3] = fp8x2_to_bf16x2<true>(cw[1]);
-          }
-          *(__attribute__((address_space(3))) u32x4_t*)(tile + t * kRowB + (((c & ~7) | ((c ^ swz_f(t)) & 7)) << 4)) = o;
-        }
-        {
-          const int t = tid >> 3, cc = tid & 7;
-          const u32x4_t v = *(const __attribute__((address_space(3))) u32x4_t*)(st + kF8Codes + t * 128 + cc * 16);
-          *(__attribute__((address_space(3))) u32x4_t*)(tile + t * kRowB + ((64 + (cc ^ swz_f(t))) << 4)) = v;
-        }
+      if (FP8) {
+        convert(0, nvalid_of(0));
+        __syncthreads();
+      } else if (n_last < kSub && n_sub == 1) {
+        zero_tail(0);
         __syncthreads();
       }
+    }
 
-      // ---- S^T = K . Q^T  (rolling prefetch: fragment j of the next 4-step
-      //      group is requested as soon as the MFMA consuming slot j issues)
-      f32x16_t sc, sr;
+    // B operand of QK step f: the query fragment (fp8: RoPE steps from LDS)
+    auto qfrag = [&](int f) {
+      if (FP8 && f >= 32) return lds_b128(qr_lds + head * kQrStride + (2 * (f - 32) + g) * 16);
+      return q[f % kQReg];
+    };
+    // ---- helpers on LDS tiles
+    // QK A-operand fragment f (0..35) of a tile: k-block f, slot group g
+    auto kfrag = [&](const lds_u8* tile, int f) { return lds_b128(tile + off_qk[f & 3] + (f >> 2) * 128); };
+    // PV A-operand fragment of step (db, ks): V^T[dims db*32.., tokens 16ks + {4g..4g+3, 8+4g..}]
+    auto vfrag = [&](const lds_u8* tile, int step) {
+      const int db = step & 15, ks = step >> 4;  // ks-outer order
+      const int kofs = (db >> 1) * 128 + ks * 16 * kRowB;
+      const bf16x4_t lo = lds_tr16(tile + off_pv[db & 1][0] + kofs);
+      const bf16x4_t hi = lds_tr16(tile + off_pv[db & 1][1] + kofs);
+      bf16x8_t v;
+      v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+      v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+      return v;
+    };
+    // raw scores of the token rows past the end of a ragged subtile -> -inf
+    // (a uniform branch; full subtiles skip it)
+    auto mask_tail = [&](f32x16_t& sv, int nv) {
+      if (nv < kSub) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { sc[r] = 0.f; sr[r] = 0.f; }
-      {
-        const lds_u8* pk[4] = {tile + off_qk[0], tile + off_qk[1], tile + off_qk[2], tile + off_qk[3]};
-        bf16x8_t ka[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ka[j] = lds_b128(pk[j]);
-#pragma unroll
-        for (int k4 = 0; k4 < 9; ++k4) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (FP8 && k4 >= 8)
-              sr = mfma(ka[j], lds_b128(qr_lds + head * kQrStride + (2 * j + g) * 16), sr);
-            else
-              sc = mfma(ka[j], q[(4 * k4 + j) % kQReg], sc);
-            if (k4 < 8) ka[j] = lds_b128(pk[j] + (k4 + 1) * 128);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+        for (int r = 0; r < 16; ++r) {
+          const int t = 8 * (r >> 2) + 4 * g + (r & 3);
+          sv[r] = t < nv ? sv[r] : -INFINITY;
         }
       }
+    };
+    // max of the 16 raw scores of a lane (tree), then of the two wave halves
+    // holding the same head, in the exp2 domain (the scale is positive)
+    auto row_max = [&](const f32x16_t& sv) {
+      float m8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m8[i] = fmaxf(sv[2 * i], sv[2 * i + 1]);
+#pragma unroll
+      for (int w2 = 4; w2 >= 1; w2 >>= 1)
+#pragma unroll
+        for (int i = 0; i < w2; ++i) m8[i] = fmaxf(m8[i], m8[i + w2]);
+      return half_swap_max(m8[0]) * scale2;
+    };
 
-      // ---- scores, mask, online softmax (lane: head, 16 tokens 8(r/4)+4g+r%4)
-      // fp8: per-token scales of this lane's tokens, 4 groups of 4 consecutive
-      const lds_u8* scl = smem + (it % kStages) * kF8Stage + kF8Codes + kF8Kr + 16 * g;
-      auto token_scale = [&](int qd) {
-        return *(const __attribute__((address_space(3))) f32x4_t*)(scl + 32 * qd);
-      };
-      float s[16];
-      float mx = -INFINITY;
+    // softmax of the raw scores sp of one subtile against the running max:
+    // lazy new reference, exp2 weights in bf16 (P) and their row sum.  The
+    // VALU work is split in pieces so it can sit between MFMAs.
+    f32x16_t sp;    // raw S of the subtile whose P.V comes next
+    f32x16_t sc;    // S of the following subtile, accumulating (content part for fp8)
+    f32x16_t sr;    // fp8: its RoPE part
+    bf16x8_t P[2];  // P of subtile sp
+    int sp_sub = 0; // subtile index of sp (fp8: scales of P)
+    // fp8: S = scale_t * content + RoPE for the 16 rows of a lane
+    auto form_scores = [&](int s) {
+      if (FP8) {
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        f32x4_t ts;
-        if (FP8) ts = token_scale(qd);
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x4_t ts = scales_of(s, qd);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * qd + e;
-          const int t = 8 * qd + 4 * g + e;
-          float v = FP8 ? (sc[r] * ts[e] + sr[r]) : sc[r];
-          v *= scale2;
-          if (ragged && t >= nvalid) v = -INFINITY;
-          s[r] = v;
-          mx = fmaxf(mx, v);
+          for (int e = 0; e < 4; ++e) sc[4 * qd + e] = __builtin_fmaf(sc[4 * qd + e], ts[e], sr[4 * qd + e]);
         }
       }
-      mx = half_swap_max(mx);
-      if (m_run == -INFINITY) {
-        m_run = mx;  // first subtile: the accumulator is still zero
-      } else if (mx > m_run + kTau) {
-        const float f = __builtin_amdgcn_exp2f(m_run - mx);
+    };
+    float m_new = -INFINITY, ps0 = 0.f, ps1 = 0.f;
+    float m8[8];
+    auto sm_max = [&](int piece) {  // pieces 0..3
+      if (piece == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m8[i] = fmaxf(sp[2 * i], sp[2 * i + 1]);
+      } else if (piece == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m8[i] = fmaxf(m8[i], m8[i + 4]);
+      } else if (piece == 2) {
+        m8[0] = fmaxf(m8[0], m8[2]);
+        m8[1] = fmaxf(m8[1], m8[3]);
+        m8[0] = fmaxf(m8[0], m8[1]);
+      } else {
+        const float mx = half_swap_max(m8[0]) * scale2;
+        m_new = mx > m_run + kTau ? mx : m_run;  // lazy: keep the reference unless far behind
+        ps0 = ps1 = 0.f;
+      }
+    };
+    auto sm_exp = [&](int r) {  // rows r, r+1
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[r], scale2, -m_new));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[r + 1], scale2, -m_new));
+      ps0 += p0;
+      ps1 += p1;
+      if (FP8) {  // the value rows hold raw codes: their scale goes into P
+        const f32x4_t ts = scales_of(sp_sub, r >> 2);
+        const int t0 = 8 * (r >> 2) + 4 * g + (r & 3);  // masked rows may hold any scale
+        const int nv = nvalid_of(sp_sub);
+        P[r >> 3][r & 7] = (__bf16)(t0 < nv ? p0 * ts[r & 3] : 0.f);
+        P[r >> 3][(r & 7) + 1] = (__bf16)(t0 + 1 < nv ? p1 * ts[(r & 3) + 1] : 0.f);
+      } else {
+        P[r >> 3][r & 7] = (__bf16)p0;
+        P[r >> 3][(r & 7) + 1] = (__bf16)p1;
+      }
+    };
+    // the reference moved (rare): rescale O and the row sum before new P.V
+    auto sm_commit = [&]() {
+      if (m_new != m_run) {
+        const float f = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= f;
         acc_fence(acc);
 #pragma unroll
         for (int d = 0; d < 16; ++d) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[d][r] *= f;
-          asm volatile("" : "+a"(acc[d]));  // back to AGPRs block by block
+          asm volatile("" : "+a"(acc[d]));
         }
         acc_fence(acc);
-        m_run = mx;
+        m_run = m_new;
       }
-      float ps = 0.f;
-      bf16x8_t P[2];
-      if (FP8) asm volatile("" ::: "memory");  // re-read the token scales instead of keeping 16 live
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        f32x4_t ts;
-        if (FP8) ts = token_scale(qd);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * qd + e;
-          float p = __builtin_amdgcn_exp2f(s[r] - m_run);
-          ps += p;
-          if (FP8) {
-            const int t = 8 * qd + 4 * g + e;
-            p = (ragged && t >= nvalid) ? 0.f : p * ts[e];  // masked rows may hold any scale
-          }
-          P[r >> 3][r & 7] = (__bf16)p;
-        }
-      }
-      l_run += ps;
+      l_run += ps0 + ps1;
+    };
 
-      // ---- O^T += V^T . P^T  (rolling prefetch of the transposed value reads)
-      {
-        auto load_v = [&](int db, int ks) {
-          const int kofs = (db >> 1) * 128 + ks * 16 * kRowB;
-          const bf16x4_t lo = lds_tr16(tile + off_pv[db & 1][0] + kofs);
-          const bf16x4_t hi = lds_tr16(tile + off_pv[db & 1][1] + kofs);
-          bf16x8_t v;
-          v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
-          v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
-          return v;
-        };
-        bf16x8_t va[2] = {load_v(0, 0), load_v(0, 1)};
+    if (n_sub > 0) {
+      // S(0) -> sp, its first reference max
+      const lds_u8* tile = tile_of(0);
 #pragma unroll
-        for (int db = 0; db < 16; ++db) {
+      for (int r = 0; r < 16; ++r) { sc[r] = 0.f; sr[r] = 0.f; }
+      bf16x8_t ka[2] = {kfrag(tile, 0), kfrag(tile, 1)};
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            mfma_acc(acc[db], va[ks], P[ks]);
-            if (db < 15) va[ks] = load_v(db + 1, ks);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+      for (int f = 0; f < 36; ++f) {
+        if (FP8 && f >= 32) sr = mfma(ka[f & 1], qfrag(f), sr); else sc = mfma(ka[f & 1], qfrag(f), sc);
+        if (f + 2 < 36) ka[f & 1] = kfrag(tile, f + 2);
+      }
+      form_scores(0);
+      sp = sc;
+      sp_sub = 0;
+      mask_tail(sp, nvalid_of(0));
+      m_run = row_max(sp);
+    }
+
+    constexpr int kQkA = 16;  // QK steps overlapped with the softmax
+    for (int it = 0; it + 1 < n_sub; ++it) {
+      // ---- (A) next subtile resident; refill the stage subtile it-1 used
+      wait_dma_groups<kDma>(min(kAhead - 1, n_sub - 2 - it));
+      __syncthreads();
+      if (FP8) {  // expand subtile it+1 into the slot subtile it-1 used
+        convert(it + 1, nvalid_of(it + 1));
+        __syncthreads();
+      } else if (it + 1 == n_sub - 1 && n_last < kSub) {
+        zero_tail(it + 1);
+        __syncthreads();
+      }
+      // subtile it+kAhead+1 goes to the stage subtile it-1 (bf16) / it (fp8)
+      // used; its DMA instructions are spread over the QK steps below
+      const int s_dma = it + kAhead + 1;
+      const bool dma_on = s_dma < n_sub;
+      i32x4_t dma_rs = {0, 0, 0, 0};
+      int dma_m0 = 0;
+      if (dma_on) {
+        dma_rs = page_rsrc(s_dma);
+        dma_m0 = dma_dst(s_dma);
+        dma_fence();
+      }
+      const lds_u8* tile = tile_of(it);
+      const lds_u8* tile_n = tile_of(it + 1);
+
+      // ---- phase 1: QK(it+1) steps 0..15 (one dependent chain) with the
+      //      softmax of subtile it in the gaps
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { sc[r] = 0.f; sr[r] = 0.f; }
+      bf16x8_t ka[2] = {kfrag(tile_n, 0), kfrag(tile_n, 1)};
+#pragma unroll
+      for (int f = 0; f < kQkA; ++f) {
+        sc = mfma(ka[f & 1], qfrag(f), sc);
+        ka[f & 1] = kfrag(tile_n, f + 2);
+        if (f < 4) sm_max(f);
+        else if (f < 12) sm_exp(2 * (f - 4));
+        if (f == 7) asm volatile("" : "+v"(P[0]));  // keep the conversions in place
+        if (f == 11) asm volatile("" : "+v"(P[1]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sm_commit();
+
+      // ---- phase 2: QK(it+1) steps 16..35 interleaved with the 32 P.V
+      //      steps of subtile it (12 x [QK, PV, PV] + 8 x [QK, PV]); the
+      //      DMA of subtile it+3 rides along
+      bf16x8_t va[2] = {vfrag(tile, 0), vfrag(tile, 1)};
+      int step = 0;
+#pragma unroll
+      for (int f = kQkA; f < 36; ++f) {
+        if (FP8 && f >= 32) sr = mfma(ka[f & 1], qfrag(f), sr); else sc = mfma(ka[f & 1], qfrag(f), sc);
+        if (f + 2 < 36) ka[f & 1] = kfrag(tile_n, f + 2);
+        const int npv = (f - kQkA) < 12 ? 2 : 1;
+#pragma unroll
+        for (int u = 0; u < npv; ++u) {
+          mfma_acc(acc[step & 15], va[step & 1], P[step >> 4]);
+          if (step + 2 < 32) va[step & 1] = vfrag(tile, step + 2);
+          ++step;
         }
+        if (((f - kQkA) & 1) == 0 && (f - kQkA) / 2 < kDma && dma_on) dma_one(dma_rs, dma_m0, s_dma, (f - kQkA) / 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      form_scores(it + 1);
+      sp = sc;
+      sp_sub = it + 1;
+      mask_tail(sp, nvalid_of(it + 1));
+    }
+    if (n_sub > 0) {  // the last subtile: softmax and P.V only
+      const lds_u8* tile = tile_of(n_sub - 1);
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) sm_max(pc);
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) sm_exp(r);
+      sm_commit();
+      bf16x8_t va[2] = {vfrag(tile, 0), vfrag(tile, 1)};
+#pragma unroll
+      for (int step = 0; step < 32; ++step) {
+        mfma_acc(acc[step & 15], va[step & 1], P[step >> 4]);
+        if (step + 2 < 32) va[step & 1] = vfrag(tile, step + 2);
       }
     }
 
-    // ---- finalize this unit
+    // ---- finalize: normalise, stage rows through LDS, store whole rows
     acc_fence(acc);
     const float l_tot = half_swap_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-    const long long orow = ((long long)b * a.s_q + qi) * kHeads + head;
+    const long long orow0 = ((long long)b * a.s_q + qi) * kHeads;  // first output row of this (b, qi)
     const bool final_out = wk.w < 0;
-    const long long prow = (long long)wk.w * R + qi * kHeads + head;
-    // fp32 rows: the partial slot or an fp32 output; bf16 output otherwise
-    const bool bf16_out = final_out && a.out_dtype != 0;
-    float* o32 = final_out ? (float*)a.out + orow * kDc : a.o_part + prow * kDc;
-    uint16_t* o16 = (uint16_t*)a.out + orow * kDc;
-#pragma unroll
-    for (int db = 0; db < 16; ++db) {
-      asm volatile("" : "+a"(acc[db]));  // read one block at a time
-      const f32x16_t t = acc[db];
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int d0 = db * 32 + 8 * qd + 4 * g;
-        const float v0 = t[4 * qd] * inv, v1 = t[4 * qd + 1] * inv;
-        const float v2 = t[4 * qd + 2] * inv, v3 = t[4 * qd + 3] * inv;
-        if (bf16_out) {
-          uint2 pk;
-          pk.x = f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
-          pk.y = f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16);
-          *(uint2*)(o16 + d0) = pk;
-        } else {
-          *(float4*)(o32 + d0) = make_float4(v0, v1, v2, v3);
-        }
-      }
-    }
+    const long long prow0 = (long long)wk.w * R + qi * kHeads;
+    const bool bf16_out = final_out ? a.out_dtype != 0 : a.part_bf16 != 0;
+    float* o32 = final_out ? (float*)a.out + orow0 * kDc : a.o_part + prow0 * kDc;
+    uint16_t* o16 = final_out ? (uint16_t*)a.out + orow0 * kDc : (uint16_t*)a.o_part + prow0 * kDc;
     if (g == 0) {
       if (!final_out)
-        a.lse_part[prow] = lse_v;
+        a.lse_part[prow0 + head] = lse_v;
       else if (a.lse)
-        a.lse[orow] = lse_v;
+        a.lse[orow0 + head] = lse_v;
+    }
+    __syncthreads();  // every wave is done with the tiles
+    typedef __attribute__((address_space(3))) f32x4_t lds_f4;
+    typedef __attribute__((address_space(3))) u32x2_t lds_u2;
+    typedef __attribute__((address_space(3))) u32x4_t lds_u4;
+    if (bf16_out) {
+      // all 128 rows at once in bf16, then 16-byte stores of whole rows
+      lds_u8* rowp = smem + (size_t)(w * 32 + l32) * kOutRowH;
+#pragma unroll
+      for (int db = 0; db < 16; ++db) {
+        asm volatile("" : "+a"(acc[db]));  // one block at a time
+        const f32x16_t t = acc[db];
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          u32x2_t pk;
+          pk[0] = pack_bf16x2(t[4 * qd] * inv, t[4 * qd + 1] * inv);
+          pk[1] = pack_bf16x2(t[4 * qd + 2] * inv, t[4 * qd + 3] * inv);
+          *(lds_u2*)(rowp + (db * 32 + 8 * qd + 4 * g) * 2) = pk;
+        }
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int e = tid; e < kHeads * (kDc / 8); e += 256) {
+        const int r = e / (kDc / 8), c8 = e % (kDc / 8);
+        const u32x4_t v = *(const lds_u4*)(smem + (size_t)r * kOutRowH + c8 * 16);
+        *(u32x4_t*)(o16 + (long long)r * kDc + 8 * c8) = v;
+      }
+      continue;  // the next unit starts with a barrier before touching LDS
+    }
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if ((w >> 1) == pass) {
+        lds_u8* rowp = smem + (size_t)((w & 1) * 32 + l32) * kOutRowF * 4;
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+          asm volatile("" : "+a"(acc[db]));  // one block at a time
+          const f32x16_t t = acc[db];
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            f32x4_t v;
+            v[0] = t[4 * qd] * inv; v[1] = t[4 * qd + 1] * inv; v[2] = t[4 * qd + 2] * inv; v[3] = t[4 * qd + 3] * inv;
+            *(lds_f4*)(rowp + (db * 32 + 8 * qd + 4 * g) * 4) = v;
+          }
+        }
+      }
+      __syncthreads();
+      // 64 staged rows (heads 64*pass ..) x 512 floats: 128 threads per row, 16 B each
+#pragma unroll 4
+      for (int e = tid; e < 64 * (kDc / 4); e += 256) {
+        const int r = e / (kDc / 4), c4 = e % (kDc / 4);
+        const f32x4_t v = *(const lds_f4*)(smem + ((size_t)r * kOutRowF + 4 * c4) * 4);
+        const long long row = 64 * pass + r;
+        *(float4*)(o32 + row * kDc + 4 * c4) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      __syncthreads();
     }
   }
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t s) {
-  if (a.kv_dtype != 2) return launch_decode_bf16(a, grid_x, s);
-  if (a.kv_dtype == 2) return launch_decode_fp8(a, grid_x, s);
+template <bool FP8>
+static hipError_t launch_pipe(const DecodeArgs& a, int grid_x, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_mfma_kernel<true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes(true));
+    hipError_t e = hipFuncSetAttribute((const void*)decode_pipe_kernel<FP8>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kPipeLds(FP8));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(grid_x, a.s_q), dim3(256), kLdsBytes(true), s, a);
+  hipLaunchKernelGGL(decode_pipe_kernel<FP8>, dim3(grid_x, a.s_q), dim3(256), kPipeLds(FP8), s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t s) {
+  return a.kv_dtype == 2 ? launch_pipe<true>(a, grid_x, s) : launch_pipe<false>(a, grid_x, s);
 }
 
 int mfma_max_unit_pages() { return kMaxUnitPages; }

@@ -16,20 +16,15 @@ constexpr int kBlk = 64;                          // tokens per page
 constexpr int kSub = 32;                          // tokens per subtile
 constexpr int kRowB = (kDc + kDr) * 2;            // 1152
 constexpr int kTileB = kSub * kRowB;              // 36864
-constexpr int kStages = 4;
 constexpr int kBf16Dma = kTileB / (4 * 1024);     // 9 DMA instructions per wave per subtile
-// fp8 staging per subtile: codes | k^R | scales
+// fp8 staging per subtile: e4m3 codes | bf16 k^R (the scales go to a ring)
 constexpr int kF8Codes = kSub * kDc;              // 16384
 constexpr int kF8Kr = kSub * kDr * 2;             // 4096
-constexpr int kF8Stage = kF8Codes + kF8Kr + 256;  // 20736 (scales + pad)
 constexpr int kF8Dma = 6;                         // 4 code + 1 k^R + 1 scale instruction per wave
 constexpr float kTau = 8.0f;                      // lazy-rescale threshold (log2 units)
 constexpr int kMaxUnitPages = 512;                // page ids cached in LDS per unit (32768 tokens)
 
 constexpr int kQrStride = kDr * 2 + 16;            // padded bytes per head of the LDS q_rope copy (fp8)
-constexpr int kTabOff(bool fp8) { return fp8 ? kStages * kF8Stage + kTileB : kStages * kTileB; }
-constexpr int kQrOff(bool fp8) { return kTabOff(fp8) + kMaxUnitPages * 4; }
-constexpr int kLdsBytes(bool fp8) { return kQrOff(fp8) + (fp8 ? kHeads * kQrStride : 0); }
 
 // chunk swizzle of token row t (bits 2, 3, 1 of t -> bits 0, 1, 2): chosen by
 // measuring both LDS read patterns of the tile on gfx950
@@ -48,25 +43,13 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base) {
 }
 
 // 16-byte global -> LDS DMA (buffer_load_dwordx4 ... lds): lane l's 16 bytes
-// from rsrc.base + voff land at LDS address m0 + 16*l.  Issued as inline asm so
-// that the compiler does not add its own vmcnt waits in front of later LDS
-// reads; completion is tracked explicitly with wait_vm<>() + a barrier.  The
-// leading s_nop covers the VALU-writes-SGPR -> VMEM-reads-SGPR hazard on the
-// resource, the one after the M0 write the SALU-writes-M0 -> LDS-DMA hazard.
-__device__ __forceinline__ void dma16(i32x4_t rsrc, int voff, lds_u8* l) {
-  const int m0v = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)l);
-  asm volatile(
-      "s_nop 4\n\t"
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v),
-      "v"(voff), "s"(rsrc)
-      : "memory", "m0");
-}
-
-// The same DMA with the LDS address already in an SGPR (computed with scalar
-// arithmetic from a wave-uniform base).  The caller issues dma_fence() once
-// after its resource descriptor was formed and before the first of these.
+// from rsrc.base + voff land at LDS address m0 + 16*l, m0 being computed with
+// scalar arithmetic from a wave-uniform base.  Issued as inline asm so that
+// the compiler does not add its own vmcnt waits in front of later LDS reads;
+// completion is tracked explicitly with wait_vm<>() + a barrier.  The s_nop
+// after the M0 write covers the SALU-writes-M0 -> LDS-DMA hazard; the caller
+// issues dma_fence() once after forming the resource descriptor and before
+// the first of these.
 __device__ __forceinline__ void dma16_m0(i32x4_t rsrc, int voff, int m0v) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
@@ -91,17 +74,6 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-template <int G>
-__device__ __forceinline__ void wait_groups(int outstanding) {
-  static_assert(kStages == 4, "wait table assumes 4 stages");
-  if (outstanding >= 2)
-    wait_vm<2 * G>();
-  else if (outstanding == 1)
-    wait_vm<G>();
-  else
-    wait_vm<0>();
 }
 
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -162,13 +134,5 @@ __device__ __forceinline__ bf16x8_t lds_b128(const lds_u8* p) {
 __device__ __forceinline__ bf16x4_t lds_tr16(const lds_u8* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p);
 }
-
-// two e4m3fn codes (bytes 0,1 or 2,3 of w) -> packed bf16 pair (exact)
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
-  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
-}
-
 
 }  // namespace mla

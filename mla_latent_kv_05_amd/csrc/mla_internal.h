@@ -89,8 +89,6 @@ struct PlanArgs {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_decode_generic(const DecodeArgs& a, int units_max, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t s);
-hipError_t launch_decode_bf16(const DecodeArgs& a, int grid_x, hipStream_t s);
-hipError_t launch_decode_fp8(const DecodeArgs& a, int grid_x, hipStream_t s);
 // expect_splits: the host's estimate of partitions per sequence (only picks
 // between the two merge kernels; both handle any count)
 hipError_t launch_combine_units(const DecodeArgs& a, hipStream_t s, int expect_splits);
