@@ -36,7 +36,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 CSRC = os.path.join(ROOT, "mla_latent_kv_05_amd", "csrc")
 # sources of the bf16-cache attention kernel (the traffic counters are tied to them)
 KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("decode_mfma.hip", "mfma_common.h", "device_util.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_kernel_B64_ctx8192_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_pipe_kernel_bf16_B64_ctx8192_traffic.md")
 
 
 def kernel_hash() -> str:
@@ -228,12 +228,12 @@ def main() -> int:
         achieved = latent_bytes / (kernel_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
-        kname = "decode_bf16_kernel"
+        kname = "decode_pipe_kernel<false>"
     else:
         achieved = flops / (kernel_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_MFMA_PEAK_TFLOPS}
-        kname = "decode_mfma_kernel<true>"
+        kname = "decode_pipe_kernel<true>"
     roof["traffic"] = measured_traffic(args.workload)
     roof["kernel"] = kname
     roof["kernel_ms"] = kernel_ms
