@@ -121,6 +121,9 @@ def main() -> int:
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--copies", type=int, default=4, help="physically distinct cache copies rotated per step")
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic split planning")
+    ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
+                    help="timed steps launched eagerly from Python, or replayed from captured HIP graphs "
+                         "(one per cache copy; on this stack a replay costs more than the eager launches)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -198,16 +201,55 @@ def main() -> int:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    start.record()
+
+    def timed_loop(run_steps, n):
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record()
+        run_steps(n)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / n, time.perf_counter() - t0
+
+    def eager_steps(n):
+        for i in range(n):
+            step(i)
+
+    # one captured HIP graph per cache copy, each holding one whole step
+    # (absorb, decode call, up-projection); replays launch the same kernels
+    # with no host work between them
+    graph_ms = None
+    if args.launch == "graph":
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            eager_steps(len(caches))  # warm the side stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for c in range(len(caches)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+
+        def graph_steps(n):
+            for i in range(n):
+                graphs[i % len(graphs)].replay()
+        graph_ms, t_wall = timed_loop(graph_steps, args.steps)
+    eager_ms, t_eager = timed_loop(eager_steps, args.steps)
+    if graph_ms is None:
+        t_wall = t_eager
+    ms_step = graph_ms if graph_ms is not None else eager_ms
+    # per-call breakdown and the attention kernel's own time (events between
+    # the calls; not part of the timed loops above)
     for i in range(args.steps):
         step(i, timed=True)
-    stop.record()
     torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / args.steps
     absorb_ms = float(np.mean([ev["a"][i].elapsed_time(ev["b"][i]) for i in range(args.steps)]))
     decode_ms = float(np.mean([ev["b"][i].elapsed_time(ev["c"][i]) for i in range(args.steps)]))
     up_ms = float(np.mean([ev["c"][i].elapsed_time(ev["d"][i]) for i in range(args.steps)]))
@@ -249,8 +291,9 @@ def main() -> int:
         "config": {"workload": args.workload, "n_h": n_h, "d_c": d_c, "d_r": d_r, "d_h": d_h, "B": B,
                    "s_q": s_q, "ctx": int(case.seq_lens.max()) if w["lens"][0] == "fixed" else "log-uniform",
                    "page_tokens": case.block_size, "kv_dtype": case.kv_dtype, "splits": args.splits or "auto",
-                   "cache_copies": len(caches)},
+                   "cache_copies": len(caches), "launch": args.launch},
         "decode_tok_s": tok_s, "latent_bytes": latent_bytes,
+        "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
         "roofline_frac_step": value * 1e3 / HBM_PEAK_GBS if case.kv_dtype == "bf16" else None,
         "absorb_ms": absorb_ms, "decode_call_ms": decode_ms, "decode_kernel_ms": kernel_ms, "up_proj_ms": up_ms,
         "decode_call_TBps": latent_bytes / (decode_ms * 1e-3) / 1e12, "wall_s": t_wall,

@@ -261,3 +261,48 @@ def test_absorb_strided_tokens():
     torch.cuda.synchronize()
     ref = oracle.absorb_q(oracle.bf16_to_f64(P["q_c"]), oracle.bf16_to_f64(P["w_uk"]), 128, 128)
     assert_f32_close(out.cpu().numpy().astype(np.float64), ref, "strided")
+
+
+def test_graph_replay_matches_eager():
+    """The whole step (absorb, decode, up-projection) captured in a HIP graph:
+    every replay, with eager work and synchronisations in between, gives the
+    eager results bit for bit (the library issues no memset or allocation)."""
+    say("graph replay")
+    case = inputs.decode_case(61, B=6, seq_lens=np.array([5000, 64, 777, 3001, 129, 2048]), **V3)
+    d = case_to_device(case)
+    B, s_q = case.B, case.s_q
+    P = inputs.projection_weights(62, T_q=B * s_q)
+    qc, wuk, wuv = (bf16_dev(P[k]) for k in ("q_c", "w_uk", "w_uv"))
+    q_lat = torch.empty((B * s_q, 128, 512), dtype=torch.bfloat16, device="cuda")
+    o_lat = torch.empty((B, s_q, 128, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, s_q, 128), dtype=torch.float32, device="cuda")
+    o = torch.empty((B * s_q, 128, 128), dtype=torch.bfloat16, device="cuda")
+    ws = binding.alloc_workspace(B, s_q, 128, 512, d["block_table"].shape[1])
+
+    def step():
+        binding.absorb_q(qc, wuk, out=q_lat)
+        binding.decode(q_lat.view(B, s_q, 128, 512), d["q_rope"], d["kv_cache"], d["block_table"], d["seq_lens"],
+                       d["softmax_scale"], kv_dtype=d["kv_dtype"], d_r=d["d_r"], out=o_lat, lse=lse, workspace=ws)
+        binding.up_proj_v(o_lat.view(B * s_q, 128, 512), wuv, 128, out=o)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (q_lat, o_lat, lse, o)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (q_lat, o_lat, lse, o):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, r in zip((q_lat, o_lat, lse, o), ref):
+            assert torch.equal(t, r), f"replay {rep}"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
