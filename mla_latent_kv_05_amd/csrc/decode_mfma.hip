@@ -331,37 +331,54 @@ void decode_pipe_kernel(DecodeArgs a) {
     };
     float m_new = -INFINITY, ps0 = 0.f, ps1 = 0.f;
     float m8[8];
-    auto sm_max = [&](int piece) {  // pieces 0..3
-      if (piece == 0) {
+    // The softmax of sp is software-pipelined over 11 stages that sit between
+    // the first QK steps of the next subtile: max tree (0..3), lane-half
+    // exchange and the lazy reference (4), then for groups of 4 rows: scaled
+    // shift, exp2, and row sums + bf16 P one stage apart each, so every
+    // dependent VALU op issues at least one MFMA after its producer.
+    auto sm_fma = [&](int q4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sp[4 * q4 + e] = __builtin_fmaf(sp[4 * q4 + e], scale2, -m_new);
+    };
+    auto sm_ex = [&](int q4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sp[4 * q4 + e] = __builtin_amdgcn_exp2f(sp[4 * q4 + e]);
+    };
+    auto sm_cvt = [&](int q4) {  // rows 8*q4 + 4g + 0..3 of the subtile
+      ps0 += sp[4 * q4] + sp[4 * q4 + 2];
+      ps1 += sp[4 * q4 + 1] + sp[4 * q4 + 3];
+      if (FP8) {  // the value rows hold raw codes: their scale goes into P
+        const f32x4_t ts = scales_of(sp_sub, q4);
+        const int t0 = 8 * q4 + 4 * g;  // masked rows may hold any scale
+        const int nv = nvalid_of(sp_sub);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) P[q4 >> 1][(q4 & 1) * 4 + e] = (__bf16)(t0 + e < nv ? sp[4 * q4 + e] * ts[e] : 0.f);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) P[q4 >> 1][(q4 & 1) * 4 + e] = (__bf16)sp[4 * q4 + e];
+      }
+    };
+    auto sm_stage = [&](int st) {  // stages 0..10
+      if (st == 0) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) m8[i] = fmaxf(sp[2 * i], sp[2 * i + 1]);
-      } else if (piece == 1) {
+      } else if (st == 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) m8[i] = fmaxf(m8[i], m8[i + 4]);
-      } else if (piece == 2) {
+      } else if (st == 2) {
         m8[0] = fmaxf(m8[0], m8[2]);
         m8[1] = fmaxf(m8[1], m8[3]);
+      } else if (st == 3) {
         m8[0] = fmaxf(m8[0], m8[1]);
-      } else {
+      } else if (st == 4) {
         const float mx = half_swap_max(m8[0]) * scale2;
         m_new = mx > m_run + kTau ? mx : m_run;  // lazy: keep the reference unless far behind
         ps0 = ps1 = 0.f;
-      }
-    };
-    auto sm_exp = [&](int r) {  // rows r, r+1
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[r], scale2, -m_new));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[r + 1], scale2, -m_new));
-      ps0 += p0;
-      ps1 += p1;
-      if (FP8) {  // the value rows hold raw codes: their scale goes into P
-        const f32x4_t ts = scales_of(sp_sub, r >> 2);
-        const int t0 = 8 * (r >> 2) + 4 * g + (r & 3);  // masked rows may hold any scale
-        const int nv = nvalid_of(sp_sub);
-        P[r >> 3][r & 7] = (__bf16)(t0 < nv ? p0 * ts[r & 3] : 0.f);
-        P[r >> 3][(r & 7) + 1] = (__bf16)(t0 + 1 < nv ? p1 * ts[(r & 3) + 1] : 0.f);
       } else {
-        P[r >> 3][r & 7] = (__bf16)p0;
-        P[r >> 3][(r & 7) + 1] = (__bf16)p1;
+        const int k = st - 5;  // shift of group k, exp2 of group k-1, sums and P of group k-2
+        if (k >= 2) sm_cvt(k - 2);
+        if (k >= 1 && k <= 4) sm_ex(k - 1);
+        if (k <= 3) sm_fma(k);
       }
     };
     // the reference moved (rare): rescale O and the row sum before new P.V
@@ -435,10 +452,9 @@ void decode_pipe_kernel(DecodeArgs a) {
       for (int f = 0; f < kQkA; ++f) {
         sc = mfma(ka[f & 1], qfrag(f), sc);
         ka[f & 1] = kfrag(tile_n, f + 2);
-        if (f < 4) sm_max(f);
-        else if (f < 12) sm_exp(2 * (f - 4));
-        if (f == 7) asm volatile("" : "+v"(P[0]));  // keep the conversions in place
-        if (f == 11) asm volatile("" : "+v"(P[1]));
+        if (f <= 10) sm_stage(f);
+        if (f == 8) asm volatile("" : "+v"(P[0]));  // keep the conversions in place
+        if (f == 10) asm volatile("" : "+v"(P[1]));
         __builtin_amdgcn_sched_barrier(0);
       }
       sm_commit();
@@ -470,9 +486,7 @@ void decode_pipe_kernel(DecodeArgs a) {
     if (n_sub > 0) {  // the last subtile: softmax and P.V only
       const lds_u8* tile = tile_of(n_sub - 1);
 #pragma unroll
-      for (int pc = 0; pc < 4; ++pc) sm_max(pc);
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) sm_exp(r);
+      for (int st = 0; st <= 10; ++st) sm_stage(st);
       sm_commit();
       bf16x8_t va[2] = {vfrag(tile, 0), vfrag(tile, 1)};
 #pragma unroll
