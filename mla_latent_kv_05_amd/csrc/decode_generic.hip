@@ -155,10 +155,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int n = in_lds ? nb[b] : nblocks_of(a, b);
     const int u = units_of(a, n, chunk);
     const int len = (n + u - 1) / u;
+    const int Lb = max(a.seq_lens[b], 0);
     a.seq[b] = make_int2(first, u);
     for (int k = 0; k < u; ++k) {
       const int s0 = k * len, s1 = min(n, s0 + len);
-      a.work[first + k] = make_int4(b, s0, s1, u > 1 ? first + k : -1);
+      // .w: the sequence length, bit-inverted (negative) when it is not split
+      a.work[first + k] = make_int4(b, s0, s1, u > 1 ? Lb : ~Lb);
     }
     first += u;
   }
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
   for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
     const int4 wk = a.work[unit];
     const int b = wk.x;
-    const int L = a.seq_lens[b];
+    const int L = wk.w < 0 ? ~wk.w : wk.w;
     const int vis = L - a.s_q + qi + 1;
     const int t0 = wk.y * a.block_size;
     const int t1 = min(wk.z * a.block_size, vis);
@@ -279,7 +281,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
       }
       if (lane == 0 && a.lse) a.lse[qrow] = lse_v;
     } else {
-      const long long prow = (long long)wk.w * R + r;
+      const long long prow = (long long)unit * R + r;  // partial slot = unit index
 #pragma unroll
       for (int k = 0; k < kMaxC; ++k) {
         int d = lane + 64 * k;

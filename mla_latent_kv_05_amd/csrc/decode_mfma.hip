@@ -110,7 +110,8 @@ void decode_pipe_kernel(DecodeArgs a) {
   for (int unit = xcd_slot(blockIdx.x, gridDim.x); unit < n_units; unit += gridDim.x) {
     const int4 wk = a.work[unit];
     const int b = wk.x;
-    const int L = a.seq_lens[b];
+    const bool final_out = wk.w < 0;           // the sequence is not split
+    const int L = final_out ? ~wk.w : wk.w;    // its length
     const int vis = L - a.s_q + qi + 1;
     const int tok0 = wk.y * kBlk;
     const int tok1 = min(wk.z * kBlk, vis);
@@ -120,13 +121,43 @@ void decode_pipe_kernel(DecodeArgs a) {
     auto nvalid_of = [&](int t) { return t == n_sub - 1 ? n_last : kSub; };
 
     __syncthreads();  // the previous unit is done with LDS
+    // queries, their RoPE part and the unit's page ids in one round trip;
+    // everything is complete before the first DMA is issued, so the
+    // compiler's own vmcnt accounting never waits on a DMA
+    bf16x8_t q[kQReg];
+    lds_u8* qr_lds = smem + kF8QrOff;  // fp8: RoPE query rows, kQrStride bytes per head
     {
+      // uniform row base + 32-bit per-lane offset (scalar base addressing)
+      const long long row0 = ((long long)b * a.s_q + qi) * kHeads;
+      const uint8_t* ql = (const uint8_t*)a.q_lat + row0 * (kDc * 2);
+      const uint8_t* qr = (const uint8_t*)a.q_rope + row0 * (kDr * 2);
+      // recomputed here rather than kept live across the unit loop
+      int hl = threadIdx.x;
+      asm volatile("" : "+v"(hl));
+      const int hd = (hl >> 6) * 32 + (hl & 31), gg = (hl >> 5) & 1;
+      const int ol = hd * (kDc * 2) + gg * 16, orp = hd * (kDr * 2) + gg * 16;
+#pragma unroll
+      for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8_t*)(ql + ol + kb * 32);
+      bf16x8_t qrv[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) qrv[kb] = *(const bf16x8_t*)(qr + orp + kb * 32);
+      static_assert(kMaxUnitPages <= 512, "two page ids per thread");
       const int npg = (n_sub * kSub + kBlk - 1) / kBlk;
       const int32_t* trow = a.table + (long long)b * a.max_blocks + wk.y;
-      for (int i = tid; i < npg; i += 256) tab[i] = trow[i];
+      const int pg0 = tid < npg ? trow[tid] : 0;
+      const int pg1 = tid + 256 < npg ? trow[tid + 256] : 0;
+      wait_vm<0>();
+      if (tid < npg) tab[tid] = pg0;
+      if (tid + 256 < npg) tab[tid + 256] = pg1;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (FP8)
+          *(__attribute__((address_space(3))) bf16x8_t*)(qr_lds + hd * kQrStride + (2 * kb + gg) * 16) = qrv[kb];
+        else
+          q[(32 + kb) % kQReg] = qrv[kb];
+      }
     }
-    wait_vm<0>();
-    __syncthreads();  // page ids visible
+    __syncthreads();  // page ids (and fp8 RoPE queries) visible
     // DMA instruction i (0 .. kDma-1) of subtile s for this wave; the bf16
     // tile lands swizzled, the fp8 staging (codes, k^R, scales) linear
     auto page_rsrc = [&](int s) {
@@ -221,37 +252,6 @@ void decode_pipe_kernel(DecodeArgs a) {
     acc_fence(acc);
     float m_run = -INFINITY, l_run = 0.f;
 
-    // queries first, then the first three subtiles: loads complete in issue
-    // order, so "at most the later subtiles' groups in flight" covers both
-    // the queries and subtile 0 (36 + 27 loads fit the 6-bit vmcnt)
-    bf16x8_t q[kQReg];
-    lds_u8* qr_lds = smem + kF8QrOff;  // fp8: RoPE query rows, kQrStride bytes per head
-    {
-      // uniform row base + 32-bit per-lane offset (scalar base addressing)
-      const long long row0 = ((long long)b * a.s_q + qi) * kHeads;
-      const uint8_t* ql = (const uint8_t*)a.q_lat + row0 * (kDc * 2);
-      const uint8_t* qr = (const uint8_t*)a.q_rope + row0 * (kDr * 2);
-      // recomputed here rather than kept live across the unit loop
-      int hl = threadIdx.x;
-      asm volatile("" : "+v"(hl));
-      const int hd = (hl >> 6) * 32 + (hl & 31), gg = (hl >> 5) & 1;
-      const int ol = hd * (kDc * 2) + gg * 16, orp = hd * (kDr * 2) + gg * 16;
-#pragma unroll
-      for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8_t*)(ql + ol + kb * 32);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8_t v = *(const bf16x8_t*)(qr + orp + kb * 32);
-        if (FP8)
-          *(__attribute__((address_space(3))) bf16x8_t*)(qr_lds + hd * kQrStride + (2 * kb + gg) * 16) = v;
-        else
-          q[(32 + kb) % kQReg] = v;
-      }
-    }
-    // fp8: the q_rope copy to LDS already waits for the query loads; making
-    // that wait explicit on every path keeps the compiler from carrying
-    // them as outstanding into the subtile loop (where its own vmcnt waits
-    // would then also wait for the DMA)
-    if (FP8) wait_vm<0>();
     if (n_sub > 0) {
 #pragma unroll
       for (int s = 0; s <= kAhead; ++s)
@@ -502,8 +502,7 @@ void decode_pipe_kernel(DecodeArgs a) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     const long long orow0 = ((long long)b * a.s_q + qi) * kHeads;  // first output row of this (b, qi)
-    const bool final_out = wk.w < 0;
-    const long long prow0 = (long long)wk.w * R + qi * kHeads;
+    const long long prow0 = (long long)unit * R + qi * kHeads;  // partial slot = unit index
     const bool bf16_out = final_out ? a.out_dtype != 0 : a.part_bf16 != 0;
     float* o32 = final_out ? (float*)a.out + orow0 * kDc : a.o_part + prow0 * kDc;
     uint16_t* o16 = final_out ? (uint16_t*)a.out + orow0 * kDc : (uint16_t*)a.o_part + prow0 * kDc;

@@ -8,7 +8,8 @@ namespace mla {
 // ---------------------------------------------------------------- workspace
 // Layout of the decode workspace (all offsets 256-byte aligned):
 //   [0]           WsHeader
-//   work          int4[units_max]    (b, first_block, end_block, slot)
+//   work          int4[units_max]    (b, first_block, end_block, L or ~L); a split
+//                                    unit's partial rows sit at slot = its index
 //   seq           int2[B]            (first unit, unit count)
 //   lse_part      float[units_max * R]
 //   o_part        float[units_max * R * d_c]  (bf16 rows when the decode kernel
