@@ -49,6 +49,10 @@ content codes, bf16 RoPE key) is a reading: the pages name only an fp8
 content cache beside a bf16 RoPE key, so with respect to the pages it is
 parity unpinned -- it is pinned only by self-consistency (the oracle decodes
 exactly the codes and scales the GPU reads) and by the e4m3fn format facts.
+The cache producer (cache_append) is pinned by an element-by-element
+brute force with complex-number rotation, by torch's own bf16 and fp8
+casts for its encoders, and by appending a toy layer's tokens and decoding
+them to the materialised MHA-mode result.
 """
 
 from __future__ import annotations
@@ -332,3 +336,90 @@ def absorbed_layer(h, W, pos):
         o[b] = up_proj_v(ol, W["w_uv"], n_h, d_h)
     u = o.reshape(B, T, n_h * d_h) @ np.asarray(W["w_o"], dtype=np.float64).T
     return {"u": u, "o": o, "lse": lse, "o_lat": o_lat}
+
+
+# --------------------------------------------------------------------------
+# cache producer: compress, rotate, quantise, scatter into pages
+# --------------------------------------------------------------------------
+
+
+def bf16_round_bits(x) -> np.ndarray:
+    """float64 -> bfloat16 bit patterns, round to nearest, ties to even, done
+    directly on the float64 value (8 significant bits): x = m * 2^e with
+    m in [0.5, 1) keeps round(m * 256) / 256."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    r = np.rint(m * 256.0) / 256.0          # numpy rint: half to even
+    v = np.ldexp(r, e).astype(np.float32)   # exact: 8 significant bits
+    return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def e4m3fn_encode(x) -> np.ndarray:
+    """Nearest OCP e4m3fn code of each value, by comparison against all 254
+    finite codes; a tie goes to the code with the even mantissa; magnitudes
+    beyond 448 saturate to +-448.  Zero encodes as +0."""
+    x = np.asarray(x, dtype=np.float64)
+    codes = np.arange(256, dtype=np.uint8)
+    vals = e4m3fn_to_f64(codes)
+    finite = ~np.isnan(vals)
+    codes, vals = codes[finite], vals[finite]
+    flat = np.clip(x.reshape(-1), -448.0, 448.0)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for i, v in enumerate(flat):
+        d = np.abs(vals - v)
+        best = np.flatnonzero(d == d.min())
+        if len(best) > 1:  # a tie (or +-0): even mantissa, then the positive code
+            even = [k for k in best if codes[k] & 1 == 0]
+            best = even if even else best
+            best = sorted(best, key=lambda k: codes[k] & 0x80)
+        out[i] = codes[best[0]]
+    return out.reshape(x.shape)
+
+
+def quantize_token_e4m3(c_row):
+    """Per-token fp8 content quantisation: scale = amax / 448 as float32 (1.0
+    for an all-zero row), codes = e4m3fn(c / scale).  Returns (codes, scale)."""
+    c_row = np.asarray(c_row, dtype=np.float64)
+    amax = float(np.max(np.abs(c_row)))
+    scale = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+    return e4m3fn_encode(c_row / scale), scale
+
+
+def cache_append(cache, h, w_dkv, w_kr, pos, slot_mapping, kv_dtype, d_c, d_r, block_size,
+                 base: float = 10000.0):
+    """The step before decode: for each new token t, c^KV_t = W^DKV h_t and
+    k^R_t = RoPE(W^KR h_t, pos_t) (the article's "키·값 공동 압축" and "분리
+    RoPE"), stored at physical slot slot_mapping[t] (block = slot // block_size,
+    row = slot % block_size); a negative slot skips the token.
+
+    cache: a copy is returned.  Storage: "f32" rows [d_c + d_r] float32,
+    "bf16" rows of bf16 bit patterns (round to nearest even), "fp8" blocks
+    [block_size x d_c e4m3fn codes | block_size x d_r bf16 | block_size fp32
+    scales] with the content quantised per token (quantize_token_e4m3)."""
+    h = np.asarray(h, dtype=np.float64)
+    c_kv = h @ np.asarray(w_dkv, dtype=np.float64).T
+    k_r = rope(h @ np.asarray(w_kr, dtype=np.float64).T, pos, base)
+    out = np.array(cache, copy=True)
+    for t in range(h.shape[0]):
+        slot = int(slot_mapping[t])
+        if slot < 0:
+            continue
+        blk, row = slot // block_size, slot % block_size
+        if kv_dtype == "f32":
+            out[blk, row, :d_c] = c_kv[t]
+            out[blk, row, d_c:d_c + d_r] = k_r[t]
+        elif kv_dtype == "bf16":
+            out[blk, row, :d_c] = bf16_round_bits(c_kv[t])
+            out[blk, row, d_c:d_c + d_r] = bf16_round_bits(k_r[t])
+        elif kv_dtype == "fp8":
+            raw = out[blk]  # uint8 block
+            codes, scale = quantize_token_e4m3(c_kv[t])
+            raw[row * d_c:(row + 1) * d_c] = codes
+            o1 = block_size * d_c
+            kr_bits = bf16_round_bits(k_r[t]).view(np.uint8)
+            raw[o1 + row * d_r * 2:o1 + (row + 1) * d_r * 2] = kr_bits
+            o2 = o1 + block_size * d_r * 2
+            raw[o2 + 4 * row:o2 + 4 * row + 4] = np.array([scale], dtype=np.float32).view(np.uint8)
+        else:
+            raise ValueError(kv_dtype)
+    return out

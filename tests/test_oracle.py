@@ -344,3 +344,115 @@ def test_fp8_cache_roundtrip_error_bound():
         bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale[:, None]) * (1 + 1e-6)
         assert np.all(err <= bound)
         assert np.array_equal(kr, oracle.bf16_to_f64(inputs.f32_to_bf16_bits(logical[:, 512:])))
+
+
+# ---------------------------------------------------------------- cache producer
+
+def test_bf16_encoder_matches_torch_cast():
+    # float32 inputs (exact in float64): direct float64 rounding equals torch's
+    # float32 -> bfloat16 round-to-nearest-even cast
+    x = np.random.default_rng(3).standard_normal(20000).astype(np.float32)
+    x = np.concatenate([x, np.float32(1.0) + np.float32(2.0 ** -8) * np.arange(-8, 9, dtype=np.float32)])
+    ours = oracle.bf16_round_bits(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_e4m3fn_encoder_nearest_ties_saturation():
+    vals = oracle.e4m3fn_to_f64(np.arange(256, dtype=np.uint8))
+    grid = np.unique(vals[~np.isnan(vals)])
+    rng = np.random.default_rng(4)
+    x = np.concatenate([rng.standard_normal(3000) * 40, grid, (grid[1:] + grid[:-1]) / 2,
+                        [500.0, -1e4, 448.0, -448.0]])
+    codes = oracle.e4m3fn_encode(x)
+    dec = oracle.e4m3fn_to_f64(codes)
+    xc = np.clip(x, -448, 448)
+    # nearest grid value (brute force distance)
+    dist = np.abs(grid[None, :] - xc[:, None]).min(1)
+    assert np.allclose(np.abs(dec - xc), dist, rtol=0, atol=0)
+    # representable values round-trip exactly; ties go to the even mantissa
+    assert np.array_equal(oracle.e4m3fn_to_f64(oracle.e4m3fn_encode(grid)), grid)
+    mid = (grid[1:] + grid[:-1]) / 2
+    mc = oracle.e4m3fn_encode(mid)
+    assert np.all((mc & 1) == 0)
+    # agrees with torch's float32 -> float8_e4m3fn cast (round to nearest even)
+    x32 = np.clip(rng.standard_normal(3000).astype(np.float32) * 50, -448, 448)
+    ref = torch.from_numpy(x32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3fn_encode(x32.astype(np.float64)), ref)
+
+
+def test_cache_append_bruteforce_tiny():
+    """Element-by-element sums and complex-number rotation on a tiny layer."""
+    rng = np.random.default_rng(5)
+    T, d, d_c, d_r, bs = 3, 6, 4, 4, 2
+    h = rng.standard_normal((T, d))
+    wd, wr = rng.standard_normal((d_c, d)), rng.standard_normal((d_r, d))
+    pos = np.array([0, 5, 2])
+    slots = np.array([3, -1, 0])
+    cache = np.full((2, bs, d_c + d_r), 7.0, dtype=np.float32)
+    out = oracle.cache_append(cache, h, wd, wr, pos, slots, "f32", d_c, d_r, bs)
+    for t in range(T):
+        c = [sum(wd[i, k] * h[t, k] for k in range(d)) for i in range(d_c)]
+        r = [sum(wr[i, k] * h[t, k] for k in range(d)) for i in range(d_r)]
+        z = [complex(r[k], r[k + d_r // 2]) * complex(math.cos(pos[t] * 10000.0 ** (-2 * k / d_r)),
+                                                     math.sin(pos[t] * 10000.0 ** (-2 * k / d_r)))
+             for k in range(d_r // 2)]
+        row = np.array(c + [v.real for v in z] + [v.imag for v in z], dtype=np.float32)
+        if slots[t] >= 0:
+            assert np.allclose(out[slots[t] // bs, slots[t] % bs], row, rtol=1e-6, atol=1e-6)
+    # the skipped token and untouched slots keep their contents
+    assert np.all(out[0, 1] == 7.0) and np.all(out[1, 0] == 7.0)
+
+
+def test_cache_append_then_decode_equals_mha_layer():
+    """Append the toy layer's 256 tokens to a paged f32 cache through a
+    permuted slot mapping, then decode the last token in MQA mode: equals the
+    materialised MHA-mode layer output for that token."""
+    W = inputs.toy_layer(seed=11, T=256)
+    dm = W["dims"]
+    n_h, d_h, d_c, d_r = dm["n_h"], dm["d_h"], dm["d_c"], dm["d_r"]
+    h, pos = W["h"][0].astype(np.float64), W["pos"]
+    bs, T = 64, 256
+    perm = np.random.default_rng(12).permutation(T // bs + 2)[: T // bs]  # physical block of logical block j
+    slots = perm[pos // bs] * bs + pos % bs
+    cache = np.zeros((T // bs + 2, bs, d_c + d_r), dtype=np.float32)
+    cache = oracle.cache_append(cache, h, W["w_dkv"], W["w_kr"], pos, slots, "f32", d_c, d_r, bs)
+    c, kr = oracle.paged_rows(cache, perm, T, "f32", d_c, d_r, bs)
+    ref = oracle.mha_mode_layer(W["h"], W, pos)
+    _, _, q_c, q_r = oracle.project(W["h"], W, pos)
+    q_lat = oracle.absorb_q(q_c[0, -1:], W["w_uk"], n_h, d_h)
+    o_lat, lse = oracle.mqa_decode_rows(q_lat, q_r[0, -1:], c, kr, 1.0 / math.sqrt(d_h + d_r))
+    o = oracle.up_proj_v(o_lat, W["w_uv"], n_h, d_h)
+    # the cache holds float32-rounded rows: agreement to float32 precision
+    assert np.max(np.abs(o[0] - ref["o"][0, -1])) <= 1e-5 * np.max(np.abs(ref["o"][0, -1]))
+    assert np.max(np.abs(lse[0] - ref["lse"][0, -1])) <= 1e-5
+
+
+def test_cache_append_fp8_and_bf16_layouts():
+    rng = np.random.default_rng(6)
+    T, d, d_c, d_r, bs = 5, 32, 16, 8, 4
+    h = rng.standard_normal((T, d))
+    wd, wr = rng.standard_normal((d_c, d)) / 5, rng.standard_normal((d_r, d)) / 5
+    pos = np.array([3, 100, 7, 0, 4000])
+    slots = np.array([5, 0, 11, -1, 2])
+    c_ex = h @ wd.T
+    r_ex = oracle.rope(h @ wr.T, pos)
+    bb = bs * (d_c + 2 * d_r + 4)
+    out8 = oracle.cache_append(np.zeros((3, bb), np.uint8), h, wd, wr, pos, slots, "fp8", d_c, d_r, bs)
+    out16 = oracle.cache_append(np.zeros((3, bs, d_c + d_r), np.uint16), h, wd, wr, pos, slots, "bf16",
+                                d_c, d_r, bs)
+    for t in range(T):
+        if slots[t] < 0:
+            continue
+        blk, row = slots[t] // bs, slots[t] % bs
+        c8, kr8 = oracle.paged_rows(out8, [blk], bs, "fp8", d_c, d_r, bs)
+        scale = np.abs(c_ex[t]).max() / 448.0
+        bound = np.maximum(np.abs(c_ex[t]) * 2.0 ** -4, 2.0 ** -10 * scale) * (1 + 1e-6)
+        assert np.all(np.abs(c8[row] - c_ex[t]) <= bound)
+        assert np.max(np.abs(c8[row])) == pytest.approx(np.abs(c_ex[t]).max(), rel=2 ** -4)
+        assert np.all(np.abs(kr8[row] - r_ex[t]) <= np.abs(r_ex[t]) * 2.0 ** -8 + 1e-30)
+        c16, kr16 = oracle.paged_rows(out16, [blk], bs, "bf16", d_c, d_r, bs)
+        assert np.all(np.abs(c16[row] - c_ex[t]) <= np.abs(c_ex[t]) * 2.0 ** -8)
+        assert np.array_equal(kr16[row], kr8[row])
+    # the skipped token's would-be rows stay zero
+    assert not np.any(out8[0][3 * d_c:4 * d_c])
