@@ -186,6 +186,41 @@ int mla_up_proj_v(const void* o_lat, int64_t olat_stride_t, const void* w_uv, vo
                   int64_t o_stride_t, int T_q, int n_h, int d_c, int d_h, int act_dtype,
                   int w_dtype, int out_dtype, void* stream);
 
+/* mla_cache_append -- the cache producer, the step before decode (itwiki
+ * "Multi-head latent attention", sections "Joint KV compression" and
+ * "Decoupled RoPE"): for each new token t
+ *     c^KV_t = W^DKV h_t,   k^R_t = RoPE(W^KR h_t, positions[t])
+ * written into the paged cache at slot slot_mapping[t]: block slot/block_size,
+ * row slot%block_size.  A negative slot skips the token (padding).
+ *
+ *  h            [T, d], token stride h_stride_t (elements), dtype in_dtype
+ *               (MLA_F32 or MLA_BF16)
+ *  w_dkv_kr     [d_c + d_r, d], dtype in_dtype: the d_c rows of W^DKV then
+ *               the d_r rows of W^KR ([out, in])
+ *  positions    [T] int32, the tokens' positions in their sequences
+ *  slot_mapping [T] int32, physical slot or < 0
+ *  kv_cache     the cache mla_decode_absorbed reads, kv_dtype MLA_F32 /
+ *               MLA_BF16 rows [d_c | d_r], or MLA_FP8_E4M3 blocks (needs
+ *               in_dtype MLA_BF16, d_c % 16 == 0, d_r % 8 == 0): the content
+ *               is stored as e4m3fn codes of c / s with s = amax|c| / 448 as
+ *               fp32 (1 for an all-zero row), round to nearest even; k^R bf16.
+ *  rope_base    RoPE base (pairs (x_k, x_{k+d_r/2}) rotated by
+ *               positions[t] * rope_base^(-2k/d_r); angles in fp64)
+ *  workspace    >= mla_cache_append_workspace_bytes(T, d, d_c, d_r) bytes,
+ *               16-byte aligned, caller-owned (fp32 partial sums).
+ * Accumulation is fp32; stored rows round to nearest even.  bf16 inputs with
+ * d % 512 == 0, (d_c + d_r) % 32 == 0 and 16-byte aligned rows take the MFMA
+ * projection, everything else a plain fp32 kernel.  Two tokens mapping to
+ * the same slot race.  T == 0 is a no-op. */
+int mla_cache_append(const void* h, int64_t h_stride_t, const void* w_dkv_kr, const int32_t* positions,
+                     const int32_t* slot_mapping, void* kv_cache, int T, int d, int d_c, int d_r,
+                     int block_size, float rope_base, int in_dtype, int kv_dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* mla_cache_append_workspace_bytes -- workspace size for mla_cache_append
+ * (0 for invalid sizes). */
+size_t mla_cache_append_workspace_bytes(int T, int d, int d_c, int d_r);
+
 /* mla_status_string -- static, human-readable text for a status code. */
 const char* mla_status_string(int status);
 

@@ -38,6 +38,10 @@ _SIGS = {
     "mla_combine_lse": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int,
                                    _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
     "mla_decode_kernel_events": (_c.c_int, [_c.c_void_p, _c.c_void_p]),
+    "mla_cache_append": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                    _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int,
+                                    _c.c_int, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "mla_cache_append_workspace_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int]),
 }
 
 
@@ -190,6 +194,37 @@ def decode_kernel_events(before: torch.cuda.Event, after: torch.cuda.Event) -> N
     if not h0 or not h1:
         raise RuntimeError("record the events once before arming them")
     _check(lib().mla_decode_kernel_events(h0, h1), "mla_decode_kernel_events")
+
+
+def cache_append_workspace(T: int, d: int, d_c: int, d_r: int, device="cuda") -> torch.Tensor:
+    n = lib().mla_cache_append_workspace_bytes(T, d, d_c, d_r)
+    if n == 0:
+        raise RuntimeError("mla_cache_append_workspace_bytes: invalid sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def cache_append(h: torch.Tensor, w_dkv_kr: torch.Tensor, positions: torch.Tensor, slot_mapping: torch.Tensor,
+                 kv_cache: torch.Tensor, d_c: int, d_r: int, block_size: int = 64, kv_dtype: int | None = None,
+                 rope_base: float = 10000.0, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Write c^KV = W^DKV h and k^R = RoPE(W^KR h, pos) of T new tokens into
+    the paged cache (in place).  h [T, d] (token stride h.stride(0));
+    w_dkv_kr [d_c + d_r, d]; positions, slot_mapping [T] int32 (slot < 0
+    skips a token); kv_cache as for decode()."""
+    _gpu(h, w_dkv_kr, positions, slot_mapping, kv_cache)
+    T, d = h.shape
+    assert h.stride(1) == 1 and w_dkv_kr.is_contiguous() and w_dkv_kr.shape == (d_c + d_r, d)
+    assert w_dkv_kr.dtype == h.dtype and kv_cache.is_contiguous()
+    assert positions.dtype == torch.int32 and slot_mapping.dtype == torch.int32
+    assert positions.shape == (T,) and slot_mapping.shape == (T,)
+    assert positions.is_contiguous() and slot_mapping.is_contiguous()
+    if kv_dtype is None:
+        kv_dtype = _dt(kv_cache)
+    if workspace is None:
+        workspace = cache_append_workspace(max(T, 1), d, d_c, d_r, device=h.device)
+    _check(lib().mla_cache_append(_ptr(h), h.stride(0), _ptr(w_dkv_kr), _ptr(positions), _ptr(slot_mapping),
+                                  _ptr(kv_cache), T, d, d_c, d_r, block_size, float(rope_base), _dt(h),
+                                  kv_dtype, _ptr(workspace), workspace.numel(), _stream()), "mla_cache_append")
+    return kv_cache
 
 
 def combine_lse(o_part: torch.Tensor, lse_part: torch.Tensor, splits_per_row: torch.Tensor | None = None,

@@ -114,6 +114,34 @@ int mla_up_proj_v(const void* o_lat, int64_t olat_stride_t, const void* w_uv, vo
                                       act_dtype, w_dtype, out_dtype, mfma, (hipStream_t)stream));
 }
 
+size_t mla_cache_append_workspace_bytes(int T, int d, int d_c, int d_r) {
+  if (T <= 0 || d <= 0 || d_c <= 0 || d_r < 0) return 0;
+  return append_workspace_bytes(T, d, d_c, d_r);
+}
+
+int mla_cache_append(const void* h, int64_t h_stride_t, const void* w_dkv_kr, const int32_t* positions,
+                     const int32_t* slot_mapping, void* kv_cache, int T, int d, int d_c, int d_r, int block_size,
+                     float rope_base, int in_dtype, int kv_dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (T < 0 || d <= 0 || d_c <= 0 || d_r < 0 || d_r % 2 != 0 || block_size <= 0 || !(rope_base > 0.f))
+    return MLA_ERR_INVALID_ARG;
+  if (!act_dtype_ok(in_dtype) || !(kv_dtype == MLA_F32 || kv_dtype == MLA_BF16 || kv_dtype == MLA_FP8_E4M3))
+    return MLA_ERR_INVALID_ARG;
+  if (T == 0) return MLA_OK;
+  if (!h || !w_dkv_kr || !positions || !slot_mapping || !kv_cache) return MLA_ERR_INVALID_ARG;
+  if (h_stride_t < d) return MLA_ERR_INVALID_ARG;
+  if (kv_dtype == MLA_FP8_E4M3 && (in_dtype != MLA_BF16 || d_c % 16 != 0 || d_r % 8 != 0))
+    return MLA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < append_workspace_bytes(T, d, d_c, d_r)) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_MISALIGNED;
+  const long long elem = kv_dtype == MLA_F32 ? 4 : 2;
+  const long long block_bytes = kv_dtype == MLA_FP8_E4M3 ? (long long)block_size * (d_c + 2 * d_r + 4)
+                                                         : (long long)block_size * (d_c + d_r) * elem;
+  return launch_status(launch_append(h, h_stride_t, w_dkv_kr, positions, slot_mapping, kv_cache, T, d, d_c, d_r,
+                                     block_size, block_bytes, rope_base, in_dtype, kv_dtype, (float*)workspace,
+                                     (hipStream_t)stream));
+}
+
 size_t mla_decode_workspace_bytes(int B, int s_q, int n_h, int d_c, int max_blocks_per_seq, int num_splits) {
   if (B <= 0 || s_q <= 0 || n_h <= 0 || d_c <= 0 || max_blocks_per_seq <= 0 || num_splits < 0) return 0;
   const int n_cu = current_cu_count();

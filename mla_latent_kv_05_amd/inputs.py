@@ -291,6 +291,27 @@ def projection_weights(seed: int, T_q: int, n_h: int = 128, d_h: int = 128,
             "dtype": dtype, "T_q": T_q, "n_h": n_h, "d_h": d_h, "d_c": d_c}
 
 
+def append_inputs(seed: int, T: int, d: int = 7168, d_c: int = 512, d_r: int = 64, num_blocks: int = 80,
+                  block_size: int = 64, dtype: str = "bf16", max_pos: int = 32768, skip_every: int = 0) -> dict:
+    """Inputs for the cache producer: hidden states h ~ N(0,1) [T, d]; the
+    stacked weight [W^DKV; W^KR] ~ N(0, 1/d) ([out, in], fan-in d); token
+    positions uniform in [0, max_pos); each token a distinct physical slot
+    (a seeded permutation of the cache's num_blocks*block_size slots), every
+    ``skip_every``-th token marked -1 (padding).  ``dtype`` rounds h and W
+    (bf16 bits or float32)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kind = "f32" if dtype == "bf16" else "f64"
+    h = _draw(rng, (T, d), 1.0, kind)
+    w = _draw(rng, (d_c + d_r, d), 1.0 / math.sqrt(d), kind)
+    pos = rng.integers(0, max_pos, size=T).astype(np.int32)
+    slots = rng.permutation(num_blocks * block_size)[:T].astype(np.int32)
+    if skip_every:
+        slots[::skip_every] = -1
+    conv = f32_to_bf16_bits if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    return {"h": conv(h), "w": conv(w), "pos": pos, "slots": slots, "T": T, "d": d, "d_c": d_c, "d_r": d_r,
+            "num_blocks": num_blocks, "block_size": block_size, "dtype": dtype}
+
+
 # --------------------------------------------------------------------------
 # the five workloads
 # --------------------------------------------------------------------------

@@ -19,7 +19,8 @@ OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE = 0, -1, -2, -3, -4
 def test_header_functions_exported():
     names = binding.header_functions()
     assert set(names) == {"mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_absorbed",
-                          "mla_combine_lse", "mla_up_proj_v", "mla_status_string", "mla_decode_kernel_events"}
+                          "mla_combine_lse", "mla_up_proj_v", "mla_status_string", "mla_decode_kernel_events",
+                          "mla_cache_append", "mla_cache_append_workspace_bytes"}
     L = binding.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -99,3 +100,28 @@ def test_workspace_bytes_invalid():
     L = binding.lib()
     assert L.mla_decode_workspace_bytes(0, 1, 128, 512, 4, 0) == 0
     assert L.mla_decode_workspace_bytes(2, 1, 128, 512, 4, -1) == 0
+
+
+def test_cache_append_argument_validation():
+    L = binding.lib()
+    ws_n = L.mla_cache_append_workspace_bytes(64, 7168, 512, 64)
+    assert ws_n >= 14 * 64 * 576 * 4
+    assert L.mla_cache_append_workspace_bytes(0, 7168, 512, 64) == 0
+    args = dict(h=FAKE, st=7168, w=FAKE, pos=FAKE, slots=FAKE, cache=FAKE, T=64, d=7168, d_c=512, d_r=64, bs=64,
+                base=10000.0, idt=1, kdt=1, ws=FAKE, wsn=ws_n)
+
+    def call(**over):
+        a = dict(args, **over)
+        return L.mla_cache_append(a["h"], a["st"], a["w"], a["pos"], a["slots"], a["cache"], a["T"], a["d"],
+                                  a["d_c"], a["d_r"], a["bs"], a["base"], a["idt"], a["kdt"], a["ws"], a["wsn"], None)
+    assert call(T=0, h=None, w=None) == OK
+    assert call(h=None) == INVALID
+    assert call(st=100) == INVALID
+    assert call(d_r=63) == INVALID
+    assert call(base=0.0) == INVALID
+    assert call(idt=2) == INVALID
+    assert call(kdt=5) == INVALID
+    assert call(kdt=2, idt=0) == UNSUPPORTED
+    assert call(wsn=ws_n - 4) == WORKSPACE
+    assert call(ws=None) == WORKSPACE
+    assert call(ws=FAKE + 4) == MISALIGNED

@@ -306,3 +306,127 @@ def test_graph_replay_matches_eager():
             assert torch.equal(t, r), f"replay {rep}"
         step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ cache producer
+
+def _append_gpu(inp, kv_dtype, cache_np):
+    if inp["dtype"] == "bf16":
+        h, w = bf16_dev(inp["h"]), bf16_dev(inp["w"])
+    else:
+        h, w = f32_dev(inp["h"]), f32_dev(inp["w"])
+    cache = torch.from_numpy(np.ascontiguousarray(cache_np)).cuda()
+    kdt = {"bf16": binding.MLA_BF16, "fp8": binding.MLA_FP8_E4M3, "f32": binding.MLA_F32}[kv_dtype]
+    binding.cache_append(h, w, torch.from_numpy(inp["pos"]).cuda(), torch.from_numpy(inp["slots"]).cuda(), cache,
+                         inp["d_c"], inp["d_r"], inp["block_size"], kv_dtype=kdt)
+    torch.cuda.synchronize()
+    return cache.cpu().numpy()
+
+
+def _append_oracle(inp, kv_dtype, cache_np):
+    dec = oracle.bf16_to_f64 if inp["dtype"] == "bf16" else (lambda a: np.asarray(a, np.float64))
+    h, w = dec(inp["h"]), dec(inp["w"])
+    d_c = inp["d_c"]
+    return oracle.cache_append(cache_np, h, w[:d_c], w[d_c:], inp["pos"], inp["slots"], kv_dtype, d_c, inp["d_r"],
+                               inp["block_size"])
+
+
+def _exact_rows(inp):
+    dec = oracle.bf16_to_f64 if inp["dtype"] == "bf16" else (lambda a: np.asarray(a, np.float64))
+    h, w = dec(inp["h"]), dec(inp["w"])
+    y = h @ w.T
+    d_c = inp["d_c"]
+    return y[:, :d_c], oracle.rope(y[:, d_c:], inp["pos"])
+
+
+@pytest.mark.parametrize("T,skip", [(64, 0), (1, 0), (37, 5), (130, 0)])
+def test_cache_append_bf16_v3(T, skip):
+    say(f"cache append bf16 T={T}")
+    inp = inputs.append_inputs(70 + T, T, skip_every=skip)
+    nb, bs, N = inp["num_blocks"], inp["block_size"], 576
+    poison = np.full((nb, bs, N), 0x7FC1, dtype=np.uint16)  # NaN bits: untouched rows must keep them
+    got = _append_gpu(inp, "bf16", poison)
+    ref = _append_oracle(inp, "bf16", poison)
+    c_ex, r_ex = _exact_rows(inp)
+    written = np.zeros((nb * bs,), dtype=bool)
+    for t in range(T):
+        sl = inp["slots"][t]
+        if sl < 0:
+            continue
+        written[sl] = True
+        row = oracle.bf16_to_f64(got[sl // bs, sl % bs])
+        ex = np.concatenate([c_ex[t], r_ex[t]])
+        # bf16 storage of an fp32 accumulation: within one bf16 step of the exact row
+        assert np.all(np.abs(row - ex) <= np.abs(ex) * 2.0 ** -7 + 1e-6), t
+    flat_got, flat_ref = got.reshape(nb * bs, N), ref.reshape(nb * bs, N)
+    assert np.array_equal(flat_got[~written], flat_ref[~written])          # untouched rows keep their bits
+    same = np.mean(flat_got[written] == flat_ref[written]) if written.any() else 1.0
+    assert same >= 0.97                                                    # rounding ties aside, the oracle's bits
+
+
+@pytest.mark.parametrize("T", [64, 19])
+def test_cache_append_fp8_v3(T):
+    say(f"cache append fp8 T={T}")
+    inp = inputs.append_inputs(90 + T, T, skip_every=7)
+    nb, bs, d_c, d_r = inp["num_blocks"], inp["block_size"], 512, 64
+    bb = bs * (d_c + 2 * d_r + 4)
+    start = np.zeros((nb, bb), dtype=np.uint8)
+    got = _append_gpu(inp, "fp8", start)
+    ref = _append_oracle(inp, "fp8", start)
+    c_ex, r_ex = _exact_rows(inp)
+    n_code_diff = 0
+    for t in range(T):
+        sl = inp["slots"][t]
+        if sl < 0:
+            continue
+        blk, row = sl // bs, sl % bs
+        cg, kg = oracle.paged_rows(got, [blk], bs, "fp8", d_c, d_r, bs)
+        cr, _ = oracle.paged_rows(ref, [blk], bs, "fp8", d_c, d_r, bs)
+        scale = np.abs(c_ex[t]).max() / 448.0
+        # within one e4m3 step of the exact content (the fp32 accumulation may
+        # move a value across a rounding boundary), and the scale to fp32 precision
+        step = np.maximum(np.abs(c_ex[t]) * 2.0 ** -3, 2.0 ** -9 * scale) * (1 + 1e-5)
+        assert np.all(np.abs(cg[row] - c_ex[t]) <= step), t
+        s_got = got[blk, bs * (d_c + 2 * d_r) + 4 * row: bs * (d_c + 2 * d_r) + 4 * row + 4].view(np.float32)[0]
+        assert abs(s_got - scale) <= 1e-5 * scale
+        assert np.all(np.abs(kg[row] - r_ex[t]) <= np.abs(r_ex[t]) * 2.0 ** -7 + 1e-6)
+        n_code_diff += int(np.sum(got[blk, row * d_c:(row + 1) * d_c] != ref[blk, row * d_c:(row + 1) * d_c]))
+    n_written = int(np.sum(inp["slots"] >= 0))
+    assert n_code_diff <= 0.01 * n_written * d_c  # the same codes as the oracle except at rounding ties
+    written_blocks = set(int(s) // bs for s in inp["slots"] if s >= 0)
+    for blk in range(nb):
+        if blk not in written_blocks:
+            assert not got[blk].any()
+
+
+def test_cache_append_toy_fp32_generic_then_decode():
+    """fp32 toy layer (generic projection kernel): append all 256 tokens, then
+    decode the last one on the GPU; equals the oracle's append + decode."""
+    say("cache append toy fp32 + decode")
+    W = inputs.toy_layer(seed=21, T=256)
+    dm = W["dims"]
+    d, d_c, d_r, n_h, d_h = dm["d"], dm["d_c"], dm["d_r"], dm["n_h"], dm["d_h"]
+    T, bs = 256, 64
+    perm = np.random.default_rng(22).permutation(6)[:4].astype(np.int32)
+    pos = np.arange(T, dtype=np.int32)
+    slots = (perm[pos // bs] * bs + pos % bs).astype(np.int32)
+    w = np.concatenate([W["w_dkv"], W["w_kr"]]).astype(np.float32)
+    inp = {"h": W["h"][0], "w": w, "pos": pos, "slots": slots, "d_c": d_c, "d_r": d_r, "block_size": bs,
+           "dtype": "f32"}
+    start = np.zeros((6, bs, d_c + d_r), dtype=np.float32)
+    got = _append_gpu(inp, "f32", start)
+    ref = _append_oracle(inp, "f32", start)
+    assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref))
+    # decode the last token over the GPU-written cache
+    _, _, q_c, q_r = oracle.project(W["h"], W, W["pos"])
+    q_lat = oracle.absorb_q(q_c[0, -1:], W["w_uk"], n_h, d_h)
+    scale = 1.0 / math.sqrt(d_h + d_r)
+    o, lse = binding.decode(f32_dev(q_lat[None].astype(np.float32)), f32_dev(q_r[0, -1:][None].astype(np.float32)),
+                            torch.from_numpy(got).cuda(), torch.from_numpy(perm[None]).cuda(),
+                            torch.tensor([T], dtype=torch.int32).cuda(), scale, d_r=d_r, block_size=bs,
+                            out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    c, kr = oracle.paged_rows(ref, perm, T, "f32", d_c, d_r, bs)
+    o_ref, lse_ref = oracle.mqa_decode_rows(q_lat, q_r[0, -1:], c, kr, scale)
+    assert_f32_close(o.cpu().numpy()[0].astype(np.float64), o_ref, "o_lat", tol=1e-5)
+    assert np.max(np.abs(lse.cpu().numpy()[0] - lse_ref)) <= 1e-5
