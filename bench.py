@@ -113,6 +113,47 @@ def copy_probe(mib: int) -> int:
     return 0
 
 
+def bench_append(case, steps: int, dev) -> dict:
+    """The cache producer for the step's new tokens (T = B * s_q, V3 hidden
+    size 7168): projection through [W^DKV; W^KR], RoPE, storage in the cache's
+    format.  Weight-bound: algorithmic bytes = the stacked weight + the hidden
+    states read once + the rows written."""
+    import torch
+    from mla_latent_kv_05_amd import binding, inputs
+    T, d, d_c, d_r = case.B * case.s_q, 7168, case.d_c, case.d_r
+    inp = inputs.append_inputs(7, T, d=d, d_c=d_c, d_r=d_r, num_blocks=max(2, (T + 63) // 64 + 1))
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    h, w = bf(inp["h"]), bf(inp["w"])
+    pos, slots = torch.from_numpy(inp["pos"]).to(dev), torch.from_numpy(inp["slots"]).to(dev)
+    if case.kv_dtype == "bf16":
+        cache = torch.zeros((inp["num_blocks"], 64, d_c + d_r), dtype=torch.bfloat16, device=dev)
+        kdt, row_b = binding.MLA_BF16, (d_c + d_r) * 2
+    else:
+        cache = torch.zeros((inp["num_blocks"], 64 * (d_c + 2 * d_r + 4)), dtype=torch.uint8, device=dev)
+        kdt, row_b = binding.MLA_FP8_E4M3, d_c + 2 * d_r + 4
+    ws = binding.cache_append_workspace(T, d, d_c, d_r, device=dev)
+
+    def run():
+        binding.cache_append(h, w, pos, slots, cache, d_c, d_r, 64, kv_dtype=kdt, workspace=ws)
+    for _ in range(10):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(20, steps)
+    e0.record()
+    for _ in range(n):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    algo = (d_c + d_r) * d * 2 + T * d * 2 + T * row_b
+    gbs = algo / (us * 1e-6) / 1e9
+    return {"tokens": T, "d": d, "kv_dtype": case.kv_dtype, "us_per_call": us, "algorithmic_bytes": algo,
+            "achieved_GBps": gbs, "bound": "hbm", "peak_GBps": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +167,7 @@ def main() -> int:
                          "(one per cache copy; on this stack a replay costs more than the eager launches)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-append", action="store_true", help="skip the cache-producer measurement")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference kernel "
                          "for scaling HBM traffic counters) and exit")
@@ -299,6 +341,8 @@ def main() -> int:
         "decode_call_TBps": latent_bytes / (decode_ms * 1e-3) / 1e12, "wall_s": t_wall,
         "roofline": roof,
     }
+    if case.kv_dtype in ("bf16", "fp8") and not args.no_append:
+        rec["cache_append"] = bench_append(case, args.steps, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(case, P, args.cpu_seconds)
         rec["cpu_baseline"]["cpu_model"] = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")

@@ -205,7 +205,7 @@ int mla_up_proj_v(const void* o_lat, int64_t olat_stride_t, const void* w_uv, vo
  *               is stored as e4m3fn codes of c / s with s = amax|c| / 448 as
  *               fp32 (1 for an all-zero row), round to nearest even; k^R bf16.
  *  rope_base    RoPE base (pairs (x_k, x_{k+d_r/2}) rotated by
- *               positions[t] * rope_base^(-2k/d_r); angles in fp64)
+ *               positions[t] * rope_base^(-2k/d_r); angles in fp64); d_r <= 128
  *  workspace    >= mla_cache_append_workspace_bytes(T, d, d_c, d_r) bytes,
  *               16-byte aligned, caller-owned (fp32 partial sums).
  * Accumulation is fp32; stored rows round to nearest even.  bf16 inputs with

@@ -125,6 +125,7 @@ int mla_cache_append(const void* h, int64_t h_stride_t, const void* w_dkv_kr, co
                      void* stream) {
   if (T < 0 || d <= 0 || d_c <= 0 || d_r < 0 || d_r % 2 != 0 || block_size <= 0 || !(rope_base > 0.f))
     return MLA_ERR_INVALID_ARG;
+  if (d_r > 2 * kMaxRopePairs) return MLA_ERR_UNSUPPORTED;
   if (!act_dtype_ok(in_dtype) || !(kv_dtype == MLA_F32 || kv_dtype == MLA_BF16 || kv_dtype == MLA_FP8_E4M3))
     return MLA_ERR_INVALID_ARG;
   if (T == 0) return MLA_OK;

@@ -14,6 +14,8 @@
 // writes fp32 partial sums.  The store kernel (one workgroup per token) adds
 // the K partials, rotates the RoPE pairs (angles in fp64), quantises and
 // writes the row.
+#include <cmath>
+
 #include "device_util.h"
 #include "mla_internal.h"
 
@@ -22,46 +24,75 @@ namespace mla {
 constexpr int kApN = 32;    // output columns per workgroup
 constexpr int kApKS = 512;  // K range per workgroup
 constexpr int kApM = 64;    // tokens per workgroup (two 32-row MFMA blocks)
+constexpr int kApRow = kApKS + 8;  // bf16 elements per staged row (16-byte pad: conflict-free b128 reads)
+constexpr size_t kApLds = (size_t)(kApM + kApN) * kApRow * 2;  // 99,840 B
 
 // part[ks][t][n] = sum_{k in range ks} h[t][k] * w[n][k]   (bf16 in, fp32 out)
-// grid (N / 32, d / 512, ceil(T / 64)); wave w: token block w & 1, K half w >> 1
+// grid (N / 32, d / 512, ceil(T / 64)).  The workgroup stages its 64 token
+// rows and 32 weight rows of the K range in LDS with whole-row 16-byte loads
+// (all issued before any store), then wave w multiplies token block w & 1
+// over K half w >> 1 and the two halves meet in LDS.
 __global__ __launch_bounds__(256) void append_gemm_mfma_kernel(const uint16_t* h, long long h_st,
                                                                const uint16_t* w, float* part, int T,
                                                                int d, int N) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t ap_smem[];
+  typedef __attribute__((address_space(3))) uint8_t lds_b;
+  typedef __attribute__((address_space(3))) u32x4_t lds_u4;
+  lds_b* hs = (lds_b*)ap_smem;
+  lds_b* ws = hs + (size_t)kApM * kApRow * 2;
   __shared__ float red[2][32 * 33];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int n0 = blockIdx.x * kApN, ks = blockIdx.y, t0 = blockIdx.z * kApM + (wv & 1) * 32;
-  const int kb = ks * kApKS + (wv >> 1) * (kApKS / 2) + g * 8;
-  const int t = t0 + l32;
-  const bool tok_ok = t < T;
-  const uint16_t* hp = h + (long long)(tok_ok ? t : 0) * h_st + kb;
-  const uint16_t* wp = w + (long long)(n0 + l32) * d + kb;
-  constexpr int kSteps = kApKS / 2 / 16;  // 16 MFMA steps of K = 16
-  bf16x8_t a[kSteps], b[kSteps];
+  const int n0 = blockIdx.x * kApN, k0 = blockIdx.y * kApKS, tb = blockIdx.z * kApM;
+  constexpr int kRowChunks = kApKS / 8;                     // 64 16-byte pieces per row
+  constexpr int kHL = kApM * kRowChunks / 256;              // 16 per thread
+  constexpr int kWL = kApN * kRowChunks / 256;              // 8 per thread
+  u32x4_t hv[kHL], wvv[kWL];
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    a[s] = *(const bf16x8_t*)(hp + 16 * s);
-    b[s] = *(const bf16x8_t*)(wp + 16 * s);
+  for (int j = 0; j < kHL; ++j) {
+    const int c = tid + 256 * j, r = c / kRowChunks, p = c % kRowChunks;
+    hv[j] = u32x4_t{0, 0, 0, 0};
+    if (tb + r < T) hv[j] = *(const u32x4_t*)(h + (long long)(tb + r) * h_st + k0 + 8 * p);
   }
+#pragma unroll
+  for (int j = 0; j < kWL; ++j) {
+    const int c = tid + 256 * j, r = c / kRowChunks, p = c % kRowChunks;
+    wvv[j] = *(const u32x4_t*)(w + (long long)(n0 + r) * d + k0 + 8 * p);
+  }
+#pragma unroll
+  for (int j = 0; j < kHL; ++j) {
+    const int c = tid + 256 * j, r = c / kRowChunks, p = c % kRowChunks;
+    *(lds_u4*)(hs + ((size_t)r * kApRow + 8 * p) * 2) = hv[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kWL; ++j) {
+    const int c = tid + 256 * j, r = c / kRowChunks, p = c % kRowChunks;
+    *(lds_u4*)(ws + ((size_t)r * kApRow + 8 * p) * 2) = wvv[j];
+  }
+  __syncthreads();
+  const int mrow = (wv & 1) * 32 + l32, kh = (wv >> 1) * (kApKS / 2) + 8 * g;
   f32x16_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b[s], acc, 0, 0, 0);
-  // D[i = token][j = column]: lane column l32, rows 8(r/4) + 4g + r%4;
-  // the two K halves meet in LDS
+  for (int st = 0; st < kApKS / 2 / 16; ++st) {
+    const bf16x8_t a = *(const __attribute__((address_space(3))) bf16x8_t*)(hs + ((size_t)mrow * kApRow + kh + 16 * st) * 2);
+    const bf16x8_t b = *(const __attribute__((address_space(3))) bf16x8_t*)(ws + ((size_t)l32 * kApRow + kh + 16 * st) * 2);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+  }
+  // D[i = token][j = column]: lane column l32, rows 8(r/4) + 4g + r%4
   if (wv >= 2) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) red[wv & 1][(8 * (r >> 2) + 4 * g + (r & 3)) * 33 + l32] = acc[r];
   }
   __syncthreads();
   if (wv < 2) {
+    const int t0 = tb + (wv & 1) * 32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 8 * (r >> 2) + 4 * g + (r & 3);
       const int tt = t0 + i;
-      if (tt < T) part[((long long)ks * T + tt) * N + n0 + l32] = acc[r] + red[wv][i * 33 + l32];
+      if (tt < T) part[((long long)blockIdx.y * T + tt) * N + n0 + l32] = acc[r] + red[wv][i * 33 + l32];
     }
   }
 }
@@ -82,11 +113,15 @@ __global__ __launch_bounds__(256) void append_gemm_generic_kernel(const void* h,
 
 // One workgroup per token: y = sum of the K partials; RoPE on the last d_r
 // values (pairs (k, k + d_r/2), angle pos * base^(-2k/d_r) in fp64); store.
+struct RopeFreqs {
+  double f[kMaxRopePairs];  // base^(-2k/d_r), computed on the host in fp64
+};
+
 __global__ __launch_bounds__(256) void append_store_kernel(const float* part, int n_splits,
                                                            const int32_t* positions,
                                                            const int32_t* slots, void* cache, int T,
                                                            int d_c, int d_r, int block_size,
-                                                           long long block_bytes, float rope_base,
+                                                           long long block_bytes, RopeFreqs fr,
                                                            int kv_dtype) {
   extern __shared__ float y[];  // [d_c + d_r]
   __shared__ float wred[4];
@@ -94,16 +129,26 @@ __global__ __launch_bounds__(256) void append_store_kernel(const float* part, in
   const int slot = slots[t];
   if (slot < 0) return;  // uniform: the token is skipped
   const int N = d_c + d_r;
+  // K partials: every load of a column in flight at once (up to kMaxSplits
+  // per round trip)
+  constexpr int kMaxSplits = 16;
   for (int n = tid; n < N; n += 256) {
     float v = 0.f;
-    for (int s = 0; s < n_splits; ++s) v += part[((long long)s * T + t) * N + n];
+    for (int s0 = 0; s0 < n_splits; s0 += kMaxSplits) {
+      float p[kMaxSplits];
+#pragma unroll
+      for (int s = 0; s < kMaxSplits; ++s)
+        p[s] = s0 + s < n_splits ? part[((long long)(s0 + s) * T + t) * N + n] : 0.f;
+#pragma unroll
+      for (int s = 0; s < kMaxSplits; ++s) v += p[s];
+    }
     y[n] = v;
   }
   __syncthreads();
   const int half = d_r / 2;
   const double pos = (double)positions[t];
   for (int k = tid; k < half; k += 256) {
-    const double ang = pos * pow((double)rope_base, -2.0 * k / d_r);
+    const double ang = pos * fr.f[k];
     double sn, cs;
     sincos(ang, &sn, &cs);
     const double x1 = y[d_c + k], x2 = y[d_c + k + half];
@@ -159,9 +204,16 @@ hipError_t launch_append(const void* h, long long h_st, const void* w, const int
   const int N = d_c + d_r;
   int n_splits = 1;
   if (append_mfma_eligible(d, N, in_dtype, h_st, h, w)) {
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void*)append_gemm_mfma_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kApLds);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
     n_splits = d / kApKS;
     dim3 grid(N / kApN, n_splits, (T + kApM - 1) / kApM);
-    hipLaunchKernelGGL(append_gemm_mfma_kernel, grid, dim3(256), 0, s, (const uint16_t*)h, h_st,
+    hipLaunchKernelGGL(append_gemm_mfma_kernel, grid, dim3(256), kApLds, s, (const uint16_t*)h, h_st,
                        (const uint16_t*)w, part, T, d, N);
   } else {
     const long long total = (long long)T * N;
@@ -170,8 +222,10 @@ hipError_t launch_append(const void* h, long long h_st, const void* w, const int
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  RopeFreqs fr{};
+  for (int k = 0; k < d_r / 2; ++k) fr.f[k] = std::pow((double)rope_base, -2.0 * k / d_r);
   hipLaunchKernelGGL(append_store_kernel, dim3(T), dim3(256), (size_t)N * 4, s, part, n_splits, positions,
-                     slots, cache, T, d_c, d_r, block_size, block_bytes, rope_base, kv_dtype);
+                     slots, cache, T, d_c, d_r, block_size, block_bytes, fr, kv_dtype);
   return hipGetLastError();
 }
 
