@@ -148,9 +148,14 @@ __global__ __launch_bounds__(256) void append_store_kernel(const float* part, in
   const int half = d_r / 2;
   const double pos = (double)positions[t];
   for (int k = tid; k < half; k += 256) {
+    // angle reduced to [-pi, pi] by a two-part 2*pi before the fp64 sine and
+    // cosine (positions reach 10^5 radians; the reduction error stays ~1e-11)
+    constexpr double kTwoPiHi = 6.283185307179586, kTwoPiLo = 2.4492935982947064e-16;
     const double ang = pos * fr.f[k];
+    const double q = rint(ang * (1.0 / kTwoPiHi));
+    const double red = fma(-q, kTwoPiLo, fma(-q, kTwoPiHi, ang));
     double sn, cs;
-    sincos(ang, &sn, &cs);
+    sincos(red, &sn, &cs);
     const double x1 = y[d_c + k], x2 = y[d_c + k + half];
     y[d_c + k] = (float)(x1 * cs - x2 * sn);
     y[d_c + k + half] = (float)(x2 * cs + x1 * sn);
