@@ -207,6 +207,36 @@ def project(h, W, pos):
     return c_kv, k_r, q_c, q_r
 
 
+def expand_kv(c_kv, w_uk, w_uv, n_h, d_h):
+    """Materialise the per-head keys and values from the latent (MHA mode):
+    k^C_{t,i} = W^UK_i c^KV_t, v^C_{t,i} = W^UV_i c^KV_t.  c_kv [..., T, d_c];
+    weights [n_h*d_h, d_c] ([out, in]).  Returns k_c, v_c [..., T, n_h, d_h]."""
+    c = np.asarray(c_kv, dtype=np.float64)
+    k_c = (c @ np.asarray(w_uk, dtype=np.float64).T).reshape(*c.shape[:-1], n_h, d_h)
+    v_c = (c @ np.asarray(w_uv, dtype=np.float64).T).reshape(*c.shape[:-1], n_h, d_h)
+    return k_c, v_c
+
+
+def mha_attention(q_c, q_r, k_c, k_r, v_c, scale):
+    """Causal MHA-mode attention of one sequence (prefill): query t sees keys
+    j <= t; head i scores q^C_{t,i}.k^C_{j,i} + q^R_{t,i}.k^R_j (k^R shared by
+    all heads), softmax over j, weighted sum of v^C_{j,i}.
+
+    q_c [T, n_h, d_h], q_r [T, n_h, d_r], k_c [T, n_h, d_h], k_r [T, d_r],
+    v_c [T, n_h, d_v].  Returns o [T, n_h, d_v] and lse [T, n_h]."""
+    q_c, q_r, k_c, k_r, v_c = (np.asarray(a, dtype=np.float64) for a in (q_c, q_r, k_c, k_r, v_c))
+    T, n_h = q_c.shape[:2]
+    causal = np.tril(np.ones((T, T), dtype=bool))  # key j visible to query t iff j <= t
+    o = np.empty((T, n_h, v_c.shape[-1]))
+    lse = np.empty((T, n_h))
+    for i in range(n_h):
+        s = (q_c[:, i] @ k_c[:, i].T + q_r[:, i] @ k_r.T) * scale
+        s = np.where(causal, s, -np.inf)
+        p, lse[:, i] = _softmax_rows(s)
+        o[:, i] = p @ v_c[:, i]
+    return o, lse
+
+
 def mha_mode_layer(h, W, pos):
     """Full layer in MHA mode.
 
@@ -216,20 +246,12 @@ def mha_mode_layer(h, W, pos):
     n_h, d_h, d_r = dm["n_h"], dm["d_h"], dm["d_r"]
     c_kv, k_r, q_c, q_r = project(h, W, pos)
     B, T = c_kv.shape[:2]
-    w_uk = np.asarray(W["w_uk"], dtype=np.float64)
-    w_uv = np.asarray(W["w_uv"], dtype=np.float64)
-    k_c = (c_kv @ w_uk.T).reshape(B, T, n_h, d_h)
-    v_c = (c_kv @ w_uv.T).reshape(B, T, n_h, d_h)
+    k_c, v_c = expand_kv(c_kv, W["w_uk"], W["w_uv"], n_h, d_h)
     scale = 1.0 / math.sqrt(d_h + d_r)
-    causal = np.tril(np.ones((T, T), dtype=bool))  # key j visible to query t iff j <= t
     o = np.empty((B, T, n_h, d_h))
     lse = np.empty((B, T, n_h))
     for b in range(B):
-        for i in range(n_h):
-            s = (q_c[b, :, i] @ k_c[b, :, i].T + q_r[b, :, i] @ k_r[b].T) * scale
-            s = np.where(causal, s, -np.inf)
-            p, lse[b, :, i] = _softmax_rows(s)
-            o[b, :, i] = p @ v_c[b, :, i]
+        o[b], lse[b] = mha_attention(q_c[b], q_r[b], k_c[b], k_r[b], v_c[b], scale)
     u = o.reshape(B, T, n_h * d_h) @ np.asarray(W["w_o"], dtype=np.float64).T
     return {"u": u, "o": o, "lse": lse, "c_kv": c_kv, "k_r": k_r, "q_c": q_c, "q_r": q_r}
 

@@ -456,3 +456,39 @@ def test_cache_append_fp8_and_bf16_layouts():
         assert np.array_equal(kr16[row], kr8[row])
     # the skipped token's would-be rows stay zero
     assert not np.any(out8[0][3 * d_c:4 * d_c])
+
+
+# ---------------------------------------------------------------- MHA-mode prefill pieces
+
+def test_mha_attention_matches_torch_sdpa_causal():
+    """Prefill attention with a RoPE key shared by all heads equals torch's
+    causal attention on the concatenated [k^C; k^R] keys."""
+    rng = np.random.default_rng(13)
+    T, n_h, d_h, d_r = 45, 3, 16, 8
+    q_c, q_r = rng.standard_normal((T, n_h, d_h)), rng.standard_normal((T, n_h, d_r))
+    k_c, k_r, v_c = rng.standard_normal((T, n_h, d_h)), rng.standard_normal((T, d_r)), rng.standard_normal((T, n_h, 12))
+    scale = 0.17
+    o, lse = oracle.mha_attention(q_c, q_r, k_c, k_r, v_c, scale)
+    q = torch.from_numpy(np.concatenate([q_c, q_r], -1)).permute(1, 0, 2)
+    k = torch.from_numpy(np.concatenate([k_c, np.broadcast_to(k_r[:, None], (T, n_h, d_r))], -1)).permute(1, 0, 2)
+    v = torch.from_numpy(v_c).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=scale)
+    assert np.max(np.abs(ref.permute(1, 0, 2).numpy() - o)) <= 1e-13
+    s = (q @ k.transpose(-1, -2)) * scale
+    s = s.masked_fill(~torch.ones(T, T, dtype=torch.bool).tril(), float("-inf"))
+    assert np.max(np.abs(torch.logsumexp(s, -1).permute(1, 0).numpy() - lse)) <= 1e-12
+    # the first query sees only the first key
+    assert np.allclose(o[0], v_c[0], rtol=0, atol=1e-14)
+
+
+def test_expand_kv_per_head_blocks():
+    rng = np.random.default_rng(14)
+    T, n_h, d_h, d_c = 7, 3, 4, 5
+    c = rng.standard_normal((T, d_c))
+    wk, wv = rng.standard_normal((n_h * d_h, d_c)), rng.standard_normal((n_h * d_h, d_c))
+    k_c, v_c = oracle.expand_kv(c, wk, wv, n_h, d_h)
+    for t in range(T):
+        for i in range(n_h):
+            for e in range(d_h):
+                assert abs(k_c[t, i, e] - sum(wk[i * d_h + e, j] * c[t, j] for j in range(d_c))) <= 1e-12
+                assert abs(v_c[t, i, e] - sum(wv[i * d_h + e, j] * c[t, j] for j in range(d_c))) <= 1e-12
