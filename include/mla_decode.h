@@ -221,6 +221,36 @@ int mla_cache_append(const void* h, int64_t h_stride_t, const void* w_dkv_kr, co
  * (0 for invalid sizes). */
 size_t mla_cache_append_workspace_bytes(int T, int d, int d_c, int d_r);
 
+/* mla_expand_kv -- MHA-mode keys and values from the latent (itwiki
+ * "Multi-head latent attention", section "Joint KV compression"), the input
+ * of prefill: k_c[t,i,:] = W^UK_i c_kv[t,:], v_c[t,i,:] = W^UV_i c_kv[t,:].
+ *
+ *  c_kv      [T, d_c], token stride c_stride_t, dtype act_dtype
+ *  w_uk/w_uv [n_h*d_h, d_c] ([out, in]; head i = rows i*d_h ..), dtype w_dtype
+ *  k_c, v_c  [T, n_h, d_h] contiguous, dtype out_dtype
+ *  bf16 inputs take the MFMA up-projection kernel (same limits and
+ *  alignment rules as mla_up_proj_v), other combinations a plain fp32 kernel.
+ *  T == 0 is a no-op. */
+int mla_expand_kv(const void* c_kv, int64_t c_stride_t, const void* w_uk, const void* w_uv, void* k_c,
+                  void* v_c, int T, int n_h, int d_c, int d_h, int act_dtype, int w_dtype, int out_dtype,
+                  void* stream);
+
+/* mla_prefill_mha -- causal MHA-mode attention of one sequence (prefill; the
+ * itwiki article's layer equation with k = [k^C; k^R], k^R shared by the
+ * heads): o[t,i,:] = sum_{j<=t} softmax_j(softmax_scale * (q[t,i,:d_h] .
+ * k_c[j,i,:] + q[t,i,d_h:] . k_r[j,:])) v_c[j,i,:].
+ *
+ *  q    [T, n_h, d_h + d_r] (q^C then q^R per head), contiguous
+ *  k_c  [T, n_h, d_h], k_r [T, d_r], v_c [T, n_h, d_h], contiguous; dtype
+ *       in_dtype (MLA_F32 or MLA_BF16)
+ *  o    [T, n_h, d_h], dtype out_dtype; lse [T, n_h] fp32 (natural log) or NULL
+ *  bf16 with d_h == 128, d_r == 64 and 16-byte aligned buffers takes the MFMA
+ *  kernel (fp32 accumulation, exp2-domain online softmax); everything else
+ *  (d_h + d_r <= 256) a plain fp32 kernel.  T == 0 is a no-op. */
+int mla_prefill_mha(const void* q, const void* k_c, const void* k_r, const void* v_c, void* o, float* lse,
+                    int T, int n_h, int d_h, int d_r, float softmax_scale, int in_dtype, int out_dtype,
+                    void* stream);
+
 /* mla_status_string -- static, human-readable text for a status code. */
 const char* mla_status_string(int status);
 

@@ -42,6 +42,11 @@ _SIGS = {
                                     _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int,
                                     _c.c_int, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "mla_cache_append_workspace_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int]),
+    "mla_expand_kv": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                 _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_void_p]),
+    "mla_prefill_mha": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                   _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int,
+                                   _c.c_void_p]),
 }
 
 
@@ -225,6 +230,40 @@ def cache_append(h: torch.Tensor, w_dkv_kr: torch.Tensor, positions: torch.Tenso
                                   _ptr(kv_cache), T, d, d_c, d_r, block_size, float(rope_base), _dt(h),
                                   kv_dtype, _ptr(workspace), workspace.numel(), _stream()), "mla_cache_append")
     return kv_cache
+
+
+def expand_kv(c_kv: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor, d_h: int,
+              out_dtype: torch.dtype | None = None):
+    """k_c, v_c [T, n_h, d_h] = per-head W^UK / W^UV applied to c_kv [T, d_c]."""
+    _gpu(c_kv, w_uk, w_uv)
+    T, d_c = c_kv.shape
+    n_h = w_uk.shape[0] // d_h
+    assert c_kv.stride(1) == 1 and w_uk.is_contiguous() and w_uv.is_contiguous()
+    assert w_uk.shape == (n_h * d_h, d_c) and w_uv.shape == (n_h * d_h, d_c)
+    odt = c_kv.dtype if out_dtype is None else out_dtype
+    k_c = torch.empty((T, n_h, d_h), dtype=odt, device=c_kv.device)
+    v_c = torch.empty((T, n_h, d_h), dtype=odt, device=c_kv.device)
+    _check(lib().mla_expand_kv(_ptr(c_kv), c_kv.stride(0), _ptr(w_uk), _ptr(w_uv), _ptr(k_c), _ptr(v_c), T, n_h,
+                               d_c, d_h, _dt(c_kv), _dt(w_uk), _dt(k_c), _stream()), "mla_expand_kv")
+    return k_c, v_c
+
+
+def prefill_mha(q: torch.Tensor, k_c: torch.Tensor, k_r: torch.Tensor, v_c: torch.Tensor, softmax_scale: float,
+                out_dtype: torch.dtype | None = None, with_lse: bool = True):
+    """Causal MHA-mode attention: q [T, n_h, d_h+d_r], k_c/v_c [T, n_h, d_h],
+    k_r [T, d_r] (shared by the heads).  Returns (o [T, n_h, d_h], lse [T, n_h])."""
+    _gpu(q, k_c, k_r, v_c)
+    T, n_h, dq = q.shape
+    d_h = k_c.shape[-1]
+    d_r = dq - d_h
+    for t in (q, k_c, k_r, v_c):
+        assert t.is_contiguous() and t.dtype == q.dtype
+    assert k_c.shape == (T, n_h, d_h) and v_c.shape == (T, n_h, d_h) and k_r.shape == (T, d_r)
+    o = torch.empty((T, n_h, d_h), dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
+    lse = torch.empty((T, n_h), dtype=torch.float32, device=q.device) if with_lse else None
+    _check(lib().mla_prefill_mha(_ptr(q), _ptr(k_c), _ptr(k_r), _ptr(v_c), _ptr(o), _ptr(lse), T, n_h, d_h, d_r,
+                                 float(softmax_scale), _dt(q), _dt(o), _stream()), "mla_prefill_mha")
+    return o, lse
 
 
 def combine_lse(o_part: torch.Tensor, lse_part: torch.Tensor, splits_per_row: torch.Tensor | None = None,

@@ -110,8 +110,43 @@ int mla_up_proj_v(const void* o_lat, int64_t olat_stride_t, const void* w_uv, vo
     // outputs are written two adjacent elements at a time
     if (((uintptr_t)o % (out_dtype == MLA_F32 ? 8 : 4)) != 0 || o_stride_t % 2 != 0) return MLA_ERR_MISALIGNED;
   }
-  return launch_status(launch_up_proj(o_lat, olat_stride_t, w_uv, o, o_stride_t, T_q, n_h, d_c, d_h,
+  return launch_status(launch_up_proj(o_lat, olat_stride_t, d_c, w_uv, o, o_stride_t, T_q, n_h, d_c, d_h,
                                       act_dtype, w_dtype, out_dtype, mfma, (hipStream_t)stream));
+}
+
+int mla_expand_kv(const void* c_kv, int64_t c_stride_t, const void* w_uk, const void* w_uv, void* k_c, void* v_c,
+                  int T, int n_h, int d_c, int d_h, int act_dtype, int w_dtype, int out_dtype, void* stream) {
+  if (T < 0 || n_h <= 0 || d_h <= 0 || d_c <= 0) return MLA_ERR_INVALID_ARG;
+  if (!act_dtype_ok(act_dtype) || !act_dtype_ok(w_dtype) || !act_dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
+  if (T == 0) return MLA_OK;
+  if (!c_kv || !w_uk || !w_uv || !k_c || !v_c || c_stride_t < d_c) return MLA_ERR_INVALID_ARG;
+  const bool mfma = act_dtype == MLA_BF16 && w_dtype == MLA_BF16;
+  if (mfma) {
+    if (d_c % 64 != 0 || d_c > 512 || d_h % 32 != 0) return MLA_ERR_UNSUPPORTED;
+    if (!aligned16(c_kv) || !aligned16(w_uk) || !aligned16(w_uv) || c_stride_t % 8 != 0) return MLA_ERR_MISALIGNED;
+    const uintptr_t oa = out_dtype == MLA_F32 ? 8 : 4;
+    if ((uintptr_t)k_c % oa != 0 || (uintptr_t)v_c % oa != 0 || ((int64_t)n_h * d_h) % 2 != 0) return MLA_ERR_MISALIGNED;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const long long o_st = (long long)n_h * d_h;
+  // one latent row per token feeds every head: activation head stride 0
+  hipError_t e = launch_up_proj(c_kv, c_stride_t, 0, w_uk, k_c, o_st, T, n_h, d_c, d_h, act_dtype, w_dtype, out_dtype,
+                                mfma, st);
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  return launch_status(launch_up_proj(c_kv, c_stride_t, 0, w_uv, v_c, o_st, T, n_h, d_c, d_h, act_dtype, w_dtype,
+                                      out_dtype, mfma, st));
+}
+
+int mla_prefill_mha(const void* q, const void* k_c, const void* k_r, const void* v_c, void* o, float* lse, int T,
+                    int n_h, int d_h, int d_r, float softmax_scale, int in_dtype, int out_dtype, void* stream) {
+  if (T < 0 || n_h <= 0 || d_h <= 0 || d_r < 0 || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  if (!act_dtype_ok(in_dtype) || !act_dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
+  if (T == 0) return MLA_OK;
+  if (!q || !k_c || !v_c || !o || (d_r > 0 && !k_r)) return MLA_ERR_INVALID_ARG;
+  if (d_h + d_r > 256 || d_h > 256) return MLA_ERR_UNSUPPORTED;
+  if (in_dtype == MLA_BF16 && d_h == 128 && d_r == 64 && !aligned16(o)) return MLA_ERR_MISALIGNED;
+  return launch_status(launch_prefill(q, k_c, k_r, v_c, o, lse, T, n_h, d_h, d_r, softmax_scale, in_dtype,
+                                      out_dtype, (hipStream_t)stream));
 }
 
 size_t mla_cache_append_workspace_bytes(int T, int d, int d_c, int d_r) {

@@ -99,13 +99,16 @@ hipError_t launch_combine_lse(const float* o_part, const float* lse_part, const 
 hipError_t launch_absorb(const void* q, long long q_st, const void* w, void* out, long long o_st,
                          int T, int n_h, int d_h, int d_c, int act_dt, int w_dt, int out_dt,
                          bool mfma, hipStream_t s);
+hipError_t launch_prefill(const void* q, const void* kc, const void* kr, const void* v, void* out, float* lse,
+                          int T, int n_h, int d_h, int d_r, float scale, int in_dtype, int out_dtype,
+                          hipStream_t s);
 constexpr int kMaxRopePairs = 64;  // d_r <= 128 for the cache producer
 size_t append_workspace_bytes(int T, int d, int d_c, int d_r);
 hipError_t launch_append(const void* h, long long h_st, const void* w, const int32_t* positions,
                          const int32_t* slots, void* cache, int T, int d, int d_c, int d_r, int block_size,
                          long long block_bytes, float rope_base, int in_dtype, int kv_dtype, float* part,
                          hipStream_t s);
-hipError_t launch_up_proj(const void* o_lat, long long a_st, const void* w, void* out,
+hipError_t launch_up_proj(const void* o_lat, long long a_st, long long a_hs, const void* w, void* out,
                           long long o_st, int T, int n_h, int d_c, int d_h, int act_dt,
                           int w_dt, int out_dt, bool mfma, hipStream_t s);
 

@@ -21,7 +21,7 @@ __device__ __forceinline__ f32x16_t mfma16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 // out[t, h, n] = sum_k A[t, h, k] * W(h, k, n); absorb: W(h,k,n) = w[(h*d_h+k)*d_c + n]
 // (K = d_h, N = d_c); up-proj: W(h,k,n) = w[(h*d_h+n)*d_c + k] (K = d_c, N = d_h).
 template <bool UP>
-__global__ __launch_bounds__(256) void proj_generic_kernel(const void* A, long long a_st, const void* w,
+__global__ __launch_bounds__(256) void proj_generic_kernel(const void* A, long long a_st, long long a_hs, const void* w,
                                                            void* out, long long o_st, int T, int n_h,
                                                            int K, int N, int d_h, int d_c, int act_dt,
                                                            int w_dt, int out_dt) {
@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(const void* A, long l
   const int h = (int)((idx / N) % n_h);
   const int t = (int)(idx / ((long long)N * n_h));
   float acc = 0.f;
-  const long long arow = t * a_st + (long long)h * K;
+  const long long arow = t * a_st + (long long)h * a_hs;
   for (int k = 0; k < K; ++k) {
     const long long wi = UP ? ((long long)(h * d_h + n) * d_c + k) : ((long long)(h * d_h + k) * d_c + n);
     acc += load_elem(A, arow + k, act_dt) * load_elem(w, wi, w_dt);
@@ -176,7 +176,7 @@ constexpr int kUpMaxCb = 8;      // d_c / 64 (16-wide k-steps per wave) up to d_
 constexpr int kUpAStride = 520;  // bf16 elements per staged activation row
 
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void up_mfma_kernel(const uint16_t* a, long long a_st, const uint16_t* w,
+__global__ __launch_bounds__(256) void up_mfma_kernel(const uint16_t* a, long long a_st, long long a_hs, const uint16_t* w,
                                                       void* out, long long o_st, int T, int n_h, int d_c,
                                                       int d_h) {
   __shared__ float red[4][32 * 33];
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void up_mfma_kernel(const uint16_t* a, long lo
     for (int j = 0; j < 8; ++j) {
       const int e = j * 256 + tid, row = e / apc, pc = e % apc;
       av[j] = u32x4_t{0, 0, 0, 0};
-      if (row < 32 && t0 + row < T) av[j] = *(const u32x4_t*)(a + (long long)(t0 + row) * a_st + (long long)h * d_c + pc * 8);
+      if (row < 32 && t0 + row < T) av[j] = *(const u32x4_t*)(a + (long long)(t0 + row) * a_st + (long long)h * a_hs + pc * 8);
     }
   };
   auto store_a = [&]() {
@@ -263,25 +263,28 @@ hipError_t launch_absorb(const void* q, long long q_st, const void* w, void* out
   } else {
     const long long total = (long long)T * n_h * d_c;
     hipLaunchKernelGGL(proj_generic_kernel<false>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                       q, q_st, w, out, o_st, T, n_h, d_h, d_c, d_h, d_c, act_dt, w_dt, out_dt);
+                       q, q_st, (long long)d_h, w, out, o_st, T, n_h, d_h, d_c, d_h, d_c, act_dt, w_dt, out_dt);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_up_proj(const void* o_lat, long long a_st, const void* w, void* out, long long o_st,
-                          int T, int n_h, int d_c, int d_h, int act_dt, int w_dt, int out_dt, bool mfma,
-                          hipStream_t s) {
+// a_hs: element distance between the heads' activation rows of one token
+// (d_c for the up-projection; 0 when one latent row feeds every head, as in
+// the MHA-mode key/value expansion)
+hipError_t launch_up_proj(const void* o_lat, long long a_st, long long a_hs, const void* w, void* out,
+                          long long o_st, int T, int n_h, int d_c, int d_h, int act_dt, int w_dt, int out_dt,
+                          bool mfma, hipStream_t s) {
   if (mfma) {
     if (out_dt == 1)
       hipLaunchKernelGGL(up_mfma_kernel<true>, dim3(d_h / 32, n_h), dim3(256), 0, s, (const uint16_t*)o_lat, a_st,
-                         (const uint16_t*)w, out, o_st, T, n_h, d_c, d_h);
+                         a_hs, (const uint16_t*)w, out, o_st, T, n_h, d_c, d_h);
     else
       hipLaunchKernelGGL(up_mfma_kernel<false>, dim3(d_h / 32, n_h), dim3(256), 0, s, (const uint16_t*)o_lat,
-                         a_st, (const uint16_t*)w, out, o_st, T, n_h, d_c, d_h);
+                         a_st, a_hs, (const uint16_t*)w, out, o_st, T, n_h, d_c, d_h);
   } else {
     const long long total = (long long)T * n_h * d_h;
     hipLaunchKernelGGL(proj_generic_kernel<true>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                       o_lat, a_st, w, out, o_st, T, n_h, d_c, d_h, d_h, d_c, act_dt, w_dt, out_dt);
+                       o_lat, a_st, a_hs, w, out, o_st, T, n_h, d_c, d_h, d_h, d_c, act_dt, w_dt, out_dt);
   }
   return hipGetLastError();
 }

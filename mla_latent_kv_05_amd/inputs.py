@@ -312,6 +312,31 @@ def append_inputs(seed: int, T: int, d: int = 7168, d_c: int = 512, d_r: int = 6
             "num_blocks": num_blocks, "block_size": block_size, "dtype": dtype}
 
 
+def prefill_inputs(seed: int, T: int, n_h: int = 128, d_h: int = 128, d_r: int = 64, d_c: int = 512,
+                   dtype: str = "bf16") -> dict:
+    """Inputs of MHA-mode prefill at V3 head shapes, one sequence of T tokens.
+
+    Latent c^KV ~ N(0,1) [T, d_c] (it leaves an RMSNorm) with W^UK, W^UV ~
+    N(0, 1/d_c) [n_h*d_h, d_c] ([out, in], fan-in d_c), so the expanded keys
+    and values have unit variance; the attention inputs themselves are drawn
+    independently: q = [q^C | q^R] ~ N(0,1) [T, n_h, d_h+d_r], k^C, v^C ~
+    N(0,1) [T, n_h, d_h], k^R ~ N(0,1) [T, d_r] (RoPE keeps norms).  With
+    scale 1/sqrt(d_h+d_r) the scores have unit variance."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kind = "f32" if dtype == "bf16" else "f64"
+    out = {"c_kv": _draw(rng, (T, d_c), 1.0, kind),
+           "w_uk": _draw(rng, (n_h * d_h, d_c), 1.0 / math.sqrt(d_c), kind),
+           "w_uv": _draw(rng, (n_h * d_h, d_c), 1.0 / math.sqrt(d_c), kind),
+           "q": _draw(rng, (T, n_h, d_h + d_r), 1.0, kind),
+           "k_c": _draw(rng, (T, n_h, d_h), 1.0, kind),
+           "v_c": _draw(rng, (T, n_h, d_h), 1.0, kind),
+           "k_r": _draw(rng, (T, d_r), 1.0, kind)}
+    conv = f32_to_bf16_bits if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    out = {k: conv(v) for k, v in out.items()}
+    out.update(T=T, n_h=n_h, d_h=d_h, d_r=d_r, d_c=d_c, dtype=dtype, scale=1.0 / math.sqrt(d_h + d_r))
+    return out
+
+
 # --------------------------------------------------------------------------
 # the five workloads
 # --------------------------------------------------------------------------

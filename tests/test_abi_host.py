@@ -20,7 +20,8 @@ def test_header_functions_exported():
     names = binding.header_functions()
     assert set(names) == {"mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_absorbed",
                           "mla_combine_lse", "mla_up_proj_v", "mla_status_string", "mla_decode_kernel_events",
-                          "mla_cache_append", "mla_cache_append_workspace_bytes"}
+                          "mla_cache_append", "mla_cache_append_workspace_bytes", "mla_expand_kv",
+                          "mla_prefill_mha"}
     L = binding.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -125,3 +126,17 @@ def test_cache_append_argument_validation():
     assert call(wsn=ws_n - 4) == WORKSPACE
     assert call(ws=None) == WORKSPACE
     assert call(ws=FAKE + 4) == MISALIGNED
+
+
+def test_prefill_and_expand_argument_validation():
+    L = binding.lib()
+    assert L.mla_prefill_mha(None, None, None, None, None, None, 0, 128, 128, 64, 0.07, 1, 1, None) == OK
+    assert L.mla_prefill_mha(FAKE, FAKE, FAKE, FAKE, None, None, 8, 128, 128, 64, 0.07, 1, 1, None) == INVALID
+    assert L.mla_prefill_mha(FAKE, FAKE, FAKE, FAKE, FAKE, None, 8, 128, 128, 64, 0.0, 1, 1, None) == INVALID
+    assert L.mla_prefill_mha(FAKE, FAKE, None, FAKE, FAKE, None, 8, 128, 128, 64, 0.07, 1, 1, None) == INVALID
+    assert L.mla_prefill_mha(FAKE, FAKE, FAKE, FAKE, FAKE, None, 8, 128, 256, 64, 0.07, 1, 1, None) == UNSUPPORTED
+    assert L.mla_prefill_mha(FAKE, FAKE, FAKE, FAKE, FAKE + 4, None, 8, 128, 128, 64, 0.07, 1, 1, None) == MISALIGNED
+    assert L.mla_expand_kv(None, 0, None, None, None, None, 0, 128, 512, 128, 1, 1, 1, None) == OK
+    assert L.mla_expand_kv(FAKE, 100, FAKE, FAKE, FAKE, FAKE, 4, 128, 512, 128, 1, 1, 1, None) == INVALID
+    assert L.mla_expand_kv(FAKE, 512, FAKE, FAKE, FAKE, FAKE, 4, 128, 512, 100, 1, 1, 1, None) == UNSUPPORTED
+    assert L.mla_expand_kv(FAKE + 2, 512, FAKE, FAKE, FAKE, FAKE, 4, 128, 512, 128, 1, 1, 1, None) == MISALIGNED

@@ -430,3 +430,126 @@ def test_cache_append_toy_fp32_generic_then_decode():
     o_ref, lse_ref = oracle.mqa_decode_rows(q_lat, q_r[0, -1:], c, kr, scale)
     assert_f32_close(o.cpu().numpy()[0].astype(np.float64), o_ref, "o_lat", tol=1e-5)
     assert np.max(np.abs(lse.cpu().numpy()[0] - lse_ref)) <= 1e-5
+
+
+# ------------------------------------------------------------------ MHA-mode prefill
+
+def _pf_dev(inp, *keys):
+    conv = bf16_dev if inp["dtype"] == "bf16" else f32_dev
+    return [conv(inp[k]) for k in keys]
+
+
+def _pf_dec(inp, *keys):
+    dec = oracle.bf16_to_f64 if inp["dtype"] == "bf16" else (lambda a: np.asarray(a, np.float64))
+    return [dec(inp[k]) for k in keys]
+
+
+def _pf_oracle(inp, heads=None):
+    q, k_c, v_c, k_r = _pf_dec(inp, "q", "k_c", "v_c", "k_r")
+    if heads is not None:
+        q, k_c, v_c = q[:, heads], k_c[:, heads], v_c[:, heads]
+    d_h = inp["d_h"]
+    return oracle.mha_attention(q[..., :d_h], q[..., d_h:], k_c, k_r, v_c, inp["scale"])
+
+
+@pytest.mark.parametrize("T", [1, 37, 128, 300])
+def test_prefill_mha_bf16_v3(T):
+    """MFMA kernel (d_h 128, d_r 64, 128 heads) against the oracle: one query
+    block, ragged tails, several causal subtiles."""
+    say(f"prefill bf16 T={T}")
+    inp = inputs.prefill_inputs(110 + T, T)
+    q, k_c, k_r, v_c = _pf_dev(inp, "q", "k_c", "k_r", "v_c")
+    o, lse = binding.prefill_mha(q, k_c, k_r, v_c, inp["scale"], out_dtype=torch.float32)
+    o16, _ = binding.prefill_mha(q, k_c, k_r, v_c, inp["scale"], with_lse=False)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = _pf_oracle(inp)
+    g = o.cpu().numpy().astype(np.float64)
+    assert_bf16_close(g, ref_o, f"prefill T={T}")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64), ref_lse, "prefill lse")
+    # bf16 output: the fp32 result rounded once more
+    assert_bf16_close(o16.float().cpu().numpy().astype(np.float64), ref_o, "prefill bf16 out")
+    if T == 1:  # one visible key: the output is that key's value row exactly (p = 1)
+        assert np.array_equal(g[0], oracle.bf16_to_f64(inp["v_c"])[0])
+
+
+def test_prefill_mha_full_size_sampled_heads():
+    """4096-token prefill at V3 heads; the oracle checks every query of 3 heads
+    (first, middle, last) and the rest is checked to be finite."""
+    T = 4096
+    say(f"prefill bf16 T={T} sampled heads")
+    inp = inputs.prefill_inputs(131, T)
+    q, k_c, k_r, v_c = _pf_dev(inp, "q", "k_c", "k_r", "v_c")
+    o, lse = binding.prefill_mha(q, k_c, k_r, v_c, inp["scale"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    heads = [0, 77, 127]
+    g = o.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(g))
+    ref_o, ref_lse = _pf_oracle(inp, heads)
+    assert_bf16_close(g[:, heads], ref_o, "prefill 4096 sampled")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64)[:, heads], ref_lse, "prefill 4096 lse")
+
+
+@pytest.mark.parametrize("T,n_h,d_h,d_r", [(1, 2, 64, 32), (50, 3, 64, 32), (70, 2, 128, 64), (33, 1, 192, 64)])
+def test_prefill_mha_fp32_generic(T, n_h, d_h, d_r):
+    """fp32 inputs (portable kernel) at toy and odd head sizes."""
+    say(f"prefill fp32 T={T} n_h={n_h} d_h={d_h} d_r={d_r}")
+    inp = inputs.prefill_inputs(150 + T, T, n_h=n_h, d_h=d_h, d_r=d_r, d_c=64, dtype="f32")
+    q, k_c, k_r, v_c = _pf_dev(inp, "q", "k_c", "k_r", "v_c")
+    o, lse = binding.prefill_mha(q, k_c, k_r, v_c, inp["scale"])
+    torch.cuda.synchronize()
+    ref_o, ref_lse = _pf_oracle(inp)
+    assert_f32_close(o.cpu().numpy().astype(np.float64), ref_o, "prefill fp32", tol=1e-5)
+    assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= 1e-5
+
+
+def test_prefill_mfma_matches_generic_on_bf16():
+    """Same bf16 inputs through both kernels (the portable one takes a
+    misaligned view of the same values)."""
+    T = 200
+    say("prefill mfma vs generic")
+    inp = inputs.prefill_inputs(171, T)
+    q, k_c, k_r, v_c = _pf_dev(inp, "q", "k_c", "k_r", "v_c")
+    o1, l1 = binding.prefill_mha(q, k_c, k_r, v_c, inp["scale"], out_dtype=torch.float32)
+    # shift k_r by one element inside a larger buffer: no longer 16-byte aligned
+    buf = torch.empty(k_r.numel() + 1, dtype=k_r.dtype, device=k_r.device)
+    buf[1:] = k_r.reshape(-1)
+    k_r_mis = buf[1:].view(k_r.shape)
+    o2, l2 = binding.prefill_mha(q, k_c, k_r_mis, v_c, inp["scale"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    a, b = o1.cpu().numpy().astype(np.float64), o2.cpu().numpy().astype(np.float64)
+    assert_bf16_close(a, b, "mfma vs generic")
+    assert np.max(np.abs(l1.cpu().numpy() - l2.cpu().numpy())) <= 1e-3
+
+
+@pytest.mark.parametrize("T", [1, 45, 300])
+def test_expand_kv_bf16_v3(T):
+    say(f"expand_kv bf16 T={T}")
+    inp = inputs.prefill_inputs(190 + T, T)
+    c_kv, w_uk, w_uv = _pf_dev(inp, "c_kv", "w_uk", "w_uv")
+    k_c, v_c = binding.expand_kv(c_kv, w_uk, w_uv, 128, out_dtype=torch.float32)
+    k16, v16 = binding.expand_kv(c_kv, w_uk, w_uv, 128)
+    torch.cuda.synchronize()
+    rk, rv = oracle.expand_kv(*_pf_dec(inp, "c_kv", "w_uk", "w_uv"), 128, 128)
+    # bf16 inputs, fp32 accumulation over d_c = 512 terms
+    assert_f32_close(k_c.cpu().numpy().astype(np.float64), rk, "k_c", tol=1e-5)
+    assert_f32_close(v_c.cpu().numpy().astype(np.float64), rv, "v_c", tol=1e-5)
+    assert_bf16_close(k16.float().cpu().numpy().astype(np.float64), rk, "k_c bf16")
+    assert_bf16_close(v16.float().cpu().numpy().astype(np.float64), rv, "v_c bf16")
+
+
+def test_expand_then_prefill_toy_fp32_layer():
+    """fp32 toy layer in MHA mode, every step on the GPU: latent -> expand_kv ->
+    prefill, against the oracle's MHA-mode layer output o (before W^O)."""
+    say("toy fp32 expand + prefill")
+    W = inputs.toy_layer(seed=5, B=1, T=256)
+    dm = W["dims"]
+    n_h, d_h, d_r = dm["n_h"], dm["d_h"], dm["d_r"]
+    ref = oracle.mha_mode_layer(W["h"], W, W["pos"])
+    c_kv = f32_dev(ref["c_kv"][0])
+    k_c, v_c = binding.expand_kv(c_kv, f32_dev(W["w_uk"]), f32_dev(W["w_uv"]), d_h)
+    q = f32_dev(np.concatenate([ref["q_c"][0], ref["q_r"][0]], -1))
+    o, lse = binding.prefill_mha(q, k_c, v_c=v_c, k_r=f32_dev(ref["k_r"][0]),
+                                 softmax_scale=1.0 / math.sqrt(d_h + d_r))
+    torch.cuda.synchronize()
+    assert_f32_close(o.cpu().numpy().astype(np.float64), ref["o"][0], "toy layer o", tol=1e-5)
+    assert np.max(np.abs(lse.cpu().numpy() - ref["lse"][0])) <= 1e-5
