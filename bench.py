@@ -154,6 +154,57 @@ def bench_append(case, steps: int, dev) -> dict:
             "achieved_GBps": gbs, "bound": "hbm", "peak_GBps": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS}
 
 
+PREFILL_T = 4096
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(steps: int, dev, T: int = PREFILL_T) -> dict:
+    """MHA-mode prefill of one T-token sequence at V3 heads (128 heads, d_h 128,
+    d_r 64, d_c 512, bf16): the key/value expansion from the latent and the
+    causal attention.  MFMA-bound: algorithmic flops of the attention =
+    2 * (d_h + d_r + d_h) * n_h * T(T+1)/2 (QK^T and PV over the causal
+    triangle); of the expansion 2 * 2 * T * d_c * n_h * d_h."""
+    import torch
+    from mla_latent_kv_05_amd import binding
+    n_h, d_h, d_r, d_c = 128, 128, 64, 512
+    g = torch.Generator(device=dev)
+    g.manual_seed(17)
+
+    def rn(*shape, std=1.0):
+        return (torch.randn(*shape, generator=g, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
+    c_kv = rn(T, d_c)
+    w_uk, w_uv = rn(n_h * d_h, d_c, std=d_c ** -0.5), rn(n_h * d_h, d_c, std=d_c ** -0.5)
+    q, k_r = rn(T, n_h, d_h + d_r), rn(T, d_r)
+    scale = (d_h + d_r) ** -0.5
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+    k_c, v_c = binding.expand_kv(c_kv, w_uk, w_uv, d_h)
+    n = max(10, min(steps, 50))
+    us_exp = timed(lambda: binding.expand_kv(c_kv, w_uk, w_uv, d_h), n)
+    us_att = timed(lambda: binding.prefill_mha(q, k_c, k_r, v_c, scale), n)
+    fl_att = 2.0 * (d_h + d_r + d_h) * n_h * T * (T + 1) / 2
+    fl_exp = 2.0 * 2 * T * d_c * n_h * d_h
+    tf_att = fl_att / (us_att * 1e-6) / 1e12
+    tf_exp = fl_exp / (us_exp * 1e-6) / 1e12
+    return {"tokens": T, "n_h": n_h, "d_qk": d_h + d_r, "d_v": d_h, "dtype": "bf16",
+            "attention": {"us_per_call": us_att, "algorithmic_flops": fl_att, "achieved_TFLOPs": tf_att,
+                          "bound": "mfma", "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                          "frac": tf_att / MFMA_BF16_PEAK_TFLOPS},
+            "expand_kv": {"us_per_call": us_exp, "algorithmic_flops": fl_exp, "achieved_TFLOPs": tf_exp,
+                          "bound": "mfma", "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                          "frac": tf_exp / MFMA_BF16_PEAK_TFLOPS}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +219,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the cache-producer measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the MHA-mode prefill measurement")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference kernel "
                          "for scaling HBM traffic counters) and exit")
@@ -343,6 +395,8 @@ def main() -> int:
     }
     if case.kv_dtype in ("bf16", "fp8") and not args.no_append:
         rec["cache_append"] = bench_append(case, args.steps, dev)
+    if not args.no_prefill:
+        rec["prefill_mha"] = bench_prefill(args.steps, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(case, P, args.cpu_seconds)
         rec["cpu_baseline"]["cpu_model"] = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")

@@ -7,57 +7,64 @@
 // up-projection kernel with one latent row per token feeding every head).
 //
 // MFMA kernel (bf16, d_h = 128, d_r = 64): a workgroup of 4 waves takes one
-// head and 128 query rows, wave w rows 32w .. 32w+31.  Keys stream through
-// LDS in 32-key subtiles (k^C | k^R rows of 192 values, v^C rows of 128),
-// double-buffered: the next subtile's global loads are in flight while the
-// current one is used.  Per subtile and wave:
+// head and 128 query rows, wave w rows 32w .. 32w+31.  Keys stream through a
+// 3-stage LDS ring in 32-key subtiles (content keys, RoPE keys and values in
+// three swizzled regions), filled by 16-byte global->LDS DMA two subtiles
+// ahead; one barrier per subtile.  Per subtile and wave:
 //   S^T[key, query] = K[key, 0:192] . Q^T  (12 v_mfma_f32_32x32x16_bf16; A =
 //                     key rows by ds_read_b128, B = the queries in registers)
-//   online softmax per query (the lane is the query; exp2 domain, exact
-//                     rescale), causal mask on the diagonal subtile
+//   online softmax per query (the lane is the query; exp2 domain, lazy
+//                     reference max), causal mask only where the subtile
+//                     reaches the wave's diagonal or the end of the sequence
 //   O^T[dim, query] += V^T[dim, key] . P^T[key, query]  (8 MFMAs; A = value
 //                     columns by ds_read_b64_tr_b16, B = P from the S layout)
-#include "device_util.h"
-#include "mla_internal.h"
+// Workgroups are dealt to the 8 XCDs so that all query blocks of a head run
+// on one XCD (its L2 keeps that head's keys and values), longest first.
+#include "mfma_common.h"
 
 namespace mla {
 
 namespace {
 
-typedef __attribute__((address_space(3))) uint8_t pf_lds;
-typedef __attribute__((address_space(3))) u32x4_t pf_lds4;
-
 constexpr int kPfDh = 128, kPfDr = 64, kPfDq = kPfDh + kPfDr;  // 192
 constexpr int kPfQ = 128;                                     // query rows per workgroup
 constexpr int kPfSub = 32;                                    // keys per subtile
-constexpr int kPfKRow = kPfDq * 2 + 16;                        // 400 B: padded key row
-constexpr int kPfVRow = kPfDh * 2 + 16;                        // 272 B: padded value row
-constexpr int kPfKTile = kPfSub * kPfKRow;                     // 12,800 B
-constexpr int kPfVTile = kPfSub * kPfVRow;                     // 8,704 B
-constexpr int kPfStage = kPfKTile + kPfVTile;                  // 21,504 B
-constexpr int kPfChunksK = kPfSub * (kPfDq / 8);               // 768 16-byte pieces
-constexpr int kPfChunks = kPfChunksK + kPfSub * (kPfDh / 8);   // 1280
-constexpr int kPfLoads = kPfChunks / 256;                      // 5 per thread
+constexpr int kPfKcB = kPfSub * kPfDh * 2;                     // 8192: content keys, 256-byte rows
+constexpr int kPfKrB = kPfSub * kPfDr * 2;                     // 4096: RoPE keys, 128-byte rows
+constexpr int kPfVB = kPfSub * kPfDh * 2;                      // 8192: values, 256-byte rows
+constexpr int kPfStage = kPfKcB + kPfKrB + kPfVB;              // 20480
+constexpr int kPfRing = 3;
+constexpr int kPfDma = 5;                                      // DMA instructions per thread per subtile
+constexpr float kPfTau = 8.f;                                  // lazy-max slack (log2 units)
 
-__device__ __forceinline__ bf16x4_t pf_tr16(const pf_lds* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p);
-}
+// physical 16-byte chunk of logical chunk c (0..7 within its group of 8) in
+// key row t: XORed with the row's swizzle
+__device__ __forceinline__ int pf_chunk(int c, int t) { return c ^ swz_f(t); }
 
 }  // namespace
 
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(const uint16_t* q, const uint16_t* kc,
                                                            const uint16_t* kr, const uint16_t* v, void* out,
-                                                           float* lse, int T, int n_h, float scale2,
+                                                           float* lse, int T, int n_h, int nqb, float scale2,
                                                            int out_bf16) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * kPfStage];
-  pf_lds* smem = (pf_lds*)smem_raw;
+  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[kPfRing * kPfStage];
+  lds_u8* smem = (lds_u8*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31, j16 = lane & 15, G = lane >> 4;
-  const int h = blockIdx.y;
-  const int qb = blockIdx.x * kPfQ;
+  // XCD-aware work item: the k-th workgroup dealt to XCD x takes head
+  // (k / nqb) * 8 + x and query block nqb - 1 - k % nqb
+  int h, qblk;
+  {
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    h = (k / nqb) * 8 + x;
+    qblk = nqb - 1 - k % nqb;
+  }
+  if (h >= n_h) return;  // the grid is padded to a multiple of 8 heads
+  const int qb = qblk * kPfQ;
   const int q0 = qb + 32 * w;  // this wave's first query
   const int qrow = q0 + l32;   // this lane's query
   const long long ldq = (long long)n_h * kPfDq, ldk = (long long)n_h * kPfDh;
+  const int w_s = __builtin_amdgcn_readfirstlane(w);
 
   // queries as B fragments: dims 16f + 8g .. +7 of query qrow
   bf16x8_t qf[kPfDq / 16];
@@ -72,49 +79,57 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const uint16_t* q, co
   const int n_sub = (kend + kPfSub - 1) / kPfSub;
   const int wave_end = min(q0 + 32, T);  // keys this wave needs: < wave_end
 
-  // global -> registers -> LDS staging of subtile s (zeros past T)
-  u32x4_t st[kPfLoads];
-  auto load_sub = [&](int s) {
+  // DMA sources of this thread: chunk p = i*256 + tid of a region lands at
+  // LDS chunk p; content keys and values (rows of 16 chunks) take i = 0, 1,
+  // RoPE keys (rows of 8 chunks) i = 0.  Key rows past the sequence end read
+  // its last row (finite values; their scores are masked).
+  int rw[2], cb[2];
 #pragma unroll
-    for (int i = 0; i < kPfLoads; ++i) {
-      const int c = tid + 256 * i;
-      st[i] = u32x4_t{0, 0, 0, 0};
-      int key, part;
-      if (c < kPfChunksK) {
-        key = s * kPfSub + c / (kPfDq / 8);
-        part = c % (kPfDq / 8);
-        if (key < T) {
-          if (part < kPfDh / 8)
-            st[i] = *(const u32x4_t*)(kc + key * ldk + (long long)h * kPfDh + 8 * part);
-          else
-            st[i] = *(const u32x4_t*)(kr + (long long)key * kPfDr + 8 * (part - kPfDh / 8));
-        }
-      } else {
-        const int c2 = c - kPfChunksK;
-        key = s * kPfSub + c2 / (kPfDh / 8);
-        part = c2 % (kPfDh / 8);
-        if (key < T) st[i] = *(const u32x4_t*)(v + key * ldk + (long long)h * kPfDh + 8 * part);
-      }
-    }
-  };
-  auto store_sub = [&](int buf) {
-    pf_lds* base = smem + buf * kPfStage;
+  for (int i = 0; i < 2; ++i) {
+    const int p = i * 256 + tid, t = p >> 4;
+    rw[i] = t;
+    cb[i] = ((p & 8) | pf_chunk(p & 7, t)) * 16;
+  }
+  const int rw_r = tid >> 3, cb_r = pf_chunk(tid & 7, tid >> 3) * 16;
+  const int kstride = (int)(ldk * 2);  // bytes between key rows of k^C / v^C
+  auto issue = [&](int s) {
+    const int j0 = s * kPfSub, last = T - 1 - j0;
+    const i32x4_t rkc = make_rsrc(kc + (long long)j0 * ldk + (long long)h * kPfDh);
+    const i32x4_t rkr = make_rsrc(kr + (long long)j0 * kPfDr);
+    const i32x4_t rv = make_rsrc(v + (long long)j0 * ldk + (long long)h * kPfDh);
+    const int m0b = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(smem + (s % kPfRing) * kPfStage));
+    dma_fence();
 #pragma unroll
-    for (int i = 0; i < kPfLoads; ++i) {
-      const int c = tid + 256 * i;
-      if (c < kPfChunksK)
-        *(pf_lds4*)(base + (c / (kPfDq / 8)) * kPfKRow + (c % (kPfDq / 8)) * 16) = st[i];
-      else {
-        const int c2 = c - kPfChunksK;
-        *(pf_lds4*)(base + kPfKTile + (c2 / (kPfDh / 8)) * kPfVRow + (c2 % (kPfDh / 8)) * 16) = st[i];
-      }
-    }
+    for (int i = 0; i < 2; ++i)
+      dma16_m0(rkc, min(rw[i], last) * kstride + cb[i], m0b + i * 4096 + w_s * 1024);
+    dma16_m0(rkr, min(rw_r, last) * (kPfDr * 2) + cb_r, m0b + kPfKcB + w_s * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      dma16_m0(rv, min(rw[i], last) * kstride + cb[i], m0b + kPfKcB + kPfKrB + i * 4096 + w_s * 1024);
   };
 
-  // value fragment offsets (transposed reads): rows ta (first 4 k-slots) and
-  // ta + 8 (last 4) of a 16-key step; dims of block db: 32db + 16(G&1) + 4(j16&3)
-  const int ta = 4 * g + (j16 >> 2);
-  const int vcol = (16 * (G & 1) + 4 * (j16 & 3)) * 2;
+  // LDS read offsets.  QK step f: k-block f (dims 16f .. 16f+15), this lane's
+  // key row l32, chunk 2f + g of the content (f < 8) or RoPE (f >= 8) row.
+  int off_kc[4], off_kr[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    off_kc[b] = l32 * (kPfDh * 2) + pf_chunk(2 * b + g, l32) * 16;
+    off_kr[b] = kPfKcB + l32 * (kPfDr * 2) + pf_chunk(2 * b + g, l32) * 16;
+  }
+  // transposed value reads: rows ta (first 4 k-slots) and ta + 8 (last 4) of
+  // a 16-key step; even / odd 32-dim blocks
+  int off_pv[2][2];
+  {
+    const int ta = 4 * g + (j16 >> 2);
+    const int clo = 2 * (G & 1) + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int t = ta + 8 * hh;
+        off_pv[pp][hh] = kPfKcB + kPfKrB + t * (kPfDh * 2) + pf_chunk(4 * pp + clo, t) * 16 + (j16 & 1) * 8;
+      }
+  }
 
   f32x16_t acc[kPfDh / 32];
 #pragma unroll
@@ -123,13 +138,17 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const uint16_t* q, co
     for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  load_sub(0);
-  store_sub(0);
-  __syncthreads();
+  wait_vm<0>();  // the query loads are complete before the first DMA
+  issue(0);
+  if (n_sub > 1) issue(1);
   for (int s = 0; s < n_sub; ++s) {
-    if (s + 1 < n_sub) load_sub(s + 1);  // in flight during this subtile
-    const pf_lds* kt = smem + (s & 1) * kPfStage;
-    const pf_lds* vt = kt + kPfKTile;
+    if (s + 1 < n_sub)
+      wait_vm<kPfDma>();  // subtile s landed (s + 1 may still be in flight)
+    else
+      wait_vm<0>();
+    __syncthreads();  // subtile s visible; every wave is done with subtile s - 1
+    if (s + 2 < n_sub) issue(s + 2);  // into the slot subtile s - 1 used
+    const lds_u8* tile = smem + (s % kPfRing) * kPfStage;
     const int j0 = s * kPfSub;
     if (j0 < wave_end) {  // uniform per wave: some of these keys are visible
       // ---- S^T = K . Q^T
@@ -138,59 +157,64 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const uint16_t* q, co
       for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
       for (int f = 0; f < kPfDq / 16; ++f) {
-        const bf16x8_t ka = *(const __attribute__((address_space(3))) bf16x8_t*)(kt + l32 * kPfKRow + (16 * f + 8 * g) * 2);
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[f], sc, 0, 0, 0);
+        const bf16x8_t ka = f < 8 ? lds_b128(tile + off_kc[f & 3] + (f >> 2) * 128)
+                                  : lds_b128(tile + off_kr[f & 3] + ((f - 8) >> 2) * 128);
+        sc = mfma(ka, qf[f], sc);
       }
-      // ---- causal mask (diagonal subtile) and online softmax, exp2 domain
-      float mx = -INFINITY;
+      // ---- causal mask (only subtiles that reach past the wave's first query
+      // or past T) and online softmax in the exp2 domain
+      if (j0 + kPfSub - 1 > q0 || j0 + kPfSub > T) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        sc[r] = key <= qrow && key < T ? sc[r] * scale2 : -INFINITY;
-        mx = fmaxf(mx, sc[r]);
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key > qrow || key >= T) sc[r] = -INFINITY;
+        }
       }
+      float mx = sc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
       }
-      const float m_new = fmaxf(m_run, mx);
-      const float corr = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      // lazy reference: it moves only when some query's max exceeds it by
+      // more than 2^kPfTau (numerator and denominator share it, so the result
+      // is exact; p stays below 2^kPfTau)
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kPfTau)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first update
+        l_run *= corr;
+#pragma unroll
+        for (int d = 0; d < kPfDh / 32; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[d][r] *= corr;
+        m_run = m_new;
+      }
       float ps = 0.f;
       bf16x8_t P[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = m_new == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[r] - m_new);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], scale2, -m_run));
         ps += p;
         P[r >> 3][r & 7] = (__bf16)p;
       }
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
-        ps = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        l_run += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
-      l_run = l_run * corr + ps;
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < kPfDh / 32; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[d][r] *= corr;
       // ---- O^T += V^T . P^T: keys 16ks + {4g..4g+3, 8+4g..8+4g+3}
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int d = 0; d < kPfDh / 32; ++d) {
-          const pf_lds* p0 = vt + (16 * ks + ta) * kPfVRow + 32 * d * 2 + vcol;
-          const bf16x4_t lo = pf_tr16(p0);
-          const bf16x4_t hi = pf_tr16(p0 + 8 * kPfVRow);
+          const lds_u8* p0 = tile + (d >> 1) * 128 + ks * 16 * (kPfDh * 2);
+          const bf16x4_t lo = lds_tr16(p0 + off_pv[d & 1][0]);
+          const bf16x4_t hi = lds_tr16(p0 + off_pv[d & 1][1]);
           bf16x8_t va;
           va[0] = lo[0]; va[1] = lo[1]; va[2] = lo[2]; va[3] = lo[3];
           va[4] = hi[0]; va[5] = hi[1]; va[6] = hi[2]; va[7] = hi[3];
-          acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, P[ks], acc[d], 0, 0, 0);
+          acc[d] = mfma(va, P[ks], acc[d]);
         }
-    }
-    __syncthreads();  // every wave is done with buffer s & 1
-    if (s + 1 < n_sub) {
-      store_sub((s + 1) & 1);
-      __syncthreads();
     }
   }
   // ---- normalise and store: lane = query, acc[d] rows = dims 32d + 8(r/4) + 4g + r%4
@@ -276,10 +300,12 @@ hipError_t launch_prefill(const void* q, const void* kc, const void* kr, const v
                           int T, int n_h, int d_h, int d_r, float scale, int in_dtype, int out_dtype,
                           hipStream_t s) {
   if (prefill_mfma_eligible(d_h, d_r, in_dtype, q, kc, kr, v)) {
-    dim3 grid((T + kPfQ - 1) / kPfQ, n_h);
-    hipLaunchKernelGGL(prefill_mfma_kernel, grid, dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)kc,
-                       (const uint16_t*)kr, (const uint16_t*)v, out, lse, T, n_h, scale * kLog2e,
-                       out_dtype == 1 ? 1 : 0);
+    const int nqb = (T + kPfQ - 1) / kPfQ;
+    const long long grid = (long long)nqb * ((n_h + 7) / 8 * 8);  // heads padded to a multiple of the 8 XCDs
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(prefill_mfma_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const uint16_t*)q,
+                       (const uint16_t*)kc, (const uint16_t*)kr, (const uint16_t*)v, out, lse, T, n_h, nqb,
+                       scale * kLog2e, out_dtype == 1 ? 1 : 0);
   } else {
     const long long rows = (long long)T * n_h;
     hipLaunchKernelGGL(prefill_generic_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, q, kc, kr, v,

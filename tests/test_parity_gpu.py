@@ -468,8 +468,9 @@ def test_prefill_mha_bf16_v3(T):
     assert_lse_close(lse.cpu().numpy().astype(np.float64), ref_lse, "prefill lse")
     # bf16 output: the fp32 result rounded once more
     assert_bf16_close(o16.float().cpu().numpy().astype(np.float64), ref_o, "prefill bf16 out")
-    if T == 1:  # one visible key: the output is that key's value row exactly (p = 1)
-        assert np.array_equal(g[0], oracle.bf16_to_f64(inp["v_c"])[0])
+    if T == 1:  # one visible key: the output is that key's value row (p = 1 up to fp32 rounding)
+        v0 = oracle.bf16_to_f64(inp["v_c"])[0]
+        assert np.all(np.abs(g[0] - v0) <= 1e-6 * np.abs(v0))
 
 
 def test_prefill_mha_full_size_sampled_heads():
