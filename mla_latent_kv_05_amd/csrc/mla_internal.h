@@ -102,6 +102,10 @@ hipError_t launch_absorb(const void* q, long long q_st, const void* w, void* out
 hipError_t launch_prefill(const void* q, const void* kc, const void* kr, const void* v, void* out, float* lse,
                           int T, int n_h, int d_h, int d_r, float scale, int in_dtype, int out_dtype,
                           hipStream_t s);
+bool expand_gemm_eligible(long long a_st, int N, int K, int out_dtype, const void* a, const void* w0,
+                          const void* w1, const void* o0, const void* o1);
+hipError_t launch_expand_gemm(const void* a, long long a_st, const void* w0, const void* w1, void* o0, void* o1,
+                              int T, int N, int K, int out_dtype, hipStream_t s);
 constexpr int kMaxRopePairs = 64;  // d_r <= 128 for the cache producer
 size_t append_workspace_bytes(int T, int d, int d_c, int d_r);
 hipError_t launch_append(const void* h, long long h_st, const void* w, const int32_t* positions,

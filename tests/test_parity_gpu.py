@@ -538,6 +538,20 @@ def test_expand_kv_bf16_v3(T):
     assert_bf16_close(v16.float().cpu().numpy().astype(np.float64), rv, "v_c bf16")
 
 
+def test_expand_kv_bf16_heads_off_the_gemm_tile():
+    """n_h * d_h = 192 is not a multiple of the GEMM's 256-row tile: the
+    expansion takes the per-head up-projection kernel (shared latent row)."""
+    T, n_h, d_h, d_c = 70, 3, 64, 128
+    say("expand_kv bf16 small heads")
+    inp = inputs.prefill_inputs(211, T, n_h=n_h, d_h=d_h, d_r=32, d_c=d_c)
+    c_kv, w_uk, w_uv = _pf_dev(inp, "c_kv", "w_uk", "w_uv")
+    k_c, v_c = binding.expand_kv(c_kv, w_uk, w_uv, d_h, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rk, rv = oracle.expand_kv(*_pf_dec(inp, "c_kv", "w_uk", "w_uv"), n_h, d_h)
+    assert_f32_close(k_c.cpu().numpy().astype(np.float64), rk, "k_c", tol=1e-5)
+    assert_f32_close(v_c.cpu().numpy().astype(np.float64), rv, "v_c", tol=1e-5)
+
+
 def test_expand_then_prefill_toy_fp32_layer():
     """fp32 toy layer in MHA mode, every step on the GPU: latent -> expand_kv ->
     prefill, against the oracle's MHA-mode layer output o (before W^O)."""
