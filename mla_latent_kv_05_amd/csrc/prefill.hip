@@ -20,6 +20,8 @@
 //                     columns by ds_read_b64_tr_b16, B = P from the S layout)
 // Workgroups are dealt to the 8 XCDs so that all query blocks of a head run
 // on one XCD (its L2 keeps that head's keys and values), longest first.
+#include <type_traits>
+
 #include "mfma_common.h"
 
 namespace mla {
@@ -37,9 +39,16 @@ constexpr int kPfRing = 3;
 constexpr int kPfDma = 5;                                      // DMA instructions per thread per subtile
 constexpr float kPfTau = 8.f;                                  // lazy-max slack (log2 units)
 
-// physical 16-byte chunk of logical chunk c (0..7 within its group of 8) in
-// key row t: XORed with the row's swizzle
-__device__ __forceinline__ int pf_chunk(int c, int t) { return c ^ swz_f(t); }
+// LDS swizzles (64 banks of 4 bytes: a 256-byte line per cycle).  Content
+// key and value rows are 256 bytes (16 chunks of 16 bytes): chunk c of row t
+// sits at c ^ f16(t).  f16 is a bijection on the row's low 4 bits, so 16
+// consecutive rows reading one logical chunk (ds_read_b128) hit 16 different
+// chunk positions, and rows 4a .. 4a+3 get distinct values of bits 2-3, so
+// the transposed value reads (4 rows x 4 adjacent chunks per 32 lanes) cover
+// all 16 positions too.  RoPE key rows are 128 bytes (two per line): chunk c
+// of row t sits at c ^ ((t >> 1) & 7).
+__device__ __forceinline__ int pf_f16(int t) { return 4 * (t & 3) + ((t >> 2) & 3); }
+__device__ __forceinline__ int pf_f8(int t) { return (t >> 1) & 7; }
 
 }  // namespace
 
@@ -60,11 +69,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const uint16_t* q, co
     qblk = nqb - 1 - k % nqb;
   }
   if (h >= n_h) return;  // the grid is padded to a multiple of 8 heads
-  const int qb = qblk * kPfQ;
-  const int q0 = qb + 32 * w;  // this wave's first query
-  const int qrow = q0 + l32;   // this lane's query
-  const long long ldq = (long long)n_h * kPfDq, ldk = (long long)n_h * kPfDh;
   const int w_s = __builtin_amdgcn_readfirstlane(w);
+  const int qb = qblk * kPfQ;
+  const int q0 = qb + 32 * w_s;  // this wave's first query (scalar)
+  const int qrow = q0 + l32;     // this lane's query
+  const long long ldq = (long long)n_h * kPfDq, ldk = (long long)n_h * kPfDh;
 
   // queries as B fragments: dims 16f + 8g .. +7 of query qrow
   bf16x8_t qf[kPfDq / 16];
@@ -88,16 +97,17 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const uint16_t* q, co
   for (int i = 0; i < 2; ++i) {
     const int p = i * 256 + tid, t = p >> 4;
     rw[i] = t;
-    cb[i] = ((p & 8) | pf_chunk(p & 7, t)) * 16;
+    cb[i] = ((p & 15) ^ pf_f16(t)) * 16;
   }
-  const int rw_r = tid >> 3, cb_r = pf_chunk(tid & 7, tid >> 3) * 16;
+  const int rw_r = tid >> 3, cb_r = ((tid & 7) ^ pf_f8(tid >> 3)) * 16;
   const int kstride = (int)(ldk * 2);  // bytes between key rows of k^C / v^C
-  auto issue = [&](int s) {
+  const int lds0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)smem);
+  auto issue = [&](int s, int slot) {
     const int j0 = s * kPfSub, last = T - 1 - j0;
     const i32x4_t rkc = make_rsrc(kc + (long long)j0 * ldk + (long long)h * kPfDh);
     const i32x4_t rkr = make_rsrc(kr + (long long)j0 * kPfDr);
     const i32x4_t rv = make_rsrc(v + (long long)j0 * ldk + (long long)h * kPfDh);
-    const int m0b = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(smem + (s % kPfRing) * kPfStage));
+    const int m0b = lds0 + slot * kPfStage;
     dma_fence();
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -108,26 +118,27 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const uint16_t* q, co
       dma16_m0(rv, min(rw[i], last) * kstride + cb[i], m0b + kPfKcB + kPfKrB + i * 4096 + w_s * 1024);
   };
 
-  // LDS read offsets.  QK step f: k-block f (dims 16f .. 16f+15), this lane's
-  // key row l32, chunk 2f + g of the content (f < 8) or RoPE (f >= 8) row.
-  int off_kc[4], off_kr[4];
+  // LDS read offsets (relative to a ring slot, which is a compile-time
+  // constant in the unrolled loop).  QK step f: this lane's key row l32,
+  // logical chunk 2f + g of the content (f < 8) or RoPE (f >= 8) row.
+  int off_kc[8], off_kr[4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    off_kc[b] = l32 * (kPfDh * 2) + pf_chunk(2 * b + g, l32) * 16;
-    off_kr[b] = kPfKcB + l32 * (kPfDr * 2) + pf_chunk(2 * b + g, l32) * 16;
-  }
-  // transposed value reads: rows ta (first 4 k-slots) and ta + 8 (last 4) of
-  // a 16-key step; even / odd 32-dim blocks
-  int off_pv[2][2];
+  for (int f = 0; f < 8; ++f) off_kc[f] = l32 * (kPfDh * 2) + ((2 * f + g) ^ pf_f16(l32)) * 16;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) off_kr[b] = kPfKcB + l32 * (kPfDr * 2) + ((2 * b + g) ^ pf_f8(l32)) * 16;
+  // transposed value reads of dim block d (32 dims = chunks 4d .. 4d+3): rows
+  // ta (first 4 k-slots) and ta + 8 (last 4) of a 16-key step (+16 rows for
+  // the second step: the swizzle ignores bit 4)
+  int off_pv[4][2];
   {
     const int ta = 4 * g + (j16 >> 2);
     const int clo = 2 * (G & 1) + ((j16 & 3) >> 1);
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp)
+    for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int t = ta + 8 * hh;
-        off_pv[pp][hh] = kPfKcB + kPfKrB + t * (kPfDh * 2) + pf_chunk(4 * pp + clo, t) * 16 + (j16 & 1) * 8;
+        off_pv[d][hh] = kPfKcB + kPfKrB + t * (kPfDh * 2) + ((4 * d + clo) ^ pf_f16(t)) * 16 + (j16 & 1) * 8;
       }
   }
 
@@ -138,27 +149,26 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const uint16_t* q, co
     for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  wait_vm<0>();  // the query loads are complete before the first DMA
-  issue(0);
-  if (n_sub > 1) issue(1);
-  for (int s = 0; s < n_sub; ++s) {
+  // one subtile in ring slot SLOT (a compile-time constant, so every LDS
+  // offset below folds into the instruction's immediate)
+  auto step = [&](int s, auto slot_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
     if (s + 1 < n_sub)
       wait_vm<kPfDma>();  // subtile s landed (s + 1 may still be in flight)
     else
       wait_vm<0>();
     __syncthreads();  // subtile s visible; every wave is done with subtile s - 1
-    if (s + 2 < n_sub) issue(s + 2);  // into the slot subtile s - 1 used
-    const lds_u8* tile = smem + (s % kPfRing) * kPfStage;
+    if (s + 2 < n_sub) issue(s + 2, (SLOT + 2) % kPfRing);  // into the slot subtile s - 1 used
+    const lds_u8* tile = smem + SLOT * kPfStage;
     const int j0 = s * kPfSub;
-    if (j0 < wave_end) {  // uniform per wave: some of these keys are visible
+    if (j0 < wave_end) {  // scalar branch: some of these keys are visible to this wave
       // ---- S^T = K . Q^T
       f32x16_t sc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
       for (int f = 0; f < kPfDq / 16; ++f) {
-        const bf16x8_t ka = f < 8 ? lds_b128(tile + off_kc[f & 3] + (f >> 2) * 128)
-                                  : lds_b128(tile + off_kr[f & 3] + ((f - 8) >> 2) * 128);
+        const bf16x8_t ka = f < 8 ? lds_b128(tile + off_kc[f & 7]) : lds_b128(tile + off_kr[f & 3]);
         sc = mfma(ka, qf[f], sc);
       }
       // ---- causal mask (only subtiles that reach past the wave's first query
@@ -207,15 +217,23 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const uint16_t* q, co
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int d = 0; d < kPfDh / 32; ++d) {
-          const lds_u8* p0 = tile + (d >> 1) * 128 + ks * 16 * (kPfDh * 2);
-          const bf16x4_t lo = lds_tr16(p0 + off_pv[d & 1][0]);
-          const bf16x4_t hi = lds_tr16(p0 + off_pv[d & 1][1]);
+          const lds_u8* p0 = tile + ks * 16 * (kPfDh * 2);
+          const bf16x4_t lo = lds_tr16(p0 + off_pv[d][0]);
+          const bf16x4_t hi = lds_tr16(p0 + off_pv[d][1]);
           bf16x8_t va;
           va[0] = lo[0]; va[1] = lo[1]; va[2] = lo[2]; va[3] = lo[3];
           va[4] = hi[0]; va[5] = hi[1]; va[6] = hi[2]; va[7] = hi[3];
           acc[d] = mfma(va, P[ks], acc[d]);
         }
     }
+  };
+  wait_vm<0>();  // the query loads are complete before the first DMA
+  issue(0, 0);
+  if (n_sub > 1) issue(1, 1);
+  for (int s = 0; s < n_sub; s += kPfRing) {
+    step(s, std::integral_constant<int, 0>{});
+    if (s + 1 < n_sub) step(s + 1, std::integral_constant<int, 1>{});
+    if (s + 2 < n_sub) step(s + 2, std::integral_constant<int, 2>{});
   }
   // ---- normalise and store: lane = query, acc[d] rows = dims 32d + 8(r/4) + 4g + r%4
   if (qrow < T) {
