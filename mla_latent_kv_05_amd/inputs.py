@@ -26,6 +26,13 @@ Storage layouts (shared contract with the C ABI):
   per token = ``[c^KV | k^R]``.
 * fp8 cache: per block ``[block_size*d_c e4m3fn | block_size*d_r bf16 k^R |
   block_size fp32 scale]``, i.e. 644 bytes per token at d_c=512, d_r=64.
+* int4 / int2 caches (4-bit or 2-bit content, 4-bit RoPE key): per block
+  ``[block_size x content codes | block_size x RoPE codes | block_size x
+  (d_c+d_r)/32 (scale, min) fp16 pairs]``; groups of 32 consecutive values of
+  one token share a scale and a minimum, value = code * scale + min.  Codes
+  are packed in little-endian 32-bit words of 8 (4-bit) or 16 (2-bit)
+  consecutive values: value 2k sits at bit k*b, value 2k+1 at bit 16 + k*b.
+  360 (int4) or 232 (int2) bytes per token at d_c=512, d_r=64.
 """
 
 from __future__ import annotations
@@ -114,6 +121,57 @@ def quantize_rows_e4m3(c) -> tuple[np.ndarray, np.ndarray]:
     return codes, scale
 
 
+INT_GROUP = 32
+
+
+def pack_codes(codes, bits: int) -> np.ndarray:
+    """Pack unsigned codes [..., n] (n a multiple of 32 / bits * 2) into
+    little-endian uint32 words: value 2k of a word at bit k*bits, value 2k+1
+    at bit 16 + k*bits.  Returns the bytes [..., n * bits / 8]."""
+    c = np.asarray(codes, dtype=np.uint32)
+    per = 32 // bits
+    w = c.reshape(*c.shape[:-1], -1, per)
+    word = np.zeros(w.shape[:-1], dtype=np.uint32)
+    for k in range(per // 2):
+        word |= w[..., 2 * k] << np.uint32(k * bits)
+        word |= w[..., 2 * k + 1] << np.uint32(16 + k * bits)
+    return word.view(np.uint8).reshape(*c.shape[:-1], -1)
+
+
+def quantize_groups(x, bits: int, group: int = INT_GROUP):
+    """Asymmetric uniform quantisation of rows x [..., n] in groups of
+    ``group`` consecutive values: min m and scale s = (max - min) / (2^bits - 1),
+    both rounded to fp16; codes = clip(rint((x - m) / s), 0, 2^bits - 1)
+    (0 where s = 0).  Returns (codes uint8 [..., n], params fp16 [..., n/group, 2])."""
+    x = np.asarray(x, dtype=np.float64)
+    g = x.reshape(*x.shape[:-1], -1, group)
+    lo, hi = g.min(axis=-1), g.max(axis=-1)
+    qmax = (1 << bits) - 1
+    s16 = ((hi - lo) / qmax).astype(np.float16)
+    m16 = lo.astype(np.float16)
+    s = s16.astype(np.float64)[..., None]
+    m = m16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s > 0, np.rint((g - m) / np.where(s > 0, s, 1.0)), 0.0)
+    codes = np.clip(q, 0, qmax).astype(np.uint8).reshape(x.shape)
+    return codes, np.stack([s16, m16], axis=-1)
+
+
+def int_row_bytes(d_c: int, d_r: int, content_bits: int) -> int:
+    return d_c * content_bits // 8 + d_r // 2 + (d_c + d_r) // INT_GROUP * 4
+
+
+def int_blocks(rows, d_c: int, content_bits: int) -> np.ndarray:
+    """Rows [n, block_size, d_c + d_r] -> int cache blocks [n, block bytes]."""
+    n, bs = rows.shape[:2]
+    d_r = rows.shape[-1] - d_c
+    cc, cp = quantize_groups(rows[..., :d_c], content_bits)
+    rc, rp = quantize_groups(rows[..., d_c:], 4)
+    parts = [pack_codes(cc, content_bits).reshape(n, -1), pack_codes(rc, 4).reshape(n, -1),
+             np.concatenate([cp, rp], axis=-2).view(np.uint8).reshape(n, -1)]
+    return np.concatenate(parts, axis=1)
+
+
 # --------------------------------------------------------------------------
 # toy layer (fp32): d=1024, n_h=8, d_h=64, d_c=128, d_cq=256, d_r=32
 # --------------------------------------------------------------------------
@@ -155,7 +213,7 @@ class DecodeCase:
     d_r: int
     d_h: int
     block_size: int
-    kv_dtype: str               # "bf16" | "fp8" | "f32"
+    kv_dtype: str               # "bf16" | "fp8" | "f32" | "int4" | "int2"
     q_dtype: str                # "bf16" | "f32"
     seq_lens: np.ndarray        # [B] int32
     block_table: np.ndarray     # [B, max_blocks] int32 (unused slots = -1 ... or poison)
@@ -170,6 +228,8 @@ class DecodeCase:
     def row_bytes(self) -> int:
         if self.kv_dtype == "fp8":
             return self.d_c + 2 * self.d_r + 4
+        if self.kv_dtype in ("int4", "int2"):
+            return int_row_bytes(self.d_c, self.d_r, 4 if self.kv_dtype == "int4" else 2)
         return (self.d_c + self.d_r) * (2 if self.kv_dtype == "bf16" else 4)
 
     @property
@@ -232,6 +292,9 @@ def decode_case(seed: int, B: int, seq_lens, s_q: int = 1, n_h: int = 128,
         cache = np.empty((num_blocks, block_size, D), dtype=np.float32)
     elif kv_dtype == "fp8":
         cache = np.empty((num_blocks, block_size * (d_c + 2 * d_r + 4)), dtype=np.uint8)
+    elif kv_dtype in ("int4", "int2"):
+        cbits = 4 if kv_dtype == "int4" else 2
+        cache = np.empty((num_blocks, block_size * int_row_bytes(d_c, d_r, cbits)), dtype=np.uint8)
     else:
         raise ValueError(kv_dtype)
     chunk = 32
@@ -242,6 +305,8 @@ def decode_case(seed: int, B: int, seq_lens, s_q: int = 1, n_h: int = 128,
             cache[i0:i1] = f32_to_bf16_bits(rows)
         elif kv_dtype == "f32":
             cache[i0:i1] = rows
+        elif kv_dtype in ("int4", "int2"):
+            cache[i0:i1] = int_blocks(rows, d_c, cbits)
         else:
             n = i1 - i0
             codes, scale = quantize_rows_e4m3(rows[..., :d_c])

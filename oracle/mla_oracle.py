@@ -49,6 +49,11 @@ content codes, bf16 RoPE key) is a reading: the pages name only an fp8
 content cache beside a bf16 RoPE key, so with respect to the pages it is
 parity unpinned -- it is pinned only by self-consistency (the oracle decodes
 exactly the codes and scales the GPU reads) and by the e4m3fn format facts.
+The low-bit caches (int4 / int2: grouped fp16 scale and minimum, packed
+codes) are a reading as well -- the pages name only the bit widths -- and are
+parity unpinned with respect to the pages; the decoder is pinned by
+hand-written byte fixtures and by the quantisation error bound of a
+separately written encoder.
 The cache producer (cache_append) is pinned by an element-by-element
 brute force with complex-number rotation, by torch's own bf16 and fp8
 casts for its encoders, and by appending a toy layer's tokens and decoding
@@ -114,9 +119,44 @@ def paged_rows(cache, block_table_row, L, kv_dtype, d_c, d_r, block_size):
             scale = raw[o2:o2 + 4 * block_size].view(np.float32)[:n].astype(np.float64)
             c[j:j + n] = e4m3fn_to_f64(codes) * scale[:, None]
             kr[j:j + n] = bf16_to_f64(kbits)
+        elif kv_dtype in ("int4", "int2"):
+            cb = 4 if kv_dtype == "int4" else 2
+            raw = np.asarray(blk, dtype=np.uint8)
+            o1 = block_size * d_c * cb // 8
+            o2 = o1 + block_size * d_r // 2
+            ng = (d_c + d_r) // INT_GROUP
+            cc = unpack_codes(raw[:o1].reshape(block_size, -1)[:n], cb)
+            rc = unpack_codes(raw[o1:o2].reshape(block_size, -1)[:n], 4)
+            prm = raw[o2:o2 + 4 * ng * block_size].view(np.float16).reshape(block_size, ng, 2)[:n]
+            prm = prm.astype(np.float64)
+            vals = np.concatenate([cc, rc], axis=1).reshape(n, ng, INT_GROUP)
+            deq = (vals * prm[..., 0:1] + prm[..., 1:2]).reshape(n, d_c + d_r)
+            c[j:j + n], kr[j:j + n] = deq[:, :d_c], deq[:, d_c:]
         else:
             raise ValueError(kv_dtype)
     return c, kr
+
+
+# Low-bit caches (the QuantMLA review's INT4 content + INT4 RoPE and INT2
+# content + INT4 RoPE; the grouping, the asymmetric (scale, min) form and the
+# packing are readings): groups of INT_GROUP consecutive values of one token
+# share an fp16 scale and an fp16 minimum, value = code * scale + min.
+INT_GROUP = 32
+
+
+def unpack_codes(raw, bits):
+    """Little-endian 32-bit words of packed unsigned codes -> codes as float64.
+
+    A word holds 32 / bits consecutive values; value 2k is the bit field at
+    k * bits, value 2k + 1 the one at 16 + k * bits."""
+    words = np.ascontiguousarray(raw).view("<u4").astype(np.int64)
+    per = 32 // bits
+    mask = (1 << bits) - 1
+    out = np.empty(words.shape + (per,), dtype=np.float64)
+    for k in range(per // 2):
+        out[..., 2 * k] = (words >> (k * bits)) & mask
+        out[..., 2 * k + 1] = (words >> (16 + k * bits)) & mask
+    return out.reshape(*words.shape[:-1], -1)
 
 
 # --------------------------------------------------------------------------

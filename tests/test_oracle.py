@@ -346,6 +346,76 @@ def test_fp8_cache_roundtrip_error_bound():
         assert np.array_equal(kr, oracle.bf16_to_f64(inputs.f32_to_bf16_bits(logical[:, 512:])))
 
 
+# ---------------------------------------------------------------- low-bit caches
+# Layout (a reading; the QuantMLA review names only INT4 content + INT4 RoPE
+# and INT2 content + INT4 RoPE): per block [bs x content codes | bs x RoPE
+# codes | bs x groups x (fp16 scale, fp16 min)], groups of 32 values of one
+# token, value = code * scale + min; little-endian 32-bit words, value 2k at
+# bit k*b and value 2k+1 at bit 16 + k*b.  The fixtures below are written out
+# by hand from that description.
+
+_W4_0_7 = "20643175"      # values 0..7      -> word 0x75316420
+_W4_8_15 = "a8ecb9fd"     # values 8..15     -> word 0xFDB9ECA8
+_W2_0123 = "8888dddd"     # values 0,1,2,3 repeated (2-bit) -> word 0xDDDD8888
+
+
+def _hexbytes(*parts):
+    return np.frombuffer(bytes.fromhex("".join(parts)), dtype=np.uint8)
+
+
+def test_int4_decoder_hand_fixture():
+    # block_size 2, d_c = d_r = 32: token 0 content codes e % 16 with scale 0.5,
+    # min -1; RoPE codes all 3 with scale 0.25, min 2; token 1 all codes 0 with
+    # scale 0 and mins 1.5 / -0.5
+    content = _hexbytes(_W4_0_7, _W4_8_15, _W4_0_7, _W4_8_15) .tolist() + [0] * 16
+    rope = _hexbytes("33333333" * 4).tolist() + [0] * 16
+    params = _hexbytes("0038" "00bc", "0034" "0040", "0000" "003e", "0000" "00b8").tolist()
+    blk = np.array(content + rope + params, dtype=np.uint8)[None]
+    c, kr = oracle.paged_rows(blk, [0], 2, "int4", 32, 32, 2)
+    e = np.arange(32)
+    assert np.array_equal(c[0], -1.0 + 0.5 * (e % 16))
+    assert np.array_equal(kr[0], np.full(32, 2.75))
+    assert np.array_equal(c[1], np.full(32, 1.5)) and np.array_equal(kr[1], np.full(32, -0.5))
+
+
+def test_int2_decoder_hand_fixture():
+    # block_size 1, d_c = 32 (2-bit codes e % 4, scale 1, min 0), d_r = 32
+    # (4-bit codes e % 16, scale 2, min -8)
+    blk = _hexbytes(_W2_0123, _W2_0123, _W4_0_7, _W4_8_15, _W4_0_7, _W4_8_15,
+                    "003c" "0000", "0040" "00c8")[None]
+    c, kr = oracle.paged_rows(blk, [0], 1, "int2", 32, 32, 1)
+    e = np.arange(32)
+    assert np.array_equal(c[0], (e % 4).astype(float))
+    assert np.array_equal(kr[0], -8.0 + 2.0 * (e % 16))
+
+
+@pytest.mark.parametrize("kv", ["int4", "int2"])
+def test_int_cache_roundtrip_error_bound(kv):
+    """Inputs' quantiser (written separately) -> oracle decoder: every value is
+    within half a step of its group's fp16 scale of the original, plus what the
+    fp16 rounding of the scale and minimum can move the grid."""
+    case = inputs.decode_case(19, B=2, seq_lens=np.array([90, 40]), n_h=4, kv_dtype=kv)
+    rng = np.random.Generator(np.random.PCG64(19))
+    rng.permutation(case.num_blocks)
+    rows = rng.standard_normal((case.num_blocks, 64, 576), dtype=np.float32).astype(np.float64)
+    for b in range(2):
+        L = int(case.seq_lens[b])
+        c, kr = oracle.paged_rows(case.cache, case.block_table[b], L, kv, 512, 64, 64)
+        logical = np.concatenate([rows[case.block_table[b, j]] for j in range((L + 63) // 64)])[:L]
+        for got, x, bits in ((c, logical[:, :512], 4 if kv == "int4" else 2), (kr, logical[:, 512:], 4)):
+            g = x.reshape(L, -1, 32)
+            lo, hi = g.min(-1, keepdims=True), g.max(-1, keepdims=True)
+            qmax = (1 << bits) - 1
+            s = (hi - lo) / qmax
+            s16 = s.astype(np.float16).astype(np.float64)
+            m16 = lo.astype(np.float16).astype(np.float64)
+            bound = 0.5 * s16 + qmax * np.abs(s16 - s) + np.abs(m16 - lo) + 1e-12
+            assert np.all(np.abs(got.reshape(L, -1, 32) - g) <= bound)
+            # the decoded values lie on the group's grid m16 + k * s16, k in 0..qmax
+            k = (got.reshape(L, -1, 32) - m16) / np.where(s16 > 0, s16, 1.0)
+            assert np.all(np.abs(k - np.rint(k)) < 1e-6) and k.min() > -1e-6 and k.max() < qmax + 1e-6
+
+
 # ---------------------------------------------------------------- cache producer
 
 def test_bf16_encoder_matches_torch_cast():
