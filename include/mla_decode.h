@@ -41,6 +41,9 @@ extern "C" {
 #define MLA_F32 0      /* IEEE binary32 */
 #define MLA_BF16 1     /* bfloat16 */
 #define MLA_FP8_E4M3 2 /* OCP 8-bit float E4M3 ("fn": max 448, no infinities) */
+/* low-bit latent-cache formats (kv_dtype of mla_decode_absorbed only) */
+#define MLA_INT4 3     /* 4-bit content codes + 4-bit RoPE codes, grouped fp16 scale/min */
+#define MLA_INT2 4     /* 2-bit content codes + 4-bit RoPE codes, grouped fp16 scale/min */
 
 /* status codes */
 #define MLA_OK 0
@@ -106,6 +109,16 @@ size_t mla_decode_workspace_bytes(int B, int s_q, int n_h, int d_c, int max_bloc
  *           kv_dtype MLA_FP8_E4M3: per block [block_size*d_c e4m3fn content |
  *             block_size*d_r bf16 k^R | block_size fp32 per-token scales];
  *             c_j = e4m3(code) * scale_j (the RoPE key stays bf16).
+ *           kv_dtype MLA_INT4 / MLA_INT2 (the QuantMLA review's INT4 content +
+ *             INT4 RoPE and INT2 content + INT4 RoPE; the grouping and packing
+ *             are this library's): per block [block_size x content codes
+ *             (d_c*b/8 bytes, b = 4 or 2) | block_size x RoPE codes (d_r/2
+ *             bytes) | block_size x (d_c+d_r)/32 pairs (fp16 scale, fp16
+ *             min)]; each group of 32 consecutive values of a token (content
+ *             groups first, then RoPE groups) decodes as code * scale + min.
+ *             Codes are packed in little-endian 32-bit words of 32/b values:
+ *             value 2k at bit k*b, value 2k+1 at bit 16 + k*b.  Needs
+ *             d_c % 32 == 0 and d_r % 32 == 0.
  *  block_table [B, max_blocks_per_seq] int32: logical block k of sequence b
  *           is physical block block_table[b*max_blocks_per_seq + k].
  *  seq_lens [B] int32 (device).

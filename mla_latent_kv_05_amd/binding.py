@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmla.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "mla_decode.h")
 
-MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
+MLA_F32, MLA_BF16, MLA_FP8_E4M3, MLA_INT4, MLA_INT2 = 0, 1, 2, 3, 4
 MLA_FLAG_FORCE_GENERIC = 1
 
 _lib = None

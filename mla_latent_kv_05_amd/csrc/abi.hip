@@ -200,6 +200,19 @@ int mla_decode_kernel_events(void* before, void* after) {
   return MLA_OK;
 }
 
+// bytes per cached token in each format (the block layouts in the header)
+static long long kv_row_bytes(int kv_dtype, int d_c, int d_r) {
+  switch (kv_dtype) {
+    case MLA_F32: return (long long)(d_c + d_r) * 4;
+    case MLA_BF16: return (long long)(d_c + d_r) * 2;
+    case MLA_FP8_E4M3: return (long long)d_c + 2 * d_r + 4;
+    default: {
+      const int cb = kv_dtype == MLA_INT4 ? 4 : 2;
+      return (long long)d_c * cb / 8 + d_r / 2 + (d_c + d_r) / 32 * 4;
+    }
+  }
+}
+
 int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_cache, const int32_t* block_table,
                         int max_blocks_per_seq, const int32_t* seq_lens, int B, int s_q, int n_h, int d_c,
                         int d_r, int block_size, float softmax_scale, int q_dtype, int kv_dtype, int out_dtype,
@@ -209,12 +222,13 @@ int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_ca
     return MLA_ERR_INVALID_ARG;
   if (num_splits < 0 || (flags & ~MLA_FLAG_FORCE_GENERIC)) return MLA_ERR_INVALID_ARG;
   if (!act_dtype_ok(q_dtype) || !act_dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
-  if (kv_dtype != MLA_F32 && kv_dtype != MLA_BF16 && kv_dtype != MLA_FP8_E4M3) return MLA_ERR_INVALID_ARG;
+  if (kv_dtype < MLA_F32 || kv_dtype > MLA_INT2) return MLA_ERR_INVALID_ARG;
   if (!q_lat || !kv_cache || !block_table || !seq_lens || !o_lat) return MLA_ERR_INVALID_ARG;
   if (d_r > 0 && !q_rope) return MLA_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return MLA_ERR_INVALID_ARG;
   if (s_q > 16 || d_c > 2048 || d_r > 256 || d_c % 4 != 0) return MLA_ERR_UNSUPPORTED;
   if (kv_dtype == MLA_FP8_E4M3 && (d_r % 8 != 0 || d_c % 16 != 0)) return MLA_ERR_UNSUPPORTED;
+  if ((kv_dtype == MLA_INT4 || kv_dtype == MLA_INT2) && (d_c % 32 != 0 || d_r % 32 != 0)) return MLA_ERR_UNSUPPORTED;
   if (!aligned16(o_lat)) return MLA_ERR_MISALIGNED;
   if (!workspace) return MLA_ERR_WORKSPACE;
 
@@ -242,9 +256,7 @@ int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_ca
   a.seq = (const int2*)(ws + L.seq);
   a.lse_part = (float*)(ws + L.lse_part);
   a.o_part = (float*)(ws + L.o_part);
-  const long long elem = kv_dtype == MLA_F32 ? 4 : 2;
-  a.block_bytes = kv_dtype == MLA_FP8_E4M3 ? (long long)block_size * (d_c + 2 * d_r + 4)
-                                           : (long long)block_size * (d_c + d_r) * elem;
+  a.block_bytes = (long long)block_size * kv_row_bytes(kv_dtype, d_c, d_r);
   a.max_blocks = max_blocks_per_seq;
   a.B = B; a.s_q = s_q; a.n_h = n_h; a.d_c = d_c; a.d_r = d_r; a.block_size = block_size;
   a.scale = softmax_scale;

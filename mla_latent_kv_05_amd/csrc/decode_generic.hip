@@ -180,16 +180,49 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
 // ============================================================== generic decode
 // One wavefront per query row (query token i, head h), exact online softmax
 // token by token in fp32.  Lanes split the d_c + d_r dimensions.  Any shapes
-// within the ABI limits, fp32 / bf16 / fp8 caches.
+// within the ABI limits, fp32 / bf16 / fp8 / int4 / int2 caches.
 
 constexpr int kMaxQ = 36;  // (2048 + 256) / 64
 constexpr int kMaxC = 32;  // 2048 / 64
+
+// value e of a row of packed b-bit codes: 32/b values per little-endian
+// 32-bit word, value 2k at bit k*b, value 2k+1 at bit 16 + k*b
+__device__ __forceinline__ int packed_code(const uint32_t* words, int e, int b) {
+  const int per = 32 / b, i = e % per;
+  const int shift = (i & 1) ? 16 + (i >> 1) * b : (i >> 1) * b;
+  return (int)((words[e / per] >> shift) & ((1u << b) - 1u));
+}
 
 template <int KV>
 __device__ __forceinline__ void load_kv_row(const DecodeArgs& a, const uint8_t* blk, int slot,
                                             int lane, int nc, float* cv, float* kr_out) {
   // content dims lane + 64k (k < nc) and RoPE dims lane + 64k (k < 4)
-  if (KV == 2) {  // fp8: [bs*d_c codes | bs*d_r bf16 | bs fp32 scale]
+  if (KV == 3 || KV == 4) {  // int4 / int2: [codes | RoPE codes | (scale, min) fp16 per 32 values]
+    constexpr int cb = KV == 3 ? 4 : 2;
+    const size_t crow = (size_t)a.d_c * cb / 8, rrow = (size_t)a.d_r / 2;
+    const int ng = (a.d_c + a.d_r) / 32;
+    const uint32_t* cw = (const uint32_t*)(blk + (size_t)slot * crow);
+    const uint32_t* rw = (const uint32_t*)(blk + (size_t)a.block_size * crow + (size_t)slot * rrow);
+    const _Float16* prm = (const _Float16*)(blk + (size_t)a.block_size * (crow + rrow)) + (size_t)slot * ng * 2;
+#pragma unroll
+    for (int k = 0; k < kMaxC; ++k) {
+      const int d = lane + 64 * k;
+      cv[k] = 0.f;
+      if (k < nc && d < a.d_c) {
+        const int g = d / 32;
+        cv[k] = (float)packed_code(cw, d, cb) * (float)prm[2 * g] + (float)prm[2 * g + 1];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int d = lane + 64 * k;
+      kr_out[k] = 0.f;
+      if (d < a.d_r) {
+        const int g = (a.d_c + d) / 32;
+        kr_out[k] = (float)packed_code(rw, d, 4) * (float)prm[2 * g] + (float)prm[2 * g + 1];
+      }
+    }
+  } else if (KV == 2) {  // fp8: [bs*d_c codes | bs*d_r bf16 | bs fp32 scale]
     const uint8_t* codes = blk + (size_t)slot * a.d_c;
     const uint16_t* kr = (const uint16_t*)(blk + (size_t)a.block_size * a.d_c) + (size_t)slot * a.d_r;
     const float sc = ((const float*)(blk + (size_t)a.block_size * (a.d_c + 2 * a.d_r)))[slot];
@@ -299,8 +332,12 @@ hipError_t launch_decode_generic(const DecodeArgs& a, int units_max, hipStream_t
     hipLaunchKernelGGL(decode_generic_kernel<0>, grid, dim3(256), 0, s, a);
   else if (a.kv_dtype == 1)
     hipLaunchKernelGGL(decode_generic_kernel<1>, grid, dim3(256), 0, s, a);
-  else
+  else if (a.kv_dtype == 2)
     hipLaunchKernelGGL(decode_generic_kernel<2>, grid, dim3(256), 0, s, a);
+  else if (a.kv_dtype == 3)
+    hipLaunchKernelGGL(decode_generic_kernel<3>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_generic_kernel<4>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ def case_to_device(case: inputs.DecodeCase, device="cuda") -> dict:
         kvdt = binding.MLA_F32
     else:
         cache = torch.from_numpy(np.ascontiguousarray(case.cache)).to(device)
-        kvdt = binding.MLA_FP8_E4M3
+        kvdt = {"fp8": binding.MLA_FP8_E4M3, "int4": binding.MLA_INT4, "int2": binding.MLA_INT2}[case.kv_dtype]
     table = np.where(case.block_table >= 0, case.block_table, 0).astype(np.int32)
     return dict(q_lat=q(case.q_lat, device), q_rope=q(case.q_rope, device), kv_cache=cache,
                 block_table=torch.from_numpy(table).to(device),

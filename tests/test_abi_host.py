@@ -140,3 +140,13 @@ def test_prefill_and_expand_argument_validation():
     assert L.mla_expand_kv(FAKE, 100, FAKE, FAKE, FAKE, FAKE, 4, 128, 512, 128, 1, 1, 1, None) == INVALID
     assert L.mla_expand_kv(FAKE, 512, FAKE, FAKE, FAKE, FAKE, 4, 128, 512, 100, 1, 1, 1, None) == UNSUPPORTED
     assert L.mla_expand_kv(FAKE + 2, 512, FAKE, FAKE, FAKE, FAKE, 4, 128, 512, 128, 1, 1, 1, None) == MISALIGNED
+
+
+def test_int_cache_argument_validation():
+    """Low-bit kv dtypes need d_c and d_r in multiples of the 32-value group."""
+    L = binding.lib()
+    args = lambda kv, d_c, d_r: (FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 1, 8, d_c, d_r, 64, 0.1, 1, kv, 1, 0,
+                                 FAKE, 1 << 30, FAKE, None, 0, None)
+    assert L.mla_decode_absorbed(*args(5, 128, 32)) == INVALID
+    assert L.mla_decode_absorbed(*args(binding.MLA_INT4, 112, 32)) == UNSUPPORTED
+    assert L.mla_decode_absorbed(*args(binding.MLA_INT2, 128, 16)) == UNSUPPORTED

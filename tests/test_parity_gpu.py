@@ -118,6 +118,34 @@ def test_v3_fp8_cache_sq2(force_generic):
         assert_lse_close(gl, ol, "lse")
 
 
+@pytest.mark.parametrize("kv", ["int4", "int2"])
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_v3_int_cache(kv, s_q):
+    """Low-bit caches (grouped fp16 scale/min, packed codes) against the
+    oracle's decoding of the same bytes."""
+    say(f"v3 {kv} s_q={s_q}")
+    lens = np.array([2, 33, 64, 129, 1500], dtype=np.int32)
+    case = inputs.decode_case(26 + s_q, B=len(lens), seq_lens=lens, s_q=s_q, kv_dtype=kv, **V3)
+    o, ol = oracle.mqa_decode_case(case)
+    for splits in (0, 3):
+        g, gl = run_decode(case, num_splits=splits)
+        assert_bf16_close(g, o, f"{kv} splits={splits}")
+        assert_lse_close(gl, ol, "lse")
+
+
+@pytest.mark.parametrize("kv", ["int4", "int2"])
+def test_toy_int_cache_fp32_queries(kv):
+    """fp32 queries at the toy dimensions (n_h 8, d_c 128, d_r 32): the
+    dequantised values are exact in fp32, so the fp32 bar applies."""
+    say(f"toy {kv} fp32 queries")
+    case = inputs.decode_case(31, B=3, seq_lens=np.array([1, 70, 200]), s_q=1, n_h=8, d_c=128, d_r=32, d_h=64,
+                              kv_dtype=kv, q_dtype="f32")
+    g, gl = run_decode(case, num_splits=2)
+    o, ol = oracle.mqa_decode_case(case)
+    assert_f32_close(g, o, f"toy {kv}")
+    assert np.max(np.abs(gl - ol)) <= 1e-5
+
+
 def test_mfma_matches_generic_kernel():
     """The two kernels agree closely with each other (both fp32 accumulation)."""
     say("mfma vs generic")
