@@ -41,7 +41,7 @@ struct DecodeShape {
 };
 
 bool mfma_eligible(const DecodeShape& s, int q_dtype, int kv_dtype) {
-  return q_dtype == MLA_BF16 && (kv_dtype == MLA_BF16 || kv_dtype == MLA_FP8_E4M3) && s.n_h == 128 &&
+  return q_dtype == MLA_BF16 && kv_dtype >= MLA_BF16 && kv_dtype <= MLA_INT2 && s.n_h == 128 &&
          s.d_c == 512 && s.d_r == 64 && s.block_size == 64;
 }
 

@@ -52,11 +52,65 @@ constexpr int kF8ScaleOff = kF8Stages3 * kF8StageB;         // 61440
 constexpr int kF8SlotOff = kF8ScaleOff + kF8ScaleSlots * 128;  // 62464
 constexpr int kF8QrOff = kF8SlotOff + 2 * kTileB;           // 136192
 constexpr int kF8TabOff = kF8QrOff + kHeads * kQrStride;    // 154624
-constexpr int kPipeTabOff(bool fp8) { return fp8 ? kF8TabOff : kB16TabOff; }
-constexpr int kPipeLds(bool fp8) { return kPipeTabOff(fp8) + kMaxUnitPages * 4; }  // 149504 / 156672
+// low-bit caches (int4 / int2 content, int4 RoPE; groups of 32 values with
+// an fp16 (scale, min) pair): 3 staging stages of [content codes | RoPE codes
+// | parameters] per subtile, expanded into two bf16 tile slots like fp8
+constexpr int kFmtBf16 = 0, kFmtFp8 = 1, kFmtInt4 = 2, kFmtInt2 = 3;
+constexpr int kIntCodeB(int fmt) { return fmt == kFmtInt4 ? kSub * kDc / 2 : kSub * kDc / 4; }  // 8192 / 4096
+constexpr int kIntRopeB = kSub * kDr / 2;                    // 1024
+constexpr int kIntGroups = (kDc + kDr) / 32;                 // 18 per token
+constexpr int kIntPrmRow = kIntGroups * 4;                   // 72 bytes of parameters per token
+constexpr int kIntPrmB = kSub * kIntPrmRow;                  // 2304
+constexpr int kIntMiscChunks = (kIntRopeB + kIntPrmB) / 16;  // 208 16-byte chunks: RoPE codes + parameters
+constexpr int kIntStageB(int fmt) { return kIntCodeB(fmt) + kIntRopeB + kIntPrmB; }  // 11520 / 7424
+constexpr int kIntStages3 = 3;
+constexpr int kIntSlotOff(int fmt) { return kIntStages3 * kIntStageB(fmt); }
+constexpr int kIntTabOff(int fmt) { return kIntSlotOff(fmt) + 2 * kTileB; }
+constexpr int kIntDma(int fmt) { return kIntCodeB(fmt) / 4096 + 1; }  // content instructions + 1
+constexpr int kPipeTabOff(int fmt) {
+  return fmt == kFmtBf16 ? kB16TabOff : fmt == kFmtFp8 ? kF8TabOff : kIntTabOff(fmt);
+}
 constexpr int kOutRowF = kDc + 4;                           // padded fp32 row of the output staging
 constexpr int kOutRowH = kDc * 2 + 16;                      // padded bf16 row (bytes)
-static_assert(kPipeLds(true) <= 160 * 1024, "LDS budget");
+// the finalize stages 64 fp32 rows or 128 bf16 rows through LDS (after every
+// tile, staging slot and page id of the unit is consumed)
+constexpr int kOutStageB = 64 * kOutRowF * 4 > kHeads * kOutRowH ? 64 * kOutRowF * 4 : kHeads * kOutRowH;
+constexpr int kPipeLds(int fmt) {
+  return kPipeTabOff(fmt) + kMaxUnitPages * 4 > kOutStageB ? kPipeTabOff(fmt) + kMaxUnitPages * 4 : kOutStageB;
+}
+static_assert(kPipeLds(kFmtFp8) <= 160 * 1024 && kPipeLds(kFmtInt4) <= 160 * 1024, "LDS budget");
+static_assert(kIntMiscChunks <= 256, "one misc DMA instruction per thread");
+
+// fp16 (scale, min) pair of a group, packed in one dword
+__device__ __forceinline__ void int_params(uint32_t pr, float& sc, float& mn) {
+  sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(pr & 0xffffu));
+  mn = (float)__builtin_bit_cast(_Float16, (uint16_t)(pr >> 16));
+}
+__device__ __forceinline__ float ubyte_f(uint32_t x, int k) { return (float)((x >> (8 * k)) & 0xffu); }
+// one packed word of 8 int4 codes (value 2k at bit 4k, 2k+1 at bit 16+4k) ->
+// 8 bf16 values code*sc + mn in value order.  Masking the low / high nibbles
+// leaves whole bytes (the high ones 16x the code) for byte-to-float converts.
+__device__ __forceinline__ u32x4_t int4_word_bf16(uint32_t wd, float sc, float mn) {
+  const uint32_t lo = wd & 0x0F0F0F0Fu, hi = wd & 0xF0F0F0F0u;
+  const float s16 = sc * 0.0625f;
+  u32x4_t o;
+  o[0] = pack_bf16x2(__builtin_fmaf(ubyte_f(lo, 0), sc, mn), __builtin_fmaf(ubyte_f(lo, 2), sc, mn));
+  o[1] = pack_bf16x2(__builtin_fmaf(ubyte_f(hi, 0), s16, mn), __builtin_fmaf(ubyte_f(hi, 2), s16, mn));
+  o[2] = pack_bf16x2(__builtin_fmaf(ubyte_f(lo, 1), sc, mn), __builtin_fmaf(ubyte_f(lo, 3), sc, mn));
+  o[3] = pack_bf16x2(__builtin_fmaf(ubyte_f(hi, 1), s16, mn), __builtin_fmaf(ubyte_f(hi, 3), s16, mn));
+  return o;
+}
+// one packed word of 16 int2 codes (value 2k at bit 2k, 2k+1 at bit 16+2k)
+// -> values 0..7 (a) and 8..15 (b) as bf16
+__device__ __forceinline__ void int2_word_bf16(uint32_t wd, float sc, float mn, u32x4_t& a, u32x4_t& b) {
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {  // bit pair f of every byte: codes x 4^f
+    const uint32_t mk = wd & (0x03030303u << (2 * f));
+    const float sf = sc * (f == 0 ? 1.f : f == 1 ? 0.25f : f == 2 ? 0.0625f : 0.015625f);
+    a[f] = pack_bf16x2(__builtin_fmaf(ubyte_f(mk, 0), sf, mn), __builtin_fmaf(ubyte_f(mk, 2), sf, mn));
+    b[f] = pack_bf16x2(__builtin_fmaf(ubyte_f(mk, 1), sf, mn), __builtin_fmaf(ubyte_f(mk, 3), sf, mn));
+  }
+}
 
 // s_waitcnt vmcnt for "at most n DMA groups of G instructions still in flight"
 template <int G>
@@ -71,13 +125,16 @@ __device__ __forceinline__ void wait_dma_groups(int n) {
     wait_vm<0>();
 }
 
-template <bool FP8>
+template <int FMT>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_pipe_kernel(DecodeArgs a) {
+  constexpr bool FP8 = FMT == kFmtFp8;      // per-token scaled e4m3 content codes
+  constexpr bool INT = FMT >= kFmtInt4;     // grouped low-bit codes
+  constexpr bool STAGED = FMT != kFmtBf16;  // codes staged, expanded into bf16 tile slots
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
-  lds_i32* tab = (lds_i32*)(smem + kPipeTabOff(FP8));
-  constexpr int kDma = FP8 ? kF8Dma : kBf16Dma;       // DMA instructions per wave per subtile
+  lds_i32* tab = (lds_i32*)(smem + kPipeTabOff(FMT));
+  constexpr int kDma = FP8 ? kF8Dma : INT ? kIntDma(FMT) : kBf16Dma;  // DMA instructions per wave per subtile
   constexpr int kAhead = 2;                           // subtiles in flight beyond the next one
   constexpr int kQReg = FP8 ? 32 : 36;                // query fragments held in registers
 
@@ -163,15 +220,32 @@ void decode_pipe_kernel(DecodeArgs a) {
     auto page_rsrc = [&](int s) {
       const int pg = __builtin_amdgcn_readfirstlane(tab[s >> 1]);
       const uint8_t* blk = (const uint8_t*)a.kv + (long long)pg * a.block_bytes;
-      return make_rsrc(FP8 ? blk : blk + (s & 1) * kTileB);
+      return make_rsrc(STAGED ? blk : blk + (s & 1) * kTileB);
     };
     auto dma_dst = [&](int s) {  // LDS base (scalar) of subtile s's DMA landing area for this wave
       return __builtin_amdgcn_readfirstlane(
-          (int)(uint32_t)(uintptr_t)(smem + (FP8 ? (s % kF8Stages3) * kF8StageB : (s % kB16Stages) * kTileB)));
+          (int)(uint32_t)(uintptr_t)(smem + (FP8   ? (s % kF8Stages3) * kF8StageB
+                                             : INT ? (s % kIntStages3) * kIntStageB(FMT)
+                                                   : (s % kB16Stages) * kTileB)));
     };
     auto dma_one = [&](const i32x4_t& rs, int m0b, int s, int i) {
-      if (!FP8) {
+      if (!STAGED) {
         dma16_m0(rs, dma_src_offset(i * 256 + tid), m0b + i * 4096 + w_s * 1024);
+      } else if (INT) {
+        // block: [64 x content codes | 64 x RoPE codes | 64 x parameters];
+        // subtile half s & 1 of each part
+        constexpr int cb = kIntCodeB(FMT);
+        const int half = s & 1;
+        if (i < kDma - 1) {  // content codes, 4 KB per instruction
+          dma16_m0(rs, half * cb + ((i * 4 + w) * 64 + lane) * 16, m0b + (i * 4 + w_s) * 1024);
+        } else {  // RoPE codes (64 chunks) then parameters (144 chunks), one per thread
+          const int p = tid;
+          if (p < kIntMiscChunks) {
+            const int src = p < kIntRopeB / 16 ? 2 * cb + half * kIntRopeB + p * 16
+                                               : 2 * cb + 2 * kIntRopeB + half * kIntPrmB + (p - kIntRopeB / 16) * 16;
+            dma16_m0(rs, src, m0b + cb + w_s * 1024);
+          }
+        }
       } else {
         const int half = s & 1;
         if (i < 4) {         // content codes: 16 KB, 4 x 1 KB per wave
@@ -192,11 +266,79 @@ void decode_pipe_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < kDma; ++i) dma_one(rs, m0b, s, i);
     };
-    auto tile_of = [&](int s) { return smem + (FP8 ? kF8SlotOff + (s & 1) * kTileB : (s % kB16Stages) * kTileB); };
+    auto tile_of = [&](int s) {
+      return smem + (FP8 ? kF8SlotOff + (s & 1) * kTileB
+                         : INT ? kIntSlotOff(FMT) + (s & 1) * kTileB : (s % kB16Stages) * kTileB);
+    };
     // per-token scales of subtile s for this lane's rows 8qd + 4g + 0..3
     auto scales_of = [&](int s, int qd) {
       return *(const __attribute__((address_space(3))) f32x4_t*)(smem + kF8ScaleOff + (s % kF8ScaleSlots) * 128 +
                                                                   16 * g + 32 * qd);
+    };
+    // int4 / int2: expand staged subtile s into its bf16 tile slot (rows past
+    // nv -> 0).  A job is one 16-byte chunk of codes: int4 content 2 per
+    // thread (32 values, one group each), int2 content 1 per thread (64
+    // values, two groups); the 64 RoPE chunks (int4, one group each) go to
+    // the first 64 threads.  All LDS reads are issued before any conversion.
+    auto convert_int = [&](int s, int nv) {
+      constexpr int cbits = FMT == kFmtInt4 ? 4 : 2;
+      constexpr int rowC = kDc * cbits / 8;      // content code bytes per token
+      constexpr int cpr = rowC / 16;             // code chunks per token
+      constexpr int nj = kSub * cpr / 256;       // content jobs per thread
+      const lds_u8* st = smem + (s % kIntStages3) * kIntStageB(FMT);
+      const lds_u8* prm = st + kIntCodeB(FMT) + kIntRopeB;
+      lds_u8* tl = smem + kIntSlotOff(FMT) + (s & 1) * kTileB;
+      typedef __attribute__((address_space(3))) u32x4_t lds_u4;
+      typedef __attribute__((address_space(3))) u32x2_t lds_u2;
+      typedef __attribute__((address_space(3))) uint32_t lds_u1;
+      u32x4_t cw[nj];
+      u32x2_t pw[nj];
+#pragma unroll
+      for (int i = 0; i < nj; ++i) {
+        const int job = tid + 256 * i, t = job / cpr, j = job % cpr;
+        cw[i] = *(const lds_u4*)(st + t * rowC + j * 16);
+        if (cbits == 4)
+          pw[i][0] = *(const lds_u1*)(prm + t * kIntPrmRow + j * 4);
+        else
+          pw[i] = *(const lds_u2*)(prm + t * kIntPrmRow + j * 8);
+      }
+      const int tr = tid >> 1, jr = tid & 1;  // RoPE job of threads 0..63
+      u32x4_t rw = {0, 0, 0, 0};
+      uint32_t rp = 0;
+      if (tid < 64) {
+        rw = *(const lds_u4*)(st + kIntCodeB(FMT) + tr * (kDr / 2) + jr * 16);
+        rp = *(const lds_u1*)(prm + tr * kIntPrmRow + (kDc / 32 + jr) * 4);
+      }
+      auto put = [&](int t, int c, const u32x4_t& v) {  // logical bf16 chunk c of row t
+        *(__attribute__((address_space(3))) u32x4_t*)(tl + t * kRowB + ((c ^ swz_f(t)) << 4)) =
+            t < nv ? v : u32x4_t{0, 0, 0, 0};
+      };
+#pragma unroll
+      for (int i = 0; i < nj; ++i) {
+        const int job = tid + 256 * i, t = job / cpr, j = job % cpr;
+        if (cbits == 4) {
+          float sc, mn;
+          int_params(pw[i][0], sc, mn);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) put(t, 4 * j + k, int4_word_bf16(cw[i][k], sc, mn));
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float sc, mn;
+            int_params(pw[i][k >> 1], sc, mn);
+            u32x4_t va, vb;
+            int2_word_bf16(cw[i][k], sc, mn, va, vb);
+            put(t, 8 * j + 2 * k, va);
+            put(t, 8 * j + 2 * k + 1, vb);
+          }
+        }
+      }
+      if (tid < 64) {
+        float sc, mn;
+        int_params(rp, sc, mn);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) put(tr, kDc / 8 + 4 * jr + k, int4_word_bf16(rw[k], sc, mn));
+      }
     };
     // fp8: expand staged subtile s into its bf16 tile slot (rows past nv -> 0).
     // Each lane takes 16 codes (one 16-byte read) of row t = 8i + 2w + g per
@@ -204,6 +346,10 @@ void decode_pipe_kernel(DecodeArgs a) {
     // are issued before any conversion.  e4m3 -> bf16 with a unit scale is
     // exact.
     auto convert = [&](int s, int nv) {
+      if constexpr (INT) {
+        convert_int(s, nv);
+        return;
+      }
       const lds_u8* st = smem + (s % kF8Stages3) * kF8StageB;
       lds_u8* tl = smem + kF8SlotOff + (s & 1) * kTileB;
       const int c0 = 2 * l32;  // first of the lane's two 8-code chunks
@@ -258,7 +404,7 @@ void decode_pipe_kernel(DecodeArgs a) {
         if (s < n_sub) issue(s);
       wait_dma_groups<kDma>(min(kAhead, n_sub - 1));
       __syncthreads();
-      if (FP8) {
+      if (STAGED) {
         convert(0, nvalid_of(0));
         __syncthreads();
       } else if (n_last < kSub && n_sub == 1) {
@@ -422,7 +568,7 @@ void decode_pipe_kernel(DecodeArgs a) {
       // ---- (A) next subtile resident; refill the stage subtile it-1 used
       wait_dma_groups<kDma>(min(kAhead - 1, n_sub - 2 - it));
       __syncthreads();
-      if (FP8) {  // expand subtile it+1 into the slot subtile it-1 used
+      if (STAGED) {  // expand subtile it+1 into the slot subtile it-1 used
         convert(it + 1, nvalid_of(it + 1));
         __syncthreads();
       } else if (it + 1 == n_sub - 1 && n_last < kSub) {
@@ -570,21 +716,27 @@ void decode_pipe_kernel(DecodeArgs a) {
   }
 }
 
-template <bool FP8>
+template <int FMT>
 static hipError_t launch_pipe(const DecodeArgs& a, int grid_x, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_pipe_kernel<FP8>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kPipeLds(FP8));
+    hipError_t e = hipFuncSetAttribute((const void*)decode_pipe_kernel<FMT>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kPipeLds(FMT));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(decode_pipe_kernel<FP8>, dim3(grid_x, a.s_q), dim3(256), kPipeLds(FP8), s, a);
+  hipLaunchKernelGGL(decode_pipe_kernel<FMT>, dim3(grid_x, a.s_q), dim3(256), kPipeLds(FMT), s, a);
   return hipGetLastError();
 }
 
+// kv dtype codes: 1 bf16, 2 fp8, 3 int4, 4 int2
 hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t s) {
-  return a.kv_dtype == 2 ? launch_pipe<true>(a, grid_x, s) : launch_pipe<false>(a, grid_x, s);
+  switch (a.kv_dtype) {
+    case 2: return launch_pipe<kFmtFp8>(a, grid_x, s);
+    case 3: return launch_pipe<kFmtInt4>(a, grid_x, s);
+    case 4: return launch_pipe<kFmtInt2>(a, grid_x, s);
+    default: return launch_pipe<kFmtBf16>(a, grid_x, s);
+  }
 }
 
 int mfma_max_unit_pages() { return kMaxUnitPages; }
