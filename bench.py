@@ -254,10 +254,11 @@ def main() -> int:
 
     if case.kv_dtype == "bf16":
         base = bf(case.cache)
-        kv_dtype = binding.MLA_BF16
     else:
         base = torch.from_numpy(np.ascontiguousarray(case.cache)).to(dev)
-        kv_dtype = binding.MLA_FP8_E4M3
+    kv_dtype = {"bf16": binding.MLA_BF16, "fp8": binding.MLA_FP8_E4M3, "int4": binding.MLA_INT4,
+                "int2": binding.MLA_INT2}[case.kv_dtype]
+    fmt = {"bf16": 0, "fp8": 1, "int4": 2, "int2": 3}[case.kv_dtype]  # the kernel's template argument
     caches = [base] + [base.clone() for _ in range(max(0, args.copies - 1))]
     table = torch.from_numpy(np.maximum(case.block_table, 0).astype(np.int32)).to(dev)
     lens = torch.from_numpy(case.seq_lens.astype(np.int32)).to(dev)
@@ -364,12 +365,11 @@ def main() -> int:
         achieved = latent_bytes / (kernel_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
-        kname = "decode_pipe_kernel<false>"
     else:
         achieved = flops / (kernel_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_MFMA_PEAK_TFLOPS}
-        kname = "decode_pipe_kernel<true>"
+    kname = f"decode_pipe_kernel<{fmt}>"
     roof["traffic"] = measured_traffic(args.workload)
     roof["kernel"] = kname
     roof["kernel_ms"] = kernel_ms
@@ -379,8 +379,9 @@ def main() -> int:
     rec = {
         "metric": METRIC, "value": value, "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if case.kv_dtype == "bf16" else "fp8e4m3+bf16",
-        "data": "synthetic: seeded PCG64 N(0,1) latent cache rounded to bf16 (fp8: per-token amax/448 e4m3fn), "
+        "vs_baseline": None, "dtype": {"bf16": "bf16", "fp8": "fp8e4m3+bf16", "int4": "int4+bf16", "int2": "int2/int4+bf16"}[case.kv_dtype],
+        "data": "synthetic: seeded PCG64 N(0,1) latent cache rounded to bf16 (fp8: per-token amax/448 e4m3fn; "
+                "int4/int2: groups of 32 with fp16 scale and min), "
                 "q_lat N(0,1/512) from W^UK absorption, shuffled 64-token pages",
         "config": {"workload": args.workload, "n_h": n_h, "d_c": d_c, "d_r": d_r, "d_h": d_h, "B": B,
                    "s_q": s_q, "ctx": int(case.seq_lens.max()) if w["lens"][0] == "fixed" else "log-uniform",
