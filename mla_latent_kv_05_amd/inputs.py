@@ -337,6 +337,72 @@ def decode_case(seed: int, B: int, seq_lens, s_q: int = 1, n_h: int = 128,
                       num_blocks=num_blocks)
 
 
+@dataclass
+class GqaCase:
+    """Paged GQA-path decode inputs (GQLA's per-group expanded cache)."""
+    B: int
+    s_q: int
+    n_h: int
+    n_g: int
+    d_h: int
+    d_r: int
+    block_size: int
+    kv_dtype: str               # "bf16" | "f32"
+    q_dtype: str
+    seq_lens: np.ndarray        # [B] int32
+    block_table: np.ndarray     # [B, max_blocks] int32 (-1 unused)
+    cache: np.ndarray           # [num_blocks, block elements] (uint16 bf16 bits or float32)
+    q_c: np.ndarray             # [B, s_q, n_h, d_h]
+    q_r: np.ndarray             # [B, s_q, n_h, d_r]
+    softmax_scale: float
+    num_blocks: int
+
+    @property
+    def row_bytes(self) -> int:
+        return (2 * self.n_g * self.d_h + self.d_r) * (2 if self.kv_dtype == "bf16" else 4)
+
+    @property
+    def cache_bytes_read(self) -> int:
+        return int(self.seq_lens.astype(np.int64).sum()) * self.row_bytes
+
+
+def gqa_case(seed: int, B: int, seq_lens, s_q: int = 2, n_h: int = 128, n_g: int = 8, d_h: int = 128,
+             d_r: int = 64, kv_dtype: str = "bf16", q_dtype: str = "bf16", block_size: int = BLOCK) -> GqaCase:
+    """GQA-path inputs: per block of block_size tokens the cache holds
+    [n_g][block_size][d_h] k^C | [n_g][block_size][d_h] v^C | [block_size][d_r] k^R.
+    k^C, v^C ~ N(0,1) (the per-group expansion of a unit-variance latent with
+    fan-in-scaled weights), k^R ~ N(0,1), q^C, q^R ~ N(0,1), so the scores
+    scaled by 1/sqrt(d_h + d_r) have unit variance.  Physical blocks are one
+    seeded permutation handed out in (sequence, logical block) order."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = np.full(B, seq_lens, dtype=np.int32) if np.isscalar(seq_lens) else np.asarray(seq_lens, dtype=np.int32)
+    assert lens.shape == (B,) and (lens >= s_q).all() and n_h % n_g == 0
+    nblk = (lens + block_size - 1) // block_size
+    num_blocks = int(nblk.sum())
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    table = np.full((B, int(nblk.max())), -1, dtype=np.int32)
+    k = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[k:k + nblk[b]]
+        k += nblk[b]
+    E = block_size * (2 * n_g * d_h + d_r)
+    kind = "f32" if (kv_dtype != "f32" and q_dtype != "f32") else "f64"
+    cache = np.empty((num_blocks, E), dtype=np.uint16 if kv_dtype == "bf16" else np.float32)
+    for i0 in range(0, num_blocks, 16):
+        i1 = min(num_blocks, i0 + 16)
+        vals = _draw(rng, (i1 - i0, E), 1.0, kind)
+        cache[i0:i1] = f32_to_bf16_bits(vals) if kv_dtype == "bf16" else vals
+    qc = _draw(rng, (B, s_q, n_h, d_h), 1.0, kind)
+    qr = _draw(rng, (B, s_q, n_h, d_r), 1.0, kind)
+    if q_dtype == "bf16":
+        qc, qr = f32_to_bf16_bits(qc), f32_to_bf16_bits(qr)
+    else:
+        qc, qr = qc.astype(np.float32), qr.astype(np.float32)
+    return GqaCase(B=B, s_q=s_q, n_h=n_h, n_g=n_g, d_h=d_h, d_r=d_r, block_size=block_size, kv_dtype=kv_dtype,
+                   q_dtype=q_dtype, seq_lens=lens, block_table=table, cache=cache, q_c=qc, q_r=qr,
+                   softmax_scale=1.0 / math.sqrt(d_h + d_r), num_blocks=num_blocks)
+
+
 def projection_weights(seed: int, T_q: int, n_h: int = 128, d_h: int = 128,
                        d_c: int = 512, dtype: str = "bf16") -> dict:
     """Inputs for the query absorption and the W^UV up-projection at V3 shapes.

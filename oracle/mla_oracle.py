@@ -54,6 +54,9 @@ codes) are a reading as well -- the pages name only the bit widths -- and are
 parity unpinned with respect to the pages; the decoder is pinned by
 hand-written byte fixtures and by the quantisation error bound of a
 separately written encoder.
+GQLA's GQA path (gqa_decode_rows) is pinned by its algebraic equality with
+the MQA-absorb path over the same weights (the page's claim) and by torch's
+scaled_dot_product_attention with grouped key/value heads.
 The cache producer (cache_append) is pinned by an element-by-element
 brute force with complex-number rotation, by torch's own bf16 and fp8
 casts for its encoders, and by appending a toy layer's tokens and decoding
@@ -294,6 +297,69 @@ def mha_mode_layer(h, W, pos):
         o[b], lse[b] = mha_attention(q_c[b], q_r[b], k_c[b], k_r[b], v_c[b], scale)
     u = o.reshape(B, T, n_h * d_h) @ np.asarray(W["w_o"], dtype=np.float64).T
     return {"u": u, "o": o, "lse": lse, "c_kv": c_kv, "k_r": k_r, "q_c": q_c, "q_r": q_r}
+
+
+# --------------------------------------------------------------------------
+# GQLA: the GQA decode path over a per-group expanded cache
+# --------------------------------------------------------------------------
+# The GQLA page (abstract) describes weights whose up-projections are shared
+# by groups of heads, so the same parameters decode either in MQA-absorb form
+# over the latent (as MLA) or in GQA form over a cache expanded per group.
+# Reading: n_g groups of n_h / n_g consecutive heads; group g has W^UK_g,
+# W^UV_g (rows g*d_h .. of [n_g*d_h, d_c]); the RoPE key stays shared; the
+# GQA cache holds k^C_{j,g} = W^UK_g c_j, v^C_{j,g} = W^UV_g c_j and k^R_j.
+
+
+def gqa_decode_rows(q_c, q_r, k_c, v_c, k_r, scale, n_g):
+    """GQA-path decode of one sequence: q_c [s_q, n_h, d_h], q_r [s_q, n_h, d_r],
+    k_c / v_c [L, n_g, d_h], k_r [L, d_r].  Head h reads group h // (n_h / n_g);
+    query i sits at L - s_q + i and sees keys 0 .. L - s_q + i.
+    Returns o [s_q, n_h, d_h] and lse [s_q, n_h]."""
+    q_c, q_r, k_c, v_c, k_r = (np.asarray(a, dtype=np.float64) for a in (q_c, q_r, k_c, v_c, k_r))
+    s_q, n_h = q_c.shape[:2]
+    L = k_c.shape[0]
+    hpg = n_h // n_g
+    o = np.zeros((s_q, n_h, v_c.shape[-1]))
+    lse = np.empty((s_q, n_h))
+    for h in range(n_h):
+        g = h // hpg
+        s = (q_c[:, h] @ k_c[:, g].T + q_r[:, h] @ k_r.T) * scale        # [s_q, L]
+        vis = np.arange(L)[None, :] <= (L - s_q + np.arange(s_q))[:, None]
+        p, lse[:, h] = _softmax_rows(np.where(vis, s, -np.inf))
+        o[:, h] = p @ v_c[:, g]
+    return o, lse
+
+
+def gqa_paged_rows(cache, block_table_row, L, n_g, d_h, d_r, block_size, kv_dtype="bf16"):
+    """Logical rows of a paged GQA cache.  Per block of block_size tokens:
+    [n_g][block_size][d_h] k^C | [n_g][block_size][d_h] v^C | [block_size][d_r]
+    k^R (bf16 bits or fp32).  Returns k_c, v_c [L, n_g, d_h], k_r [L, d_r]."""
+    k_c, v_c = np.empty((L, n_g, d_h)), np.empty((L, n_g, d_h))
+    k_r = np.empty((L, d_r))
+    dec = bf16_to_f64 if kv_dtype == "bf16" else (lambda a: np.asarray(a, dtype=np.float64))
+    n1 = n_g * block_size * d_h
+    for j in range(0, L, block_size):
+        n = min(block_size, L - j)
+        blk = dec(np.asarray(cache[int(block_table_row[j // block_size])]).reshape(-1))
+        k_c[j:j + n] = blk[:n1].reshape(n_g, block_size, d_h)[:, :n].transpose(1, 0, 2)
+        v_c[j:j + n] = blk[n1:2 * n1].reshape(n_g, block_size, d_h)[:, :n].transpose(1, 0, 2)
+        k_r[j:j + n] = blk[2 * n1:2 * n1 + block_size * d_r].reshape(block_size, d_r)[:n]
+    return k_c, v_c, k_r
+
+
+def gqla_absorbed_rows(q_c, q_r, c, k_r, w_uk, w_uv, scale, n_g):
+    """The MQA-absorb path of the same GQLA weights: head h absorbs its
+    group's W^UK into the query, decodes over the latent c [L, d_c], and
+    applies its group's W^UV.  Returns o [s_q, n_h, d_h], lse [s_q, n_h]."""
+    q_c = np.asarray(q_c, dtype=np.float64)
+    s_q, n_h, d_h = q_c.shape
+    hpg = n_h // n_g
+    w_uk = np.asarray(w_uk, dtype=np.float64).reshape(n_g, d_h, -1)
+    w_uv = np.asarray(w_uv, dtype=np.float64).reshape(n_g, d_h, -1)
+    grp = np.arange(n_h) // hpg
+    q_lat = np.einsum("ihk,hkc->ihc", q_c, w_uk[grp])
+    o_lat, lse = mqa_decode_rows(q_lat, q_r, c, k_r, scale)
+    return np.einsum("hkc,ihc->ihk", w_uv[grp], o_lat), lse
 
 
 # --------------------------------------------------------------------------

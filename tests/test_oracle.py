@@ -562,3 +562,62 @@ def test_expand_kv_per_head_blocks():
             for e in range(d_h):
                 assert abs(k_c[t, i, e] - sum(wk[i * d_h + e, j] * c[t, j] for j in range(d_c))) <= 1e-12
                 assert abs(v_c[t, i, e] - sum(wv[i * d_h + e, j] * c[t, j] for j in range(d_c))) <= 1e-12
+
+
+# ---------------------------------------------------------------- GQLA GQA path
+
+def _gqla_small(seed=0, s_q=2, n_h=8, n_g=2, d_h=16, d_c=24, d_r=8, L=37):
+    rng = np.random.default_rng(seed)
+    return dict(q_c=rng.standard_normal((s_q, n_h, d_h)), q_r=rng.standard_normal((s_q, n_h, d_r)),
+                c=rng.standard_normal((L, d_c)), k_r=rng.standard_normal((L, d_r)),
+                w_uk=rng.standard_normal((n_g * d_h, d_c)) / math.sqrt(d_c),
+                w_uv=rng.standard_normal((n_g * d_h, d_c)) / math.sqrt(d_c), n_g=n_g, d_h=d_h,
+                scale=1.0 / math.sqrt(d_h + d_r))
+
+
+@pytest.mark.parametrize("s_q,L,n_g", [(1, 1, 2), (2, 37, 2), (2, 64, 4), (3, 10, 1), (2, 20, 8)])
+def test_gqa_path_equals_absorbed_path(s_q, L, n_g):
+    """The GQLA page: one set of weights, two algebraically equal decode
+    paths.  The GQA path over k^C = W^UK_g c, v^C = W^UV_g c equals the
+    MQA-absorb path over the latent, to float64 rounding."""
+    X = _gqla_small(seed=L + n_g, s_q=s_q, n_g=n_g, L=L)
+    k_c, v_c = oracle.expand_kv(X["c"], X["w_uk"], X["w_uv"], n_g, X["d_h"])
+    o1, l1 = oracle.gqa_decode_rows(X["q_c"], X["q_r"], k_c, v_c, X["k_r"], X["scale"], n_g)
+    o2, l2 = oracle.gqla_absorbed_rows(X["q_c"], X["q_r"], X["c"], X["k_r"], X["w_uk"], X["w_uv"], X["scale"], n_g)
+    assert np.max(np.abs(o1 - o2)) <= 1e-13 * np.max(np.abs(o1))
+    assert np.max(np.abs(l1 - l2)) <= 1e-13
+
+
+@pytest.mark.parametrize("s_q,L", [(1, 5), (2, 37)])
+def test_gqa_path_matches_torch_sdpa_grouped(s_q, L):
+    X = _gqla_small(seed=3 * L, s_q=s_q, L=L, n_g=2)
+    k_c, v_c = oracle.expand_kv(X["c"], X["w_uk"], X["w_uv"], 2, X["d_h"])
+    o, lse = oracle.gqa_decode_rows(X["q_c"], X["q_r"], k_c, v_c, X["k_r"], X["scale"], 2)
+    q = torch.from_numpy(np.concatenate([X["q_c"], X["q_r"]], -1)).permute(1, 0, 2)[None]       # [1, n_h, s_q, 24]
+    kr = np.broadcast_to(X["k_r"][:, None], (L, 2, X["k_r"].shape[1]))
+    k = torch.from_numpy(np.ascontiguousarray(np.concatenate([k_c, kr], -1))).permute(1, 0, 2)[None]  # [1, n_g, L, 24]
+    v = torch.from_numpy(v_c).permute(1, 0, 2)[None]
+    mask = torch.arange(L)[None, :] <= torch.arange(L - s_q, L)[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=X["scale"],
+                                                           enable_gqa=True)[0].permute(1, 0, 2).numpy()
+    assert np.max(np.abs(o - ref)) <= 1e-14
+
+
+def test_gqa_paged_layout_brute_force():
+    """gqa_paged_rows against element-by-element placement from the block
+    layout [n_g][bs][d_h] k^C | [n_g][bs][d_h] v^C | [bs][d_r] k^R."""
+    n_g, d_h, d_r, bs, L = 2, 4, 2, 4, 7
+    rng = np.random.default_rng(5)
+    kc, vc, kr = rng.standard_normal((L, n_g, d_h)), rng.standard_normal((L, n_g, d_h)), rng.standard_normal((L, d_r))
+    table = [1, 0]
+    cache = np.full((2, bs * (2 * n_g * d_h + d_r)), np.nan)
+    for j in range(L):
+        blk, t = table[j // bs], j % bs
+        for g in range(n_g):
+            for e in range(d_h):
+                cache[blk, (g * bs + t) * d_h + e] = kc[j, g, e]
+                cache[blk, n_g * bs * d_h + (g * bs + t) * d_h + e] = vc[j, g, e]
+        for e in range(d_r):
+            cache[blk, 2 * n_g * bs * d_h + t * d_r + e] = kr[j, e]
+    a, b, c = oracle.gqa_paged_rows(cache, table, L, n_g, d_h, d_r, bs, kv_dtype="f32")
+    assert np.array_equal(a, kc) and np.array_equal(b, vc) and np.array_equal(c, kr)
