@@ -264,6 +264,32 @@ int mla_prefill_mha(const void* q, const void* k_c, const void* k_r, const void*
                     int T, int n_h, int d_h, int d_r, float softmax_scale, int in_dtype, int out_dtype,
                     void* stream);
 
+/* mla_gqa_decode -- GQLA's GQA decode path (chatpaper page on GQLA,
+ * abstract: the same weights decode either in MQA-absorb form, as
+ * mla_decode_absorbed, or in GQA form over a cache expanded per group of
+ * heads).  n_g groups of n_h/n_g consecutive heads; group g's keys and
+ * values are k^C_{j,g} = W^UK_g c_j, v^C_{j,g} = W^UV_g c_j; the RoPE key is
+ * shared:
+ *   s[j] = softmax_scale * (q_c[b,i,h,:] . k^C_{j,g(h)} + q_r[b,i,h,:] . kR_j),
+ *          j <= seq_lens[b] - s_q + i
+ *   o[b,i,h,:] = sum_j softmax(s)[j] v^C_{j,g(h)},  lse[b,i,h] = log sum_j exp(s[j])
+ *
+ *  q_c  [B, s_q, n_h, d_h], q_r [B, s_q, n_h, d_r], dtype q_dtype, contiguous
+ *  kv_cache paged, block_size tokens per block, physical block p at byte
+ *           offset p * block_size * (2*n_g*d_h + d_r) * elem; per block
+ *           [n_g][block_size][d_h] k^C | [n_g][block_size][d_h] v^C |
+ *           [block_size][d_r] k^R, dtype kv_dtype (MLA_BF16 or MLA_F32)
+ *  block_table / seq_lens as for mla_decode_absorbed (1 <= s_q <= seq_lens[b])
+ *  o    [B, s_q, n_h, d_h], dtype out_dtype; lse [B, s_q, n_h] fp32 or NULL
+ *  bf16 with d_h = 128, d_r = 64, block_size = 64, s_q * n_h / n_g = 32 and
+ *  16-byte aligned buffers takes the MFMA kernel (one workgroup per
+ *  (sequence, group), no workspace); everything else (d_h + d_r <= 256) a
+ *  portable fp32 kernel.  flags: MLA_FLAG_FORCE_GENERIC or 0. */
+int mla_gqa_decode(const void* q_c, const void* q_r, const void* kv_cache, const int32_t* block_table,
+                   int max_blocks_per_seq, const int32_t* seq_lens, int B, int s_q, int n_h, int n_g, int d_h,
+                   int d_r, int block_size, float softmax_scale, int q_dtype, int kv_dtype, int out_dtype, void* o,
+                   float* lse, int flags, void* stream);
+
 /* mla_status_string -- static, human-readable text for a status code. */
 const char* mla_status_string(int status);
 

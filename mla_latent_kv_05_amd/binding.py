@@ -42,6 +42,9 @@ _SIGS = {
                                     _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int,
                                     _c.c_int, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "mla_cache_append_workspace_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int]),
+    "mla_gqa_decode": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p,
+                                  _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float,
+                                  _c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
     "mla_expand_kv": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                  _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_void_p]),
     "mla_prefill_mha": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
@@ -230,6 +233,31 @@ def cache_append(h: torch.Tensor, w_dkv_kr: torch.Tensor, positions: torch.Tenso
                                   _ptr(kv_cache), T, d, d_c, d_r, block_size, float(rope_base), _dt(h),
                                   kv_dtype, _ptr(workspace), workspace.numel(), _stream()), "mla_cache_append")
     return kv_cache
+
+
+def gqa_decode(q_c: torch.Tensor, q_r: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+               seq_lens: torch.Tensor, n_g: int, softmax_scale: float, block_size: int = 64,
+               out_dtype: torch.dtype = torch.bfloat16, with_lse: bool = True, force_generic: bool = False,
+               out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """GQLA's GQA-path decode over a paged per-group expanded cache (layout
+    of include/mla_decode.h).  q_c [B, s_q, n_h, d_h], q_r [B, s_q, n_h, d_r].
+    Returns (o [B, s_q, n_h, d_h], lse [B, s_q, n_h] or None)."""
+    _gpu(q_c, q_r, kv_cache, block_table, seq_lens)
+    B, s_q, n_h, d_h = q_c.shape
+    d_r = q_r.shape[-1]
+    assert q_c.is_contiguous() and q_r.is_contiguous() and kv_cache.is_contiguous()
+    assert q_r.shape == (B, s_q, n_h, d_r) and q_r.dtype == q_c.dtype
+    assert block_table.dtype == torch.int32 and block_table.is_contiguous() and block_table.shape[0] == B
+    assert seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)
+    if out is None:
+        out = torch.empty((B, s_q, n_h, d_h), dtype=out_dtype, device=q_c.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, s_q, n_h), dtype=torch.float32, device=q_c.device)
+    _check(lib().mla_gqa_decode(_ptr(q_c), _ptr(q_r), _ptr(kv_cache), _ptr(block_table), block_table.shape[1],
+                                _ptr(seq_lens), B, s_q, n_h, n_g, d_h, d_r, block_size, float(softmax_scale),
+                                _dt(q_c), _dt(kv_cache), _dt(out), _ptr(out), _ptr(lse) if with_lse else None,
+                                MLA_FLAG_FORCE_GENERIC if force_generic else 0, _stream()), "mla_gqa_decode")
+    return out, (lse if with_lse else None)
 
 
 def expand_kv(c_kv: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor, d_h: int,

@@ -152,6 +152,28 @@ int mla_prefill_mha(const void* q, const void* k_c, const void* k_r, const void*
                                       out_dtype, (hipStream_t)stream));
 }
 
+int mla_gqa_decode(const void* q_c, const void* q_r, const void* kv_cache, const int32_t* block_table,
+                   int max_blocks_per_seq, const int32_t* seq_lens, int B, int s_q, int n_h, int n_g, int d_h,
+                   int d_r, int block_size, float softmax_scale, int q_dtype, int kv_dtype, int out_dtype, void* o,
+                   float* lse, int flags, void* stream) {
+  if (B <= 0 || s_q <= 0 || n_h <= 0 || n_g <= 0 || d_h <= 0 || d_r < 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || n_h % n_g != 0)
+    return MLA_ERR_INVALID_ARG;
+  if (flags & ~MLA_FLAG_FORCE_GENERIC) return MLA_ERR_INVALID_ARG;
+  if (!act_dtype_ok(q_dtype) || !act_dtype_ok(kv_dtype) || !act_dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;
+  if (!q_c || !kv_cache || !block_table || !seq_lens || !o || (d_r > 0 && !q_r)) return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return MLA_ERR_INVALID_ARG;
+  if (d_h > 256 || d_h + d_r > 256) return MLA_ERR_UNSUPPORTED;
+  const long long elem = kv_dtype == MLA_F32 ? 4 : 2;
+  const long long block_bytes = (long long)block_size * (2LL * n_g * d_h + d_r) * elem;
+  bool fast = !(flags & MLA_FLAG_FORCE_GENERIC) &&
+              gqa_mfma_eligible(s_q, n_h, n_g, d_h, d_r, block_size, q_dtype, kv_dtype) && aligned16(q_c) &&
+              aligned16(q_r) && aligned16(kv_cache) && aligned16(o);
+  return launch_status(launch_gqa_decode(q_c, q_r, kv_cache, block_table, max_blocks_per_seq, seq_lens, B, s_q, n_h,
+                                         n_g, d_h, d_r, block_size, block_bytes, softmax_scale, q_dtype, kv_dtype,
+                                         o, lse, out_dtype, fast, (hipStream_t)stream));
+}
+
 size_t mla_cache_append_workspace_bytes(int T, int d, int d_c, int d_r) {
   if (T <= 0 || d <= 0 || d_c <= 0 || d_r < 0) return 0;
   return append_workspace_bytes(T, d, d_c, d_r);

@@ -106,6 +106,11 @@ bool expand_gemm_eligible(long long a_st, int N, int K, int out_dtype, const voi
                           const void* w1, const void* o0, const void* o1);
 hipError_t launch_expand_gemm(const void* a, long long a_st, const void* w0, const void* w1, void* o0, void* o1,
                               int T, int N, int K, int out_dtype, hipStream_t s);
+bool gqa_mfma_eligible(int s_q, int n_h, int n_g, int d_h, int d_r, int bs, int q_dt, int kv_dt);
+hipError_t launch_gqa_decode(const void* q_c, const void* q_r, const void* cache, const int32_t* table,
+                             int max_blocks, const int32_t* seq_lens, int B, int s_q, int n_h, int n_g, int d_h,
+                             int d_r, int bs, long long block_bytes, float scale, int q_dt, int kv_dt, void* out,
+                             float* lse, int out_dt, bool mfma, hipStream_t s);
 constexpr int kMaxRopePairs = 64;  // d_r <= 128 for the cache producer
 size_t append_workspace_bytes(int T, int d, int d_c, int d_r);
 hipError_t launch_append(const void* h, long long h_st, const void* w, const int32_t* positions,

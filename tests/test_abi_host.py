@@ -20,7 +20,7 @@ def test_header_functions_exported():
     names = binding.header_functions()
     assert set(names) == {"mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_absorbed",
                           "mla_combine_lse", "mla_up_proj_v", "mla_status_string", "mla_decode_kernel_events",
-                          "mla_cache_append", "mla_cache_append_workspace_bytes", "mla_expand_kv",
+                          "mla_cache_append", "mla_cache_append_workspace_bytes", "mla_expand_kv", "mla_gqa_decode",
                           "mla_prefill_mha"}
     L = binding.lib()
     for n in names:
@@ -150,3 +150,16 @@ def test_int_cache_argument_validation():
     assert L.mla_decode_absorbed(*args(5, 128, 32)) == INVALID
     assert L.mla_decode_absorbed(*args(binding.MLA_INT4, 112, 32)) == UNSUPPORTED
     assert L.mla_decode_absorbed(*args(binding.MLA_INT2, 128, 16)) == UNSUPPORTED
+
+
+def test_gqa_decode_argument_validation():
+    L = binding.lib()
+    args = lambda **k: tuple({**dict(q_c=FAKE, q_r=FAKE, kv=FAKE, tab=FAKE, mb=4, lens=FAKE, B=2, s_q=2, n_h=128,
+                                     n_g=8, d_h=128, d_r=64, bs=64, sc=0.07, qd=1, kd=1, od=1, o=FAKE, lse=None,
+                                     flags=0, st=None), **k}.values())
+    assert L.mla_gqa_decode(*args(n_g=7)) == INVALID          # n_h not a multiple of n_g
+    assert L.mla_gqa_decode(*args(o=None)) == INVALID
+    assert L.mla_gqa_decode(*args(sc=0.0)) == INVALID
+    assert L.mla_gqa_decode(*args(kd=2)) == INVALID           # fp8 is not a GQA-path cache type
+    assert L.mla_gqa_decode(*args(d_h=256, d_r=64)) == UNSUPPORTED
+    assert L.mla_gqa_decode(*args(flags=4)) == INVALID

@@ -618,3 +618,111 @@ def test_expand_then_prefill_toy_fp32_layer():
     torch.cuda.synchronize()
     assert_f32_close(o.cpu().numpy().astype(np.float64), ref["o"][0], "toy layer o", tol=1e-5)
     assert np.max(np.abs(lse.cpu().numpy() - ref["lse"][0])) <= 1e-5
+
+
+# ------------------------------------------------------------------ GQLA GQA path
+
+def _gqa_gpu(case, force_generic=False, out_dtype=torch.float32):
+    conv = bf16_dev if case.q_dtype == "bf16" else f32_dev
+    cache = bf16_dev(case.cache) if case.kv_dtype == "bf16" else f32_dev(case.cache)
+    table = torch.from_numpy(np.maximum(case.block_table, 0).astype(np.int32)).cuda()
+    lens = torch.from_numpy(case.seq_lens.astype(np.int32)).cuda()
+    o, lse = binding.gqa_decode(conv(case.q_c), conv(case.q_r), cache, table, lens, case.n_g, case.softmax_scale,
+                                block_size=case.block_size, out_dtype=out_dtype, force_generic=force_generic)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def _gqa_oracle(case, seqs=None):
+    dec = oracle.bf16_to_f64 if case.q_dtype == "bf16" else (lambda a: np.asarray(a, np.float64))
+    outs, lses = [], []
+    for b in (range(case.B) if seqs is None else seqs):
+        L = int(case.seq_lens[b])
+        k_c, v_c, k_r = oracle.gqa_paged_rows(case.cache, case.block_table[b], L, case.n_g, case.d_h, case.d_r,
+                                              case.block_size, case.kv_dtype)
+        o, l = oracle.gqa_decode_rows(dec(case.q_c[b]), dec(case.q_r[b]), k_c, v_c, k_r, case.softmax_scale, case.n_g)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
+@pytest.mark.parametrize("force_generic", [False, True])
+@pytest.mark.parametrize("s_q,n_g,lens", [(2, 8, [2, 33, 64, 129, 1500, 300, 7, 4096]),
+                                          (1, 4, [1, 95, 2048])])
+def test_gqa_decode_bf16_v3(s_q, n_g, lens, force_generic):
+    """GQA path at V3 heads (128 heads, d_h 128, d_r 64): 8 groups with two
+    new tokens (MTP) and 4 groups with one, ragged lengths; the second case
+    has a workgroup count off the multiple of 8 (plain dealing)."""
+    say(f"gqa bf16 s_q={s_q} n_g={n_g} generic={force_generic}")
+    case = inputs.gqa_case(40 + s_q, B=len(lens), seq_lens=np.array(lens), s_q=s_q, n_g=n_g)
+    g, gl = _gqa_gpu(case, force_generic)
+    o, ol = _gqa_oracle(case)
+    assert_bf16_close(g, o, "gqa o")
+    assert_lse_close(gl, ol, "gqa lse")
+    g16, _ = _gqa_gpu(case, force_generic, out_dtype=torch.bfloat16)
+    assert_bf16_close(g16, o, "gqa o bf16")
+
+
+def test_gqa_decode_full_size_sampled():
+    """16 sequences of 8192 tokens, 8 groups, s_q = 2 (the MFMA kernel's
+    launch shape at full length); the oracle checks 3 sequences."""
+    say("gqa bf16 B=16 L=8192 sampled")
+    case = inputs.gqa_case(44, B=16, seq_lens=8192, s_q=2, n_g=8)
+    g, gl = _gqa_gpu(case)
+    assert np.all(np.isfinite(g))
+    seqs = [0, 7, 15]
+    o, ol = _gqa_oracle(case, seqs)
+    assert_bf16_close(g[seqs], o, "gqa 8192 sampled")
+    assert_lse_close(gl[seqs], ol, "gqa 8192 lse")
+
+
+def test_gqa_decode_fp32_toy():
+    """fp32 toy shapes (8 heads in 2 groups, d_h 64, d_r 32, 16-token blocks):
+    the portable kernel to the fp32 bar."""
+    say("gqa fp32 toy")
+    case = inputs.gqa_case(46, B=3, seq_lens=np.array([2, 40, 77]), s_q=2, n_h=8, n_g=2, d_h=64, d_r=32,
+                           kv_dtype="f32", q_dtype="f32", block_size=16)
+    g, gl = _gqa_gpu(case)
+    o, ol = _gqa_oracle(case)
+    assert_f32_close(g, o, "gqa fp32")
+    assert np.max(np.abs(gl - ol)) <= 1e-5
+
+
+def test_gqa_path_equals_absorbed_decode_on_gpu():
+    """The same GQLA weights through both GPU paths: expand the latent per
+    group (mla_expand_kv), page it, decode on the GQA path; absorb W^UK_g per
+    head, decode the latent on the MQA path, apply W^UV_g.  Both agree with
+    each other within the bf16 bar."""
+    say("gqla two paths on the GPU")
+    n_h, n_g, d_h, d_c, d_r, s_q, L = 128, 8, 128, 512, 64, 2, 256
+    rng = np.random.Generator(np.random.PCG64(48))
+    c = inputs.f32_to_bf16_bits(rng.standard_normal((L, d_c), dtype=np.float32))
+    kr = inputs.f32_to_bf16_bits(rng.standard_normal((L, d_r), dtype=np.float32))
+    w_uk = inputs.f32_to_bf16_bits(rng.standard_normal((n_g * d_h, d_c), dtype=np.float32) / np.float32(d_c ** 0.5))
+    w_uv = inputs.f32_to_bf16_bits(rng.standard_normal((n_g * d_h, d_c), dtype=np.float32) / np.float32(d_c ** 0.5))
+    q_c = inputs.f32_to_bf16_bits(rng.standard_normal((1, s_q, n_h, d_h), dtype=np.float32))
+    q_r = inputs.f32_to_bf16_bits(rng.standard_normal((1, s_q, n_h, d_r), dtype=np.float32))
+    scale = 1.0 / math.sqrt(d_h + d_r)
+    # GQA path: expand per group, lay out the pages [n_g][64][d_h] k | [n_g][64][d_h] v | [64][d_r] k^R
+    k_c, v_c = binding.expand_kv(bf16_dev(c), bf16_dev(w_uk), bf16_dev(w_uv), d_h)      # [L, n_g, d_h] bf16
+    nb = L // 64
+    kg = k_c.view(nb, 64, n_g, d_h).permute(0, 2, 1, 3).reshape(nb, -1)
+    vg = v_c.view(nb, 64, n_g, d_h).permute(0, 2, 1, 3).reshape(nb, -1)
+    cache = torch.cat([kg, vg, bf16_dev(kr).view(nb, -1)], 1).contiguous()
+    table = torch.arange(nb, dtype=torch.int32, device="cuda")[None]
+    lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+    o_gqa, l_gqa = binding.gqa_decode(bf16_dev(q_c), bf16_dev(q_r), cache, table, lens, n_g, scale,
+                                      out_dtype=torch.float32)
+    # MQA-absorb path with the group's weights repeated per head
+    w_uk_h = bf16_dev(w_uk).view(n_g, 1, d_h, d_c).expand(n_g, n_h // n_g, d_h, d_c).reshape(n_h * d_h, d_c)
+    w_uv_h = bf16_dev(w_uv).view(n_g, 1, d_h, d_c).expand(n_g, n_h // n_g, d_h, d_c).reshape(n_h * d_h, d_c)
+    q_lat = binding.absorb_q(bf16_dev(q_c).view(s_q, n_h, d_h), w_uk_h.contiguous())
+    lat_cache = torch.cat([bf16_dev(c), bf16_dev(kr)], 1).view(nb, 64, d_c + d_r).contiguous()
+    o_lat, l_mqa = binding.decode(q_lat.view(1, s_q, n_h, d_c), bf16_dev(q_r), lat_cache, table, lens, scale,
+                                  out_dtype=torch.bfloat16)
+    o_mqa = binding.up_proj_v(o_lat.view(s_q, n_h, d_c), w_uv_h.contiguous(), d_h, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    a = o_gqa.cpu().numpy().astype(np.float64).reshape(s_q, n_h, d_h)
+    b = o_mqa.cpu().numpy().astype(np.float64).reshape(s_q, n_h, d_h)
+    assert_bf16_close(a, b, "gqa vs absorbed")
+    assert np.max(np.abs(l_gqa.cpu().numpy() - l_mqa.cpu().numpy())) <= 0.05
