@@ -205,6 +205,48 @@ def bench_prefill(steps: int, dev, T: int = PREFILL_T) -> dict:
                           "frac": tf_exp / MFMA_BF16_PEAK_TFLOPS}}
 
 
+def bench_gqa(steps: int, dev, B: int = 64, L: int = 8192) -> dict:
+    """GQLA's GQA decode path on the same context: B sequences of L tokens,
+    8 groups of 16 heads, two new tokens per step (MTP), bf16 per-group
+    expanded cache.  HBM-bound: algorithmic bytes = every cached token's
+    (2 * 8 * 128 + 64) * 2 = 4224 bytes read once."""
+    import torch
+    from mla_latent_kv_05_amd import binding
+    n_h, n_g, d_h, d_r, s_q, bs = 128, 8, 128, 64, 2, 64
+    g = torch.Generator(device=dev)
+    g.manual_seed(23)
+    nb = B * ((L + bs - 1) // bs)
+    row = 2 * n_g * d_h + d_r
+    cache = torch.randn(nb, bs * row, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    perm = torch.randperm(nb, generator=g, device=dev).to(torch.int32)
+    table = perm.view(B, -1).contiguous()
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    q_c = torch.randn(B, s_q, n_h, d_h, generator=g, device=dev).to(torch.bfloat16)
+    q_r = torch.randn(B, s_q, n_h, d_r, generator=g, device=dev).to(torch.bfloat16)
+    o = torch.empty(B, s_q, n_h, d_h, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, s_q, n_h, dtype=torch.float32, device=dev)
+    scale = (d_h + d_r) ** -0.5
+
+    def run():
+        binding.gqa_decode(q_c, q_r, cache, table, lens, n_g, scale, out=o, lse=lse)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(10, min(steps, 50))
+    e0.record()
+    for _ in range(n):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    algo = B * L * row * 2
+    gbs = algo / (us * 1e-6) / 1e9
+    return {"B": B, "ctx": L, "s_q": s_q, "n_g": n_g, "bytes_per_token": row * 2, "us_per_call": us,
+            "algorithmic_bytes": algo, "achieved_GBps": gbs, "bound": "hbm", "peak_GBps": HBM_PEAK_GBS,
+            "frac": gbs / HBM_PEAK_GBS, "decode_tok_s": B * s_q / (us * 1e-6)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,6 +262,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the cache-producer measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the MHA-mode prefill measurement")
+    ap.add_argument("--no-gqa", action="store_true", help="skip the GQA-path decode measurement")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference kernel "
                          "for scaling HBM traffic counters) and exit")
@@ -398,6 +441,8 @@ def main() -> int:
         rec["cache_append"] = bench_append(case, args.steps, dev)
     if not args.no_prefill:
         rec["prefill_mha"] = bench_prefill(args.steps, dev)
+    if not args.no_gqa:
+        rec["gqa_decode"] = bench_gqa(args.steps, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(case, P, args.cpu_seconds)
         rec["cpu_baseline"]["cpu_model"] = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")

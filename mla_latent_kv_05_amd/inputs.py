@@ -482,6 +482,7 @@ WORKLOADS = {
                                  kv_dtype="bf16"),
     "v3_fp8_B64_ctx16384_sq2": dict(kind="decode", seed=5, B=64, lens=("fixed", 16384), s_q=2,
                                     kv_dtype="fp8"),
+    "v3_bf16_B64_ctx8192_sq2": dict(kind="decode", seed=8, B=64, lens=("fixed", 8192), s_q=2, kv_dtype="bf16"),
     "v3_int4_B64_ctx8192": dict(kind="decode", seed=6, B=64, lens=("fixed", 8192), s_q=1, kv_dtype="int4"),
     "v3_int2_B64_ctx8192": dict(kind="decode", seed=7, B=64, lens=("fixed", 8192), s_q=1, kv_dtype="int2"),
 }
