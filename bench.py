@@ -263,6 +263,9 @@ def main() -> int:
     ap.add_argument("--no-append", action="store_true", help="skip the cache-producer measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the MHA-mode prefill measurement")
     ap.add_argument("--no-gqa", action="store_true", help="skip the GQA-path decode measurement")
+    ap.add_argument("--step-api", choices=("fused", "separate"), default="fused",
+                    help="time the step as one mla_decode_step call (absorb, attention, merge fused with W^UV) "
+                         "or as mla_absorb_q + mla_decode_absorbed + mla_up_proj_v")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference kernel "
                          "for scaling HBM traffic counters) and exit")
@@ -321,7 +324,21 @@ def main() -> int:
             e.record()
     torch.cuda.synchronize()
 
+    qn4 = q_c.view(B, s_q, n_h, d_h)
+    ws_step = binding.decode_step_workspace(B, s_q, n_h, d_c, table.shape[1], args.splits, device=dev)
+
+    def fused_step(i, timed=False):
+        """absorb + attention + merge fused with W^UV: one library call, three launches"""
+        if timed:
+            binding.decode_kernel_events(ev["k0"][i], ev["k1"][i])
+        binding.decode_step(qn4, w_uk, q_rope, caches[i % len(caches)], table, lens, w_uv, scale,
+                            kv_dtype=kv_dtype, num_splits=args.splits, workspace=ws_step,
+                            out=o.view(B, s_q, n_h, d_h), lse=lse)
+
     def step(i, timed=False):
+        if args.step_api == "fused" and not timed:
+            fused_step(i)
+            return
         if timed:
             ev["a"][i].record()
         binding.absorb_q(q_c, w_uk, out=q_lat)
@@ -392,6 +409,13 @@ def main() -> int:
     decode_ms = float(np.mean([ev["b"][i].elapsed_time(ev["c"][i]) for i in range(args.steps)]))
     up_ms = float(np.mean([ev["c"][i].elapsed_time(ev["d"][i]) for i in range(args.steps)]))
     kernel_ms = float(np.mean([ev["k0"][i].elapsed_time(ev["k1"][i]) for i in range(args.steps)]))
+    if args.step_api == "fused":
+        # the fused step runs the same attention kernel; its time comes from
+        # the events the library records around it, in a pass of its own
+        for i in range(args.steps):
+            fused_step(i, timed=True)
+        torch.cuda.synchronize()
+        kernel_ms = float(np.mean([ev["k0"][i].elapsed_time(ev["k1"][i]) for i in range(args.steps)]))
 
     latent_bytes = case.latent_bytes
     value = latent_bytes / (ms_step * 1e-3) / 1e12
@@ -429,7 +453,7 @@ def main() -> int:
         "config": {"workload": args.workload, "n_h": n_h, "d_c": d_c, "d_r": d_r, "d_h": d_h, "B": B,
                    "s_q": s_q, "ctx": int(case.seq_lens.max()) if w["lens"][0] == "fixed" else "log-uniform",
                    "page_tokens": case.block_size, "kv_dtype": case.kv_dtype, "splits": args.splits or "auto",
-                   "cache_copies": len(caches), "launch": args.launch},
+                   "cache_copies": len(caches), "launch": args.launch, "step_api": args.step_api},
         "decode_tok_s": tok_s, "latent_bytes": latent_bytes,
         "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
         "roofline_frac_step": value * 1e3 / HBM_PEAK_GBS if case.kv_dtype == "bf16" else None,

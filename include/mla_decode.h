@@ -234,6 +234,31 @@ int mla_cache_append(const void* h, int64_t h_stride_t, const void* w_dkv_kr, co
  * (0 for invalid sizes). */
 size_t mla_cache_append_workspace_bytes(int T, int d, int d_c, int d_r);
 
+/* mla_decode_step -- one whole absorbed decode step in three launches
+ * (itwiki "Multi-head latent attention", section "Matrix absorption"):
+ * q_lat = W^UK_h^T q_nope (as mla_absorb_q), the attention of
+ * mla_decode_absorbed over the paged cache, and the split-KV merge fused
+ * with o = W^UV_h o_lat (as mla_up_proj_v).  Same results as those three
+ * calls with bf16 q_lat / o_lat, without the o_lat round trip through memory.
+ *
+ *  q_nope [B, s_q, n_h, d_h] bf16, q_rope [B, s_q, n_h, d_r] bf16, contiguous
+ *  w_uk, w_uv [n_h*d_h, d_c] bf16 ([out, in], head h = rows h*d_h ..)
+ *  kv_cache, block_table, seq_lens, kv_dtype, num_splits: as mla_decode_absorbed
+ *  o [B, s_q, n_h, d_h] bf16; lse [B, s_q, n_h] fp32 or NULL
+ *  workspace >= mla_decode_step_workspace_bytes(...), 16-byte aligned
+ * Needs the MFMA path of mla_decode_absorbed (n_h = 128, d_c = 512,
+ * d_r = 64, block_size = 64, kv bf16 / fp8 / int4 / int2) and d_h = 128,
+ * else MLA_ERR_UNSUPPORTED; all pointers 16-byte aligned. */
+int mla_decode_step(const void* q_nope, const void* w_uk, const void* q_rope, const void* kv_cache,
+                    const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens, const void* w_uv,
+                    int B, int s_q, int n_h, int d_h, int d_c, int d_r, int block_size, float softmax_scale,
+                    int kv_dtype, int num_splits, void* workspace, size_t workspace_bytes, void* o, float* lse,
+                    void* stream);
+
+/* mla_decode_step_workspace_bytes -- workspace of mla_decode_step (the
+ * decode workspace plus bf16 q_lat and merged-row buffers); 0 on bad sizes. */
+size_t mla_decode_step_workspace_bytes(int B, int s_q, int n_h, int d_c, int max_blocks_per_seq, int num_splits);
+
 /* mla_expand_kv -- MHA-mode keys and values from the latent (itwiki
  * "Multi-head latent attention", section "Joint KV compression"), the input
  * of prefill: k_c[t,i,:] = W^UK_i c_kv[t,:], v_c[t,i,:] = W^UV_i c_kv[t,:].

@@ -42,6 +42,11 @@ _SIGS = {
                                     _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int,
                                     _c.c_int, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "mla_cache_append_workspace_bytes": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int]),
+    "mla_decode_step": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int,
+                                   _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                   _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_void_p, _c.c_size_t,
+                                   _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "mla_decode_step_workspace_bytes": (_c.c_size_t, [_c.c_int] * 6),
     "mla_gqa_decode": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p,
                                   _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float,
                                   _c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
@@ -233,6 +238,42 @@ def cache_append(h: torch.Tensor, w_dkv_kr: torch.Tensor, positions: torch.Tenso
                                   _ptr(kv_cache), T, d, d_c, d_r, block_size, float(rope_base), _dt(h),
                                   kv_dtype, _ptr(workspace), workspace.numel(), _stream()), "mla_cache_append")
     return kv_cache
+
+
+def decode_step(q_nope: torch.Tensor, w_uk: torch.Tensor, q_rope: torch.Tensor, kv_cache: torch.Tensor,
+                block_table: torch.Tensor, seq_lens: torch.Tensor, w_uv: torch.Tensor, softmax_scale: float,
+                kv_dtype: int | None = None, d_c: int = 512, block_size: int = 64, num_splits: int = 0,
+                workspace: torch.Tensor | None = None, with_lse: bool = True, out: torch.Tensor | None = None,
+                lse: torch.Tensor | None = None):
+    """Whole absorbed decode step: absorb, attention, merge + up-projection.
+    q_nope [B, s_q, n_h, d_h], q_rope [B, s_q, n_h, d_r], weights [n_h*d_h, d_c]
+    (all bf16).  Returns (o [B, s_q, n_h, d_h] bf16, lse [B, s_q, n_h] or None)."""
+    _gpu(q_nope, w_uk, q_rope, kv_cache, block_table, seq_lens, w_uv)
+    B, s_q, n_h, d_h = q_nope.shape
+    d_r = q_rope.shape[-1]
+    for t in (q_nope, w_uk, q_rope, w_uv, kv_cache, block_table):
+        assert t.is_contiguous()
+    assert q_rope.shape == (B, s_q, n_h, d_r) and w_uk.shape == (n_h * d_h, d_c) and w_uv.shape == (n_h * d_h, d_c)
+    if kv_dtype is None:
+        kv_dtype = _dt(kv_cache)
+    max_blocks = block_table.shape[1]
+    if workspace is None:
+        n = lib().mla_decode_step_workspace_bytes(B, s_q, n_h, d_c, max_blocks, num_splits)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q_nope.device)
+    if out is None:
+        out = torch.empty((B, s_q, n_h, d_h), dtype=torch.bfloat16, device=q_nope.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, s_q, n_h), dtype=torch.float32, device=q_nope.device)
+    _check(lib().mla_decode_step(_ptr(q_nope), _ptr(w_uk), _ptr(q_rope), _ptr(kv_cache), _ptr(block_table),
+                                 max_blocks, _ptr(seq_lens), _ptr(w_uv), B, s_q, n_h, d_h, d_c, d_r, block_size,
+                                 float(softmax_scale), kv_dtype, num_splits, _ptr(workspace), workspace.numel(),
+                                 _ptr(out), _ptr(lse) if with_lse else None, _stream()), "mla_decode_step")
+    return out, (lse if with_lse else None)
+
+
+def decode_step_workspace(B, s_q, n_h, d_c, max_blocks_per_seq, num_splits=0, device="cuda") -> torch.Tensor:
+    n = lib().mla_decode_step_workspace_bytes(B, s_q, n_h, d_c, max_blocks_per_seq, num_splits)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def gqa_decode(q_c: torch.Tensor, q_r: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,

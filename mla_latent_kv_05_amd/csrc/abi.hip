@@ -317,6 +317,101 @@ int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_ca
   return launch_status(e);
 }
 
+static size_t step_extra_bytes(int B, int s_q, int n_h, int d_c) {
+  return 2 * align256((size_t)B * s_q * n_h * d_c * 2);  // q_lat and merged-row buffers (bf16)
+}
+
+size_t mla_decode_step_workspace_bytes(int B, int s_q, int n_h, int d_c, int max_blocks_per_seq, int num_splits) {
+  const size_t base = mla_decode_workspace_bytes(B, s_q, n_h, d_c, max_blocks_per_seq, num_splits);
+  return base ? align256(base) + step_extra_bytes(B, s_q, n_h, d_c) : 0;
+}
+
+int mla_decode_step(const void* q_nope, const void* w_uk, const void* q_rope, const void* kv_cache,
+                    const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens, const void* w_uv,
+                    int B, int s_q, int n_h, int d_h, int d_c, int d_r, int block_size, float softmax_scale,
+                    int kv_dtype, int num_splits, void* workspace, size_t workspace_bytes, void* o, float* lse,
+                    void* stream) {
+  if (B <= 0 || s_q <= 0 || n_h <= 0 || d_h <= 0 || d_c <= 0 || d_r < 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_splits < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!q_nope || !w_uk || !q_rope || !kv_cache || !block_table || !seq_lens || !w_uv || !o)
+    return MLA_ERR_INVALID_ARG;
+  if (kv_dtype < MLA_F32 || kv_dtype > MLA_INT2) return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return MLA_ERR_INVALID_ARG;
+  if (!workspace) return MLA_ERR_WORKSPACE;
+  DecodeShape shp{B, s_q, n_h, d_c, d_r, block_size, max_blocks_per_seq, num_splits};
+  if (!mfma_eligible(shp, MLA_BF16, kv_dtype) || d_h != 128 || s_q > 16) return MLA_ERR_UNSUPPORTED;
+  if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_rope) || !aligned16(kv_cache) || !aligned16(w_uv) ||
+      !aligned16(o) || !aligned16(workspace))
+    return MLA_ERR_MISALIGNED;
+  const int n_cu = current_cu_count();
+  if (n_cu <= 0) return MLA_ERR_LAUNCH;
+  const WsLayout L = layout_for(shp, n_cu);
+  const size_t dec_bytes = align256(L.total);
+  if (workspace_bytes < dec_bytes + step_extra_bytes(B, s_q, n_h, d_c)) return MLA_ERR_WORKSPACE;
+  uint8_t* ws = (uint8_t*)workspace;
+  const int T_q = B * s_q;
+  uint16_t* q_lat = (uint16_t*)(ws + dec_bytes);
+  uint16_t* o_fin = (uint16_t*)(ws + dec_bytes + align256((size_t)T_q * n_h * d_c * 2));
+  hipStream_t st = (hipStream_t)stream;
+
+  // 1. absorption into the workspace (bf16 q_lat), the split planner riding
+  //    in the same launch; 2. the attention kernel (unsplit sequences write
+  //    their final rows to o_fin); 3. merge + up-projection
+  DecodeArgs a{};
+  a.q_lat = q_lat;
+  a.q_rope = q_rope;
+  a.kv = kv_cache;
+  a.table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = o_fin;
+  a.lse = lse;
+  a.ws_header = (int*)ws;
+  a.work = (const int4*)(ws + L.work);
+  a.seq = (const int2*)(ws + L.seq);
+  a.lse_part = (float*)(ws + L.lse_part);
+  a.o_part = (float*)(ws + L.o_part);
+  a.part_bf16 = 1;
+  a.block_bytes = (long long)block_size * kv_row_bytes(kv_dtype, d_c, d_r);
+  a.max_blocks = max_blocks_per_seq;
+  a.B = B; a.s_q = s_q; a.n_h = n_h; a.d_c = d_c; a.d_r = d_r; a.block_size = block_size;
+  a.scale = softmax_scale;
+  a.q_dtype = MLA_BF16; a.kv_dtype = kv_dtype; a.out_dtype = MLA_BF16;
+  const int grid_x = n_cu / s_q > 0 ? n_cu / s_q : 1;
+  PlanArgs p{};
+  p.seq_lens = seq_lens;
+  p.ws_header = (int*)ws;
+  p.work = (int4*)(ws + L.work);
+  p.seq = (int2*)(ws + L.seq);
+  p.B = B;
+  p.block_size = block_size;
+  p.num_splits = num_splits;
+  p.slots_per_wave = grid_x;
+  p.min_chunk = 8;
+  p.max_chunk = mfma_max_unit_pages();
+  p.units_max = L.units_max;
+  hipError_t e = launch_absorb_plan(q_nope, (long long)n_h * d_h, w_uk, q_lat, (long long)n_h * d_c, T_q, n_h, d_h,
+                                    d_c, p, st);
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  hipEvent_t ev0 = g_kernel_ev_before, ev1 = g_kernel_ev_after;
+  g_kernel_ev_before = g_kernel_ev_after = nullptr;
+  if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return MLA_ERR_LAUNCH;
+  e = launch_decode_mfma(a, grid_x, st);
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return MLA_ERR_LAUNCH;
+  // 3. merge of the partitions fused with the up-projection
+  CombineUpArgs c{};
+  c.seq = a.seq;
+  c.lse_part = a.lse_part;
+  c.o_part = (const uint16_t*)a.o_part;
+  c.o_fin = o_fin;
+  c.w_uv = (const uint16_t*)w_uv;
+  c.out = (uint16_t*)o;
+  c.lse = lse;
+  c.B = B; c.s_q = s_q; c.n_h = n_h;
+  return launch_status(launch_combine_up(c, st));
+}
+
 int mla_combine_lse(const float* o_part, const float* lse_part, const int32_t* splits_per_row, int N, int S,
                     int D, void* out, float* lse_out, int out_dtype, void* stream) {
   if (N < 0 || S <= 0 || D <= 0 || !act_dtype_ok(out_dtype)) return MLA_ERR_INVALID_ARG;

@@ -86,7 +86,21 @@ struct PlanArgs {
   int units_max;
 };
 
+// fused merge + W^UV up-projection of a decode step (bf16 partial rows,
+// d_c = 512, d_h = 128)
+struct CombineUpArgs {
+  const int2* seq;
+  const float* lse_part;
+  const uint16_t* o_part;  // bf16 partial rows [unit][s_q * n_h][512]
+  const uint16_t* o_fin;   // bf16 final rows of unsplit sequences [B * s_q][n_h][512]
+  const uint16_t* w_uv;    // [n_h * 128, 512]
+  uint16_t* out;           // [B * s_q][n_h][128]
+  float* lse;              // [B * s_q][n_h] or null
+  int B, s_q, n_h;
+};
+
 // launchers (return hipError_t of the launch)
+hipError_t launch_combine_up(const CombineUpArgs& c, hipStream_t s);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_decode_generic(const DecodeArgs& a, int units_max, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t s);
@@ -99,6 +113,9 @@ hipError_t launch_combine_lse(const float* o_part, const float* lse_part, const 
 hipError_t launch_absorb(const void* q, long long q_st, const void* w, void* out, long long o_st,
                          int T, int n_h, int d_h, int d_c, int act_dt, int w_dt, int out_dt,
                          bool mfma, hipStream_t s);
+// bf16 absorption with the split planner in the same launch
+hipError_t launch_absorb_plan(const void* q, long long q_st, const void* w, void* out, long long o_st, int T,
+                              int n_h, int d_h, int d_c, const PlanArgs& pa, hipStream_t s);
 hipError_t launch_prefill(const void* q, const void* kc, const void* kr, const void* v, void* out, float* lse,
                           int T, int n_h, int d_h, int d_r, float scale, int in_dtype, int out_dtype,
                           hipStream_t s);

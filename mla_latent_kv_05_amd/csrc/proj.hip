@@ -8,6 +8,7 @@
 // keep each head's weight slice in one workgroup.
 #include "device_util.h"
 #include "mla_internal.h"
+#include "plan_body.h"
 
 namespace mla {
 
@@ -57,10 +58,10 @@ constexpr size_t absorb_lds_bytes(int d_h, bool out_bf16) {
   return (size_t)d_h * kAbsStride * 2 + 32 * kAbsQStride * 2 + 32 * (kAbsCols + 8) * (out_bf16 ? 2 : 4);
 }
 
+// one workgroup's tile: head h, column block cblk
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* q, long long q_st,
-                                                          const uint16_t* w, void* out, long long o_st,
-                                                          int T, int n_h, int d_h, int d_c) {
+__device__ __forceinline__ void absorb_tile(const uint16_t* q, long long q_st, const uint16_t* w, void* out,
+                                            long long o_st, int T, int n_h, int d_h, int d_c, int h, int cblk) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   typedef __attribute__((address_space(3))) u32x4_t lds_u4;
   lds_u8* wl = (lds_u8*)smem_raw;
@@ -68,8 +69,7 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* q, lon
   lds_u8* ol = ql + 32 * kAbsQStride * 2;
   constexpr int kOutElem = OUT_BF16 ? 2 : 4;
   constexpr int kORow = (kAbsCols + 8) * kOutElem;  // staged output row (bytes)
-  const int h = blockIdx.y;
-  const int c0 = blockIdx.x * kAbsCols;
+  const int c0 = cblk * kAbsCols;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31, j16 = lane & 15, G = lane >> 4;
   const int ncols = min(kAbsCols, d_c - c0);
@@ -247,6 +247,39 @@ __global__ __launch_bounds__(256) void up_mfma_kernel(const uint16_t* a, long lo
     if (t0 + 32 < T) store_a();
     __syncthreads();
   }
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* q, long long q_st, const uint16_t* w,
+                                                          void* out, long long o_st, int T, int n_h, int d_h,
+                                                          int d_c) {
+  absorb_tile<OUT_BF16>(q, q_st, w, out, o_st, T, n_h, d_h, d_c, blockIdx.y, blockIdx.x);
+}
+
+// The absorption with the split planner riding along: row 0 of the grid is
+// the planner (its first workgroup; the others return), rows 1.. the
+// absorption tiles, so the planning overlaps the weight reads instead of
+// taking a launch of its own.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void absorb_plan_kernel(const uint16_t* q, long long q_st, const uint16_t* w,
+                                                          void* out, long long o_st, int T, int n_h, int d_h,
+                                                          int d_c, PlanArgs pa) {
+  if (blockIdx.y == 0) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
+    if (blockIdx.x == 0) plan_body<256>(pa, smem_raw);
+    return;
+  }
+  absorb_tile<OUT_BF16>(q, q_st, w, out, o_st, T, n_h, d_h, d_c, blockIdx.y - 1, blockIdx.x);
+}
+
+hipError_t launch_absorb_plan(const void* q, long long q_st, const void* w, void* out, long long o_st, int T,
+                              int n_h, int d_h, int d_c, const PlanArgs& pa, hipStream_t s) {
+  dim3 grid((d_c + kAbsCols - 1) / kAbsCols, n_h + 1);
+  const size_t lds = absorb_lds_bytes(d_h, true) > (size_t)plan_lds_bytes(256) ? absorb_lds_bytes(d_h, true)
+                                                                                 : (size_t)plan_lds_bytes(256);
+  hipLaunchKernelGGL(absorb_plan_kernel<true>, grid, dim3(256), lds, s, (const uint16_t*)q, q_st,
+                     (const uint16_t*)w, out, o_st, T, n_h, d_h, d_c, pa);
+  return hipGetLastError();
 }
 
 hipError_t launch_absorb(const void* q, long long q_st, const void* w, void* out, long long o_st, int T,

@@ -20,7 +20,8 @@ def test_header_functions_exported():
     names = binding.header_functions()
     assert set(names) == {"mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_absorbed",
                           "mla_combine_lse", "mla_up_proj_v", "mla_status_string", "mla_decode_kernel_events",
-                          "mla_cache_append", "mla_cache_append_workspace_bytes", "mla_expand_kv", "mla_gqa_decode",
+                          "mla_cache_append", "mla_cache_append_workspace_bytes", "mla_expand_kv", "mla_gqa_decode", "mla_decode_step",
+                          "mla_decode_step_workspace_bytes",
                           "mla_prefill_mha"}
     L = binding.lib()
     for n in names:
@@ -163,3 +164,22 @@ def test_gqa_decode_argument_validation():
     assert L.mla_gqa_decode(*args(kd=2)) == INVALID           # fp8 is not a GQA-path cache type
     assert L.mla_gqa_decode(*args(d_h=256, d_r=64)) == UNSUPPORTED
     assert L.mla_gqa_decode(*args(flags=4)) == INVALID
+
+
+def test_decode_step_argument_validation():
+    L = binding.lib()
+    base = L.mla_decode_workspace_bytes(4, 2, 128, 512, 16, 0)
+    step = L.mla_decode_step_workspace_bytes(4, 2, 128, 512, 16, 0)
+    if base:  # sizes need the device's compute-unit count
+        assert step >= base + 2 * 4 * 2 * 128 * 512 * 2
+    else:
+        assert step == 0
+        step = 1 << 30
+    args = lambda **k: tuple({**dict(qn=FAKE, wuk=FAKE, qr=FAKE, kv=FAKE, tab=FAKE, mb=16, lens=FAKE, wuv=FAKE, B=4,
+                                     s_q=2, n_h=128, d_h=128, d_c=512, d_r=64, bs=64, sc=0.07, kd=1, ns=0, ws=FAKE,
+                                     wsb=step, o=FAKE, lse=None, st=None), **k}.values())
+    assert L.mla_decode_step(*args(wuv=None)) == INVALID
+    assert L.mla_decode_step(*args(d_h=64)) == UNSUPPORTED       # the fused up-projection is for d_h = 128
+    assert L.mla_decode_step(*args(n_h=64)) == UNSUPPORTED       # off the MFMA attention shape
+    assert L.mla_decode_step(*args(o=FAKE + 8)) == MISALIGNED
+    assert L.mla_decode_step(*args(ws=None)) == WORKSPACE

@@ -726,3 +726,49 @@ def test_gqa_path_equals_absorbed_decode_on_gpu():
     b = o_mqa.cpu().numpy().astype(np.float64).reshape(s_q, n_h, d_h)
     assert_bf16_close(a, b, "gqa vs absorbed")
     assert np.max(np.abs(l_gqa.cpu().numpy() - l_mqa.cpu().numpy())) <= 0.05
+
+
+# ------------------------------------------------------------------ fused decode step
+
+@pytest.mark.parametrize("kv,lens,s_q,splits", [("bf16", [2, 33, 64, 129, 1500], 1, 0),
+                                                ("bf16", [70, 4096, 9], 2, 3),
+                                                ("fp8", [2, 700, 2048], 2, 0),
+                                                ("int4", [64, 1000], 1, 1)])
+def test_decode_step_matches_separate_calls_and_oracle(kv, lens, s_q, splits):
+    """mla_decode_step (absorb, attention, merge fused with W^UV) against the
+    oracle's absorbed layer on the same rounded inputs, and equal to the three
+    separate calls (which also store o_lat in bf16)."""
+    say(f"decode step {kv} s_q={s_q} splits={splits}")
+    lens = np.array(lens, dtype=np.int32)
+    case = inputs.decode_case(60 + s_q, B=len(lens), seq_lens=lens, s_q=s_q, kv_dtype=kv, **V3)
+    T_q = case.B * s_q
+    P = inputs.projection_weights(61, T_q=T_q)
+    d = case_to_device(case)
+    qn, wuk, wuv = bf16_dev(P["q_c"]).view(case.B, s_q, 128, 128), bf16_dev(P["w_uk"]), bf16_dev(P["w_uv"])
+    o, lse = binding.decode_step(qn, wuk, d["q_rope"], d["kv_cache"], d["block_table"], d["seq_lens"], wuv,
+                                 d["softmax_scale"], kv_dtype=d["kv_dtype"], num_splits=splits)
+    # the same step through the separate entry points
+    q_lat = binding.absorb_q(qn.view(T_q, 128, 128), wuk)
+    o_lat, lse2 = binding.decode(q_lat.view(case.B, s_q, 128, 512), d["q_rope"], d["kv_cache"], d["block_table"],
+                                 d["seq_lens"], d["softmax_scale"], kv_dtype=d["kv_dtype"], num_splits=splits)
+    o2 = binding.up_proj_v(o_lat.view(T_q, 128, 512), wuv, 128)
+    torch.cuda.synchronize()
+    g = o.float().cpu().numpy().astype(np.float64).reshape(T_q, 128, 128)
+    g2 = o2.float().cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(g - g2)) <= 2e-2 * max(1.0, np.max(np.abs(g2)))
+    assert np.max(np.abs(lse.cpu().numpy() - lse2.cpu().numpy())) <= 1e-6
+    # oracle: absorbed decode on the bf16-rounded inputs, then W^UV; the step
+    # stores q_lat in bf16 (its operand type), so the oracle decodes with the
+    # exact q_lat rounded to bf16
+    ql = oracle.absorb_q(oracle.bf16_to_f64(P["q_c"]), oracle.bf16_to_f64(P["w_uk"]), 128, 128)
+    ql = oracle.bf16_to_f64(oracle.bf16_round_bits(ql)).reshape(case.B, s_q, 128, 512)
+    ref_o, ref_l = [], []
+    for b in range(case.B):
+        _, qr, c, kr = oracle.decode_case_rows(case, b)
+        ol, l = oracle.mqa_decode_rows(ql[b], qr, c, kr, case.softmax_scale)
+        ref_o.append(oracle.up_proj_v(ol, oracle.bf16_to_f64(P["w_uv"]), 128, 128))
+        ref_l.append(l)
+    ref_o = np.stack(ref_o).reshape(T_q, 128, 128)
+    assert_bf16_close(g, ref_o, f"step {kv}")
+    if kv != "int4":
+        assert_lse_close(lse.cpu().numpy().astype(np.float64).reshape(case.B, s_q, 128), np.stack(ref_l), "step lse")
