@@ -8,9 +8,11 @@
 //
 // MFMA kernel (bf16, d_h = 128, d_r = 64): a workgroup of 4 waves takes one
 // head and 128 query rows, wave w rows 32w .. 32w+31.  Keys stream through a
-// 3-stage LDS ring in 32-key subtiles (content keys, RoPE keys and values in
-// three swizzled regions), filled by 16-byte global->LDS DMA two subtiles
-// ahead; one barrier per subtile.  Per subtile and wave:
+// 2-stage LDS ring in 32-key subtiles (content keys, RoPE keys and values in
+// three swizzled regions), filled by 16-byte global->LDS DMA one subtile
+// ahead; one barrier per subtile.  40 KB of LDS and at most 168 registers
+// per lane let three workgroups share a compute unit (three waves per SIMD
+// hide each other's softmax and DMA waits).  Per subtile and wave:
 //   S^T[key, query] = K[key, 0:192] . Q^T  (12 v_mfma_f32_32x32x16_bf16; A =
 //                     key rows by ds_read_b128, B = the queries in registers)
 //   online softmax per query (the lane is the query; exp2 domain, lazy
@@ -35,7 +37,7 @@ constexpr int kPfKcB = kPfSub * kPfDh * 2;                     // 8192: content 
 constexpr int kPfKrB = kPfSub * kPfDr * 2;                     // 4096: RoPE keys, 128-byte rows
 constexpr int kPfVB = kPfSub * kPfDh * 2;                      // 8192: values, 256-byte rows
 constexpr int kPfStage = kPfKcB + kPfKrB + kPfVB;              // 20480
-constexpr int kPfRing = 3;
+constexpr int kPfRing = 2;
 constexpr int kPfDma = 5;                                      // DMA instructions per thread per subtile
 constexpr float kPfTau = 8.f;                                  // lazy-max slack (log2 units)
 
@@ -52,7 +54,7 @@ __device__ __forceinline__ int pf_f8(int t) { return (t >> 1) & 7; }
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(const uint16_t* q, const uint16_t* kc,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void prefill_mfma_kernel(const uint16_t* q, const uint16_t* kc,
                                                            const uint16_t* kr, const uint16_t* v, void* out,
                                                            float* lse, int T, int n_h, int nqb, float scale2,
                                                            int out_bf16) {
@@ -153,12 +155,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const uint16_t* q, co
   // offset below folds into the instruction's immediate)
   auto step = [&](int s, auto slot_c) {
     constexpr int SLOT = decltype(slot_c)::value;
-    if (s + 1 < n_sub)
-      wait_vm<kPfDma>();  // subtile s landed (s + 1 may still be in flight)
-    else
-      wait_vm<0>();
+    wait_vm<0>();     // subtile s landed
     __syncthreads();  // subtile s visible; every wave is done with subtile s - 1
-    if (s + 2 < n_sub) issue(s + 2, (SLOT + 2) % kPfRing);  // into the slot subtile s - 1 used
+    if (s + 1 < n_sub) issue(s + 1, (SLOT + 1) % kPfRing);  // into the slot subtile s - 1 used
     const lds_u8* tile = smem + SLOT * kPfStage;
     const int j0 = s * kPfSub;
     if (j0 < wave_end) {  // scalar branch: some of these keys are visible to this wave
@@ -229,11 +228,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const uint16_t* q, co
   };
   wait_vm<0>();  // the query loads are complete before the first DMA
   issue(0, 0);
-  if (n_sub > 1) issue(1, 1);
   for (int s = 0; s < n_sub; s += kPfRing) {
     step(s, std::integral_constant<int, 0>{});
     if (s + 1 < n_sub) step(s + 1, std::integral_constant<int, 1>{});
-    if (s + 2 < n_sub) step(s + 2, std::integral_constant<int, 2>{});
   }
   // ---- normalise and store: lane = query, acc[d] rows = dims 32d + 8(r/4) + 4g + r%4
   if (qrow < T) {
