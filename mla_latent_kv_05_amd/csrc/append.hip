@@ -209,13 +209,10 @@ hipError_t launch_append(const void* h, long long h_st, const void* w, const int
   const int N = d_c + d_r;
   int n_splits = 1;
   if (append_mfma_eligible(d, N, in_dtype, h_st, h, w)) {
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)append_gemm_mfma_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kApLds);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_raised{0};
+    if (const hipError_t e = ensure_dynamic_lds((const void*)append_gemm_mfma_kernel, (int)kApLds, lds_raised);
+        e != hipSuccess)
+      return e;
     n_splits = d / kApKS;
     dim3 grid(N / kApN, n_splits, (T + kApM - 1) / kApM);
     hipLaunchKernelGGL(append_gemm_mfma_kernel, grid, dim3(256), kApLds, s, (const uint16_t*)h, h_st,

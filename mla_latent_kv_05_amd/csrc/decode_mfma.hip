@@ -718,13 +718,10 @@ void decode_pipe_kernel(DecodeArgs a) {
 
 template <int FMT>
 static hipError_t launch_pipe(const DecodeArgs& a, int grid_x, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_pipe_kernel<FMT>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kPipeLds(FMT));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_raised{0};
+  if (const hipError_t e = ensure_dynamic_lds((const void*)decode_pipe_kernel<FMT>, kPipeLds(FMT), lds_raised);
+      e != hipSuccess)
+    return e;
   hipLaunchKernelGGL(decode_pipe_kernel<FMT>, dim3(grid_x, a.s_q), dim3(256), kPipeLds(FMT), s, a);
   return hipGetLastError();
 }

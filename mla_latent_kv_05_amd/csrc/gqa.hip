@@ -353,13 +353,10 @@ hipError_t launch_gqa_decode(const void* q_c, const void* q_r, const void* cache
                              int d_r, int bs, long long block_bytes, float scale, int q_dt, int kv_dt, void* out,
                              float* lse, int out_dt, bool mfma, hipStream_t s) {
   if (mfma) {
-    static bool attr_set = false;
-    if (!attr_set) {
-      const hipError_t e = hipFuncSetAttribute((const void*)gqa_decode_mfma_kernel,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, kGqLds);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_raised{0};
+    if (const hipError_t e = ensure_dynamic_lds((const void*)gqa_decode_mfma_kernel, kGqLds, lds_raised);
+        e != hipSuccess)
+      return e;
     const long long n_wg = (long long)B * n_g;  // one workgroup per (sequence, group)
     if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(gqa_decode_mfma_kernel, dim3((unsigned)n_wg), dim3(256), kGqLds, s, (const uint16_t*)q_c,
