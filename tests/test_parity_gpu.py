@@ -552,6 +552,20 @@ def test_prefill_mha_bf16_v3(T):
         assert np.all(np.abs(g[0] - v0) <= 1e-6 * np.abs(v0))
 
 
+@pytest.mark.parametrize("T,n_h", [(200, 3), (129, 9)])
+def test_prefill_mha_bf16_head_counts_off_the_xcd_multiple(T, n_h):
+    """MFMA kernel with head counts that are not a multiple of the 8 XCDs
+    (the grid is padded; the extra workgroups return)."""
+    say(f"prefill bf16 T={T} n_h={n_h}")
+    inp = inputs.prefill_inputs(120 + n_h, T, n_h=n_h, d_c=64)
+    q, k_c, k_r, v_c = _pf_dev(inp, "q", "k_c", "k_r", "v_c")
+    o, lse = binding.prefill_mha(q, k_c, k_r, v_c, inp["scale"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = _pf_oracle(inp)
+    assert_bf16_close(o.cpu().numpy().astype(np.float64), ref_o, f"prefill T={T} n_h={n_h}")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64), ref_lse, "prefill lse")
+
+
 def test_prefill_mha_full_size_sampled_heads():
     """4096-token prefill at V3 heads; the oracle checks every query of 3 heads
     (first, middle, last) and the rest is checked to be finite."""
@@ -690,6 +704,17 @@ def test_gqa_decode_bf16_v3(s_q, n_g, lens, force_generic):
     assert_lse_close(gl, ol, "gqa lse")
     g16, _ = _gqa_gpu(case, force_generic, out_dtype=torch.bfloat16)
     assert_bf16_close(g16, o, "gqa o bf16")
+
+
+def test_gqa_decode_bf16_four_tokens_of_eight_heads():
+    """16 groups of 8 heads with s_q = 4: the MFMA kernel's 32 rows are four
+    query tokens of eight heads (causal among the four)."""
+    say("gqa bf16 s_q=4 n_g=16")
+    case = inputs.gqa_case(43, B=4, seq_lens=np.array([4, 37, 300, 1029]), s_q=4, n_g=16)
+    g, gl = _gqa_gpu(case)
+    o, ol = _gqa_oracle(case)
+    assert_bf16_close(g, o, "gqa s_q=4")
+    assert_lse_close(gl, ol, "gqa s_q=4 lse")
 
 
 def test_gqa_decode_full_size_sampled():
