@@ -17,7 +17,7 @@ constexpr int kPlanThreads = 1024;
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[plan_lds_bytes(kPlanThreads)];
-  plan_body<kPlanThreads>(a, lds);
+  plan_body<kPlanThreads>(a, (__attribute__((address_space(3))) uint8_t*)lds);
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {

@@ -46,16 +46,19 @@ __device__ __forceinline__ int units_of(const PlanArgs& a, int n, int chunk) {
 // is split.  The cheapest c with waves <= kMaxAutoWaves wins (ties: larger c,
 // i.e. fewer partial results); if none fits, c = hi.
 // The planner's body for a workgroup of NT threads (NT / 64 >= kMaxAutoWaves + 1
-// waves); `lds` points at plan_lds_bytes(NT) bytes of the workgroup's LDS.
+// waves); `lds` points at plan_lds_bytes(NT) bytes of the workgroup's LDS
+// (a local-memory pointer: every access is a plain LDS instruction).
 template <int NT>
-__device__ __forceinline__ void plan_body(const PlanArgs& a, uint8_t* lds) {
+__device__ __forceinline__ void plan_body(const PlanArgs& a, __attribute__((address_space(3))) uint8_t* lds) {
+  typedef __attribute__((address_space(3))) int pl_int;
+  typedef __attribute__((address_space(3))) unsigned long long pl_u64;
   constexpr int kPlanThreads = NT;
   static_assert(NT / 64 >= kMaxAutoWaves + 1, "one wave per wave-count search plus one");
-  int* nb = (int*)lds;
-  unsigned long long* red = (unsigned long long*)(lds + kPlanLdsSeqs * 4);
-  int* scan = (int*)(lds + kPlanLdsSeqs * 4 + (NT / 64) * 8);
-  int& s_chunk = *(int*)(lds + kPlanLdsSeqs * 4 + (NT / 64) * 12);
-  int& s_waves = *(int*)(lds + kPlanLdsSeqs * 4 + (NT / 64) * 12 + 4);
+  pl_int* nb = (pl_int*)lds;
+  pl_u64* red = (pl_u64*)(lds + kPlanLdsSeqs * 4);
+  pl_int* scan = (pl_int*)(lds + kPlanLdsSeqs * 4 + (NT / 64) * 8);
+  pl_int& s_chunk = *(pl_int*)(lds + kPlanLdsSeqs * 4 + (NT / 64) * 12);
+  pl_int& s_waves = *(pl_int*)(lds + kPlanLdsSeqs * 4 + (NT / 64) * 12 + 4);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const bool in_lds = a.B <= kPlanLdsSeqs;
 

@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(const uint16_t* q, lon
                                                           int d_c, PlanArgs pa) {
   if (blockIdx.y == 0) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
-    if (blockIdx.x == 0) plan_body<256>(pa, smem_raw);
+    if (blockIdx.x == 0) plan_body<256>(pa, (lds_u8*)smem_raw);
     return;
   }
   absorb_tile<OUT_BF16>(q, q_st, w, out, o_st, T, n_h, d_h, d_c, blockIdx.y - 1, blockIdx.x);
