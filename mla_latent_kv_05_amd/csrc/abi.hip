@@ -130,7 +130,8 @@ int mla_expand_kv(const void* c_kv, int64_t c_stride_t, const void* w_uk, const 
   hipStream_t st = (hipStream_t)stream;
   const long long o_st = (long long)n_h * d_h;
   if (mfma && expand_gemm_eligible(c_stride_t, n_h * d_h, d_c, out_dtype, c_kv, w_uk, w_uv, k_c, v_c))
-    return launch_status(launch_expand_gemm(c_kv, c_stride_t, w_uk, w_uv, k_c, v_c, T, n_h * d_h, d_c, out_dtype, st));
+    return launch_status(launch_expand_gemm(c_kv, c_stride_t, w_uk, w_uv, k_c, v_c, T, n_h * d_h, d_c, out_dtype,
+                                                 current_cu_count(), st));
   // otherwise the up-projection kernel, one latent row per token feeding
   // every head (activation head stride 0)
   hipError_t e = launch_up_proj(c_kv, c_stride_t, 0, w_uk, k_c, o_st, T, n_h, d_c, d_h, act_dtype, w_dtype, out_dtype,

@@ -138,7 +138,7 @@ hipError_t launch_prefill(const void* q, const void* kc, const void* kr, const v
 bool expand_gemm_eligible(long long a_st, int N, int K, int out_dtype, const void* a, const void* w0,
                           const void* w1, const void* o0, const void* o1);
 hipError_t launch_expand_gemm(const void* a, long long a_st, const void* w0, const void* w1, void* o0, void* o1,
-                              int T, int N, int K, int out_dtype, hipStream_t s);
+                              int T, int N, int K, int out_dtype, int n_cu, hipStream_t s);
 bool gqa_mfma_eligible(int s_q, int n_h, int n_g, int d_h, int d_r, int bs, int q_dt, int kv_dt);
 hipError_t launch_gqa_decode(const void* q_c, const void* q_r, const void* cache, const int32_t* table,
                              int max_blocks, const int32_t* seq_lens, int B, int s_q, int n_h, int n_g, int d_h,

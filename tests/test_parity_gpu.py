@@ -631,6 +631,45 @@ def test_expand_kv_bf16_v3(T):
     assert_bf16_close(v16.float().cpu().numpy().astype(np.float64), rv, "v_c bf16")
 
 
+@pytest.mark.parametrize("T,n_h,d_c", [(1100, 128, 512), (4500, 16, 64)])
+def test_expand_kv_bf16_several_tiles_per_workgroup(T, n_h, d_c):
+    """More 256 x 256 output tiles than compute units, so each persistent
+    workgroup streams several tiles with its k-slice ring running on across
+    tile boundaries; d_c = 64 gives two k slices per tile, fewer than the
+    ring's four slots.  T is off the tile (ragged last tile)."""
+    say(f"expand_kv bf16 several tiles T={T} n_h={n_h} d_c={d_c}")
+    inp = inputs.prefill_inputs(230 + T, T, n_h=n_h, d_c=d_c)
+    c_kv, w_uk, w_uv = _pf_dev(inp, "c_kv", "w_uk", "w_uv")
+    k_c, v_c = binding.expand_kv(c_kv, w_uk, w_uv, 128, out_dtype=torch.float32)
+    k16, v16 = binding.expand_kv(c_kv, w_uk, w_uv, 128)
+    torch.cuda.synchronize()
+    rk, rv = oracle.expand_kv(*_pf_dec(inp, "c_kv", "w_uk", "w_uv"), n_h, 128)
+    assert_f32_close(k_c.cpu().numpy().astype(np.float64), rk, "k_c", tol=1e-5)
+    assert_f32_close(v_c.cpu().numpy().astype(np.float64), rv, "v_c", tol=1e-5)
+    assert_bf16_close(k16.float().cpu().numpy().astype(np.float64), rk, "k_c bf16")
+    assert_bf16_close(v16.float().cpu().numpy().astype(np.float64), rv, "v_c bf16")
+
+
+def test_expand_kv_bf16_full_size_sampled():
+    """The benchmarked size (4096 tokens, 128 heads of 128, d_c = 512) in the
+    launch configuration the benchmark times; the oracle computes 96 sampled
+    tokens (rows are independent)."""
+    T = 4096
+    say("expand_kv bf16 T=4096 sampled")
+    inp = inputs.prefill_inputs(250, T)
+    c_kv, w_uk, w_uv = _pf_dev(inp, "c_kv", "w_uk", "w_uv")
+    k16, v16 = binding.expand_kv(c_kv, w_uk, w_uv, 128)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.Generator(np.random.PCG64(251)).choice(T, 96, replace=False))
+    rows[-1] = T - 1
+    c_np, wk_np, wv_np = _pf_dec(inp, "c_kv", "w_uk", "w_uv")
+    rk, rv = oracle.expand_kv(c_np[rows], wk_np, wv_np, 128, 128)
+    got_k = k16.float().cpu().numpy().astype(np.float64)[rows]
+    got_v = v16.float().cpu().numpy().astype(np.float64)[rows]
+    assert_bf16_close(got_k, rk, "k_c bf16")
+    assert_bf16_close(got_v, rv, "v_c bf16")
+
+
 def test_expand_kv_bf16_heads_off_the_gemm_tile():
     """n_h * d_h = 192 is not a multiple of the GEMM's 256-row tile: the
     expansion takes the per-head up-projection kernel (shared latent row)."""
