@@ -20,6 +20,30 @@ __device__ __forceinline__ int nblocks_of(const PlanArgs& a, int b) {
   return n < 1 ? 1 : n;
 }
 
+// Sum or maximum over the 64 lanes of a wave, in registers only: two quad
+// permutes, the half-row and row mirrors (DPP) give every lane the total of
+// its 16-lane row, then the 16- and 32-lane swaps (permlane) combine the
+// rows.  Every lane returns the total.  (The LDS-routed shuffles a generic
+// reduction uses cost far more per step, and the search below chains many
+// of these reductions.)
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_i32(int v, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, true));  // row_half_mirror
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, true));  // row_mirror
+  const auto r16 = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  v = op((int)r16[0], (int)r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  return op((int)r32[0], (int)r32[1]);
+}
+struct OpAdd {
+  __device__ int operator()(int x, int y) const { return x + y; }
+};
+struct OpMax {
+  __device__ int operator()(int x, int y) const { return x > y ? x : y; }
+};
+
 // ceil(n / c) for 0 < n, c < 2^23 through a float reciprocal plus one correction
 __device__ __forceinline__ int ceil_div_small(int n, int c, float rc) {
   int q = (int)((float)(n + c - 1) * rc);
@@ -68,7 +92,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, __attribute__((addr
     if (in_lds) nb[b] = n;
     max_n = max(max_n, n);
   }
-  max_n = __reduce_max_sync(~0ull, max_n);
+  max_n = wave_reduce_i32(max_n, OpMax());
   if (lane == 0) red[wv] = (unsigned long long)max_n;
   __syncthreads();
   max_n = 0;
@@ -93,7 +117,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, __attribute__((addr
         v = lane < a.B ? ceil_div_small(nb_lane, c, rc) : 0;
       else
         for (int b = lane; b < a.B; b += 64) v += ceil_div_small(in_lds ? nb[b] : nblocks_of(a, b), c, rc);
-      return __reduce_add_sync(~0ull, v);  // DPP wave sum, uniform result
+      return wave_reduce_i32(v, OpAdd());  // uniform result
     };
     auto consider = [&](int c, int u) {
       const int waves = (u + a.slots_per_wave - 1) / a.slots_per_wave;
