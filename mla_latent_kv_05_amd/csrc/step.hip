@@ -18,6 +18,7 @@ namespace {
 typedef __attribute__((address_space(3))) uint8_t cu_lds;
 constexpr int kCuDc = 512, kCuDh = 128;
 constexpr int kCuMaxS = 4;         // partitions merged with all loads in flight
+constexpr int kCuBatch = 8;        // partitions per batch beyond that
 }  // namespace
 
 // 8 waves.  Each wave loads 16 whole rows of the head's weight block W^UV_h
@@ -103,12 +104,31 @@ __global__ __launch_bounds__(512) void combine_up_kernel(CombineUpArgs c) {
           for (int k = 0; k < kCuMaxS; ++k)
             if (k < n) add(expf(lv[j][k] - m), pv[j][k]);
         }
-      } else {  // many partitions (long contexts): one at a time
-        for (int k = 0; k < n; ++k) m = fmaxf(m, c.lse_part[first + (long long)k * R]);
-        if (m != -INFINITY)
-          for (int k = 0; k < n; ++k)
-            add(expf(c.lse_part[first + (long long)k * R] - m),
-                *(const u32x4_t*)(c.o_part + (first + (long long)k * R) * kCuDc + 8 * lane));
+      } else {  // many partitions (long contexts): online over batches of
+                // kCuBatch with every load of a batch in flight
+        for (int k0 = 0; k0 < n; k0 += kCuBatch) {
+          float lb[kCuBatch];
+          u32x4_t xb[kCuBatch];
+#pragma unroll
+          for (int i = 0; i < kCuBatch; ++i) {  // past the end: the last partition again, weight 0
+            const long long p = first + (long long)min(k0 + i, n - 1) * R;
+            lb[i] = c.lse_part[p];
+            xb[i] = *(const u32x4_t*)(c.o_part + p * kCuDc + 8 * lane);
+          }
+          float mb = m;
+#pragma unroll
+          for (int i = 0; i < kCuBatch; ++i)
+            if (k0 + i < n) mb = fmaxf(mb, lb[i]);
+          if (mb == -INFINITY) continue;  // only empty partitions so far
+          const float sc = expf(m - mb);  // 0 while nothing has been added
+          z *= sc;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] *= sc;
+          m = mb;
+#pragma unroll
+          for (int i = 0; i < kCuBatch; ++i)
+            if (k0 + i < n) add(expf(lb[i] - m), xb[i]);
+        }
       }
       const float iz = z > 0.f ? 1.f / z : 0.f;
 #pragma unroll

@@ -826,7 +826,8 @@ def test_gqa_path_equals_absorbed_decode_on_gpu():
 @pytest.mark.parametrize("kv,lens,s_q,splits", [("bf16", [2, 33, 64, 129, 1500], 1, 0),
                                                 ("bf16", [70, 4096, 9], 2, 3),
                                                 ("fp8", [2, 700, 2048], 2, 0),
-                                                ("int4", [64, 1000], 1, 1)])
+                                                ("int4", [64, 1000], 1, 1),
+                                                ("bf16", [9000, 300], 1, 13)])
 def test_decode_step_matches_separate_calls_and_oracle(kv, lens, s_q, splits):
     """mla_decode_step (absorb, attention, merge fused with W^UV) against the
     oracle's absorbed layer on the same rounded inputs, and equal to the three
