@@ -256,12 +256,21 @@ def test_full_size_workloads_sampled(name, seqs):
         assert_lse_close(gl[seqs], ol, name)
 
 
-def test_decode_step_full_size_sampled():
-    """mla_decode_step at the benchmark's headline shape (B=64, 8192 tokens,
-    automatic splits): absorb + attention + merge/W^UV against the oracle on
-    sampled sequences."""
-    say("decode step full size")
-    case = inputs.workload_case("v3_bf16_B64_ctx8192")
+@pytest.mark.parametrize("name,seqs", [
+    ("v3_bf16_B64_ctx8192", [0, 33, 63]),
+    ("v3_bf16_B128_ctxlogU128-32768", None),
+    ("v3_bf16_B4_ctx131072", [1]),
+])
+def test_decode_step_full_size_sampled(name, seqs):
+    """mla_decode_step at full workload sizes with automatic splits, as the
+    benchmark times it: absorb + attention + merge/W^UV against the oracle on
+    sampled sequences (the 131072-token sequences have 64 partitions each,
+    merged in batches by the fused tail)."""
+    say(f"decode step full size {name}")
+    case = inputs.workload_case(name)
+    if seqs is None:  # variable lengths: shortest, longest and a middle one
+        order = np.argsort(case.seq_lens)
+        seqs = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
     P = inputs.projection_weights(62, T_q=case.B)
     d = case_to_device(case)
     qn = bf16_dev(P["q_c"]).view(case.B, 1, 128, 128)
@@ -269,15 +278,17 @@ def test_decode_step_full_size_sampled():
                                  d["seq_lens"], bf16_dev(P["w_uv"]), d["softmax_scale"])
     torch.cuda.synchronize()
     g = o.float().cpu().numpy().astype(np.float64).reshape(case.B, 128, 128)
+    gl = lse.cpu().numpy().astype(np.float64).reshape(case.B, 1, 128)
+    del d
     assert np.all(np.isfinite(g))
     ql = oracle.absorb_q(oracle.bf16_to_f64(P["q_c"]), oracle.bf16_to_f64(P["w_uk"]), 128, 128)
     ql = oracle.bf16_to_f64(oracle.bf16_round_bits(ql))
-    for b in (0, 33, 63):
+    for b in seqs:
         _, qr, c, kr = oracle.decode_case_rows(case, b)
         ol, l = oracle.mqa_decode_rows(ql[b][None], qr, c, kr, case.softmax_scale)
         ref = oracle.up_proj_v(ol, oracle.bf16_to_f64(P["w_uv"]), 128, 128)[0]
         assert_bf16_close(g[b], ref, f"step seq {b}")
-        assert_lse_close(lse.cpu().numpy().astype(np.float64)[b], l, f"step lse {b}")
+        assert_lse_close(gl[b], l, f"step lse {b}")
 
 
 # ------------------------------------------------------------------ combine, projections
