@@ -172,8 +172,8 @@ __global__ __launch_bounds__(256) void expand_gemm_kernel(const uint16_t* a, lon
           u32x4_t v = *(const __attribute__((address_space(3))) u32x4_t*)(st + row * 256 + p * 16);
           if ((row >> 4) & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
           const int t = t0 + wt * 128 + tb * 32 + row;
-          if (t < T)
-            *(u32x4_t*)((uint16_t*)out + (long long)t * N + n0 + wn * 128 + (p ^ (row & 15)) * 8) = v;
+          if (t < T)  // streamed out: keep L2 for the operands
+            __builtin_nontemporal_store(v, (u32x4_t*)((uint16_t*)out + (long long)t * N + n0 + wn * 128 + (p ^ (row & 15)) * 8));
         }
       }
     } else {
