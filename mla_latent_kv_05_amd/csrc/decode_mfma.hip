@@ -230,32 +230,32 @@ void decode_pipe_kernel(DecodeArgs a) {
     };
     auto dma_one = [&](const i32x4_t& rs, int m0b, int s, int i) {
       if (!STAGED) {
-        dma16_m0(rs, dma_src_offset(i * 256 + tid), m0b + i * 4096 + w_s * 1024);
+        dma16_m0_stream(rs, dma_src_offset(i * 256 + tid), m0b + i * 4096 + w_s * 1024);
       } else if (INT) {
         // block: [64 x content codes | 64 x RoPE codes | 64 x parameters];
         // subtile half s & 1 of each part
         constexpr int cb = kIntCodeB(FMT);
         const int half = s & 1;
         if (i < kDma - 1) {  // content codes, 4 KB per instruction
-          dma16_m0(rs, half * cb + ((i * 4 + w) * 64 + lane) * 16, m0b + (i * 4 + w_s) * 1024);
+          dma16_m0_stream(rs, half * cb + ((i * 4 + w) * 64 + lane) * 16, m0b + (i * 4 + w_s) * 1024);
         } else {  // RoPE codes (64 chunks) then parameters (144 chunks), one per thread
           const int p = tid;
           if (p < kIntMiscChunks) {
             const int src = p < kIntRopeB / 16 ? 2 * cb + half * kIntRopeB + p * 16
                                                : 2 * cb + 2 * kIntRopeB + half * kIntPrmB + (p - kIntRopeB / 16) * 16;
-            dma16_m0(rs, src, m0b + cb + w_s * 1024);
+            dma16_m0_stream(rs, src, m0b + cb + w_s * 1024);
           }
         }
       } else {
         const int half = s & 1;
         if (i < 4) {         // content codes: 16 KB, 4 x 1 KB per wave
-          dma16_m0(rs, half * kF8Codes + ((i * 4 + w) * 64 + lane) * 16, m0b + (i * 4 + w_s) * 1024);
+          dma16_m0_stream(rs, half * kF8Codes + ((i * 4 + w) * 64 + lane) * 16, m0b + (i * 4 + w_s) * 1024);
         } else if (i == 4) {  // RoPE keys: 4 KB
-          dma16_m0(rs, kBlk * kDc + half * kF8Kr + (w * 64 + lane) * 16, m0b + kF8Codes + w_s * 1024);
+          dma16_m0_stream(rs, kBlk * kDc + half * kF8Kr + (w * 64 + lane) * 16, m0b + kF8Codes + w_s * 1024);
         } else if (lane < 8) {  // scales: 128 B to the scale ring (every wave, same bytes)
           const int ring = __builtin_amdgcn_readfirstlane(
               (int)(uint32_t)(uintptr_t)(smem + kF8ScaleOff + (s % kF8ScaleSlots) * 128));
-          dma16_m0(rs, kBlk * (kDc + 2 * kDr) + half * (kSub * 4) + lane * 16, ring);
+          dma16_m0_stream(rs, kBlk * (kDc + 2 * kDr) + half * (kSub * 4) + lane * 16, ring);
         }
       }
     };

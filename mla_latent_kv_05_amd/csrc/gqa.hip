@@ -100,13 +100,13 @@ __global__ __launch_bounds__(256, 1) void gqa_decode_mfma_kernel(const uint16_t*
     for (int i = 0; i < 8; ++i) {
       const int t = i * 4 + (lane >> 4);
       const int src = min(t, last) * (kGqDh * 2) + (((lane & 15) ^ gq_f16(t)) << 4);
-      dma16_m0(rk, src, m0b + i * 1024);
+      dma16_m0_stream(rk, src, m0b + i * 1024);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int t = i * 4 + (lane >> 4);
       const int src = min(t, last) * (kGqDh * 2) + (((lane & 15) ^ gq_f16(t)) << 4);
-      dma16_m0(rv, src, m0b + kGqKcB + kGqKrB + i * 1024);
+      dma16_m0_stream(rv, src, m0b + kGqKcB + kGqKrB + i * 1024);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
