@@ -57,6 +57,9 @@ separately written encoder.
 GQLA's GQA path (gqa_decode_rows) is pinned by its algebraic equality with
 the MQA-absorb path over the same weights (the page's claim) and by torch's
 scaled_dot_product_attention with grouped key/value heads.
+The layer's projections (project: c^KV, k^R, c^Q, q^C and the per-head
+q^R) are pinned element by element on a tiny layer with explicit sums and
+complex-number rotation at non-zero positions.
 The cache producer (cache_append) is pinned by an element-by-element
 brute force with complex-number rotation, by torch's own bf16 and fp8
 casts for its encoders, and by appending a toy layer's tokens and decoding

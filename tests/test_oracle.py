@@ -474,6 +474,55 @@ def test_cache_append_bruteforce_tiny():
     assert np.all(out[0, 1] == 7.0) and np.all(out[1, 0] == 7.0)
 
 
+def test_project_bruteforce_tiny():
+    """Every output of the layer's projections, recomputed element by element
+    on a tiny layer with explicit sums and complex-number rotation (itwiki
+    "Multi-head latent attention", "Structure": joint KV compression gives
+    c^Q = W^DQ h and q^C = W^UQ c^Q, head i owning rows i*d_h .. (i+1)*d_h-1;
+    decoupled RoPE gives q^R_i = RoPE(W^QR_i c^Q) per head and the shared
+    k^R = RoPE(W^KR h)).  Fails if W^QR reads h instead of c^Q, if RoPE is
+    dropped from either part, if a head's slice is transposed or taken from
+    the wrong rows, or if the rotation pairs the wrong elements."""
+    rng = np.random.default_rng(21)
+    B, T, d, d_cq, n_h, d_h, d_r, d_c = 2, 3, 5, 3, 2, 3, 4, 4
+    dims = {"d": d, "n_h": n_h, "d_h": d_h, "d_c": d_c, "d_cq": d_cq, "d_r": d_r}
+    W = {"dims": dims}
+    for name, (o, i) in {"w_dq": (d_cq, d), "w_uq": (n_h * d_h, d_cq), "w_qr": (n_h * d_r, d_cq),
+                         "w_dkv": (d_c, d), "w_kr": (d_r, d)}.items():
+        W[name] = rng.standard_normal((o, i))
+    h = rng.standard_normal((B, T, d))
+    pos = np.array([3, 0, 11])  # non-zero positions (0 is the identity rotation)
+    c_kv, k_r, q_c, q_r = oracle.project(h, W, pos)
+
+    def rot(vec, p):  # pair (k, k + n/2) as one complex number, times e^{i p theta_k}
+        n = len(vec)
+        out = [0.0] * n
+        for k in range(n // 2):
+            th = p * 10000.0 ** (-2.0 * k / n)
+            z = complex(vec[k], vec[k + n // 2]) * complex(math.cos(th), math.sin(th))
+            out[k], out[k + n // 2] = z.real, z.imag
+        return out
+
+    for b in range(B):
+        for t in range(T):
+            x = h[b, t]
+            cq = [sum(W["w_dq"][m, k] * x[k] for k in range(d)) for m in range(d_cq)]
+            ckv = [sum(W["w_dkv"][m, k] * x[k] for k in range(d)) for m in range(d_c)]
+            kr = rot([sum(W["w_kr"][m, k] * x[k] for k in range(d)) for m in range(d_r)], pos[t])
+            assert np.allclose(c_kv[b, t], ckv, rtol=1e-13, atol=1e-13)
+            assert np.allclose(k_r[b, t], kr, rtol=1e-13, atol=1e-13)
+            for i in range(n_h):
+                qc = [sum(W["w_uq"][i * d_h + j, m] * cq[m] for m in range(d_cq)) for j in range(d_h)]
+                qr = rot([sum(W["w_qr"][i * d_r + j, m] * cq[m] for m in range(d_cq)) for j in range(d_r)],
+                         pos[t])
+                assert np.allclose(q_c[b, t, i], qc, rtol=1e-13, atol=1e-13), (b, t, i)
+                assert np.allclose(q_r[b, t, i], qr, rtol=1e-13, atol=1e-13), (b, t, i)
+    # the rotation is not the identity here, so the test can see RoPE
+    x0 = h[0, 0]
+    cq0 = W["w_dq"] @ x0
+    assert np.max(np.abs(q_r[0, 0, 1] - W["w_qr"][d_r:2 * d_r] @ cq0)) > 1e-3
+
+
 def test_cache_append_then_decode_equals_mha_layer():
     """Append the toy layer's 256 tokens to a paged f32 cache through a
     permuted slot mapping, then decode the last token in MQA mode: equals the
