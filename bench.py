@@ -1,16 +1,29 @@
 #!/usr/bin/env python
 """Absorbed-MLA decode benchmark on one MI355X.
 
-One step = the whole hot path for one batch: W^UK absorption into the query
-(mla_absorb_q) -> paged split-KV decode over the latent cache with the
-log-sum-exp combine (mla_decode_absorbed) -> W^UV up-projection
-(mla_up_proj_v).  Inputs are seeded synthetic tensors already resident in HBM;
-the timed region rotates through several physically distinct copies of the
-latent cache so repeated steps cannot be served from the 256 MB last-level
-cache.
+One step = the whole hot path for one batch, as one mla_decode_step call:
+W^UK absorption into the query with the split planner in the same launch ->
+paged split-KV attention over the latent cache -> partition merge fused with
+the W^UV up-projection.  Inputs are seeded synthetic tensors already resident
+in HBM; the timed region rotates through several physically distinct copies
+of the latent cache so repeated steps cannot be served from the 256 MB
+last-level cache.
+
+Before the W warm-up steps the device is settled with ~300 ms of bf16 GEMMs
+(none of the measured path's data or kernels): started from idle, MI355X
+needs that long under matrix load to reach the clock it holds while serving,
+and a few-millisecond run would otherwise time the ramp.
+
+A second back-to-back loop of the same steps, issued one stage per call,
+carries HIP events recorded by this script around every attention launch:
+they give the kernel's own time for the roofline object.  A per-stage
+breakdown and the separate entry points (mla_absorb_q, mla_decode_absorbed,
+mla_up_proj_v) follow, then the secondary paths (cache producer, MHA-mode
+prefill, GQA-path decode), an HBM copy probe and the float64 oracle on a
+bounded sample of the workload on the host cores.
 
 Prints one JSON line.  Metric: latent-cache bytes read per second (TB/s) of
-the whole step, with decode tokens/s and the roofline fraction alongside.
+the whole step, with decode tokens/s and the roofline fractions alongside.
 """
 
 from __future__ import annotations
@@ -65,22 +78,17 @@ def measured_traffic(workload: str):
         return None
 
 
-def cpu_baseline(case, P, seconds: float) -> dict:
-    """The float64 oracle on a bounded sample of the same workload: whole
-    sequences (gather pages, absorb, decode, up-project) until `seconds` of
-    CPU time have been spent; reported in the GPU's unit."""
+def _oracle_rate(case, P, seconds: float, start: int = 0):
+    """The float64 oracle on whole sequences of the workload (gather pages,
+    absorb, decode, up-project) in batch order from `start` until `seconds`
+    have passed; returns (latent bytes/s, tokens/s, sequences, seconds)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
     qc = oracle.bf16_to_f64(P["q_c"]).reshape(case.B, case.s_q, case.n_h, case.d_h)
     wuk = oracle.bf16_to_f64(P["w_uk"])
     wuv = oracle.bf16_to_f64(P["w_uv"])
     done, nbytes, t0 = 0, 0, time.perf_counter()
-    while True:  # sequences in batch order (wrapping) until the time budget is spent
-        b = done % case.B
+    while True:
+        b = (start + done) % case.B
         _, qr, c, kr = oracle.decode_case_rows(case, b)
         ql = oracle.absorb_q(qc[b], wuk, case.n_h, case.d_h)
         o_lat, _ = oracle.mqa_decode_rows(ql, qr, c, kr, case.softmax_scale)
@@ -89,12 +97,112 @@ def cpu_baseline(case, P, seconds: float) -> dict:
         nbytes += int(case.seq_lens[b]) * case.row_bytes
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
-    return {"value": nbytes / el / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} sequences (batch order, {case.B} in the batch) of the workload, whole step per "
-                      f"sequence (page gather, W^UK absorb, decode, W^UV) in float64 numpy, {el:.1f} s; "
-                      f"rate = latent bytes of those sequences / time",
-            "tok_s": done * case.s_q / el, "seconds": el}
+            return nbytes / el, done * case.s_q / el, done, el
+
+
+def cpu_baseline(case, P, seconds: float) -> dict:
+    """The float64 oracle on a bounded sample of the same workload, reported
+    in the GPU's unit: three runs with the BLAS thread pool as numpy has it
+    (median reported) and one run limited to a single thread (the per-core
+    figure), each taking a quarter of `seconds`."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        pools = threadpool_info()
+    except Exception:  # noqa: BLE001
+        threadpool_info, threadpool_limits, pools = None, None, []
+    blas = [{k: p.get(k) for k in ("internal_api", "version", "num_threads", "architecture", "threading_layer")}
+            for p in pools if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in pools] or [os.cpu_count() or 1])
+    part = seconds / 4
+    runs = [_oracle_rate(case, P, part, start=r * 7) for r in range(3)]
+    rates = sorted(r[0] for r in runs)
+    med = rates[1]
+    med_run = next(r for r in runs if r[0] == med)
+    single = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            r1 = _oracle_rate(case, P, part, start=21)
+        single = {"value": r1[0] / 1e12, "unit": "TB/s", "cores": 1, "tok_s": r1[1], "sequences": r1[2],
+                  "seconds": r1[3]}
+    return {"value": med / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole sequences of the workload in batch order ({case.B} in the batch; page gather, "
+                      f"W^UK absorb, decode, W^UV in float64 numpy), {part:.1f} s per run; median of 3 runs "
+                      f"({', '.join(str(r[2]) for r in runs)} sequences); rate = latent bytes of those "
+                      f"sequences / time",
+            "runs_TBps": [r / 1e12 for r in rates], "tok_s": med_run[1], "seconds": sum(r[3] for r in runs),
+            "per_core": single, "blas": blas}
+
+
+def stream_probe(dev, mib: int = 2048, reps: int = 10) -> dict:
+    """Achievable HBM stream rate on this device: a plain device-to-device
+    copy of `mib` MiB (read + write bytes per second), timed with events."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    src.fill_(3)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"kind": "device copy", "bytes_moved": 2 * n, "ms": ms, "GBps": 2 * n / (ms * 1e-3) / 1e9,
+            "frac_of_peak": 2 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def settle_device(dev, ms: float) -> dict:
+    """Bring the device out of idle before the warm-up steps.  MI355X raises
+    its compute clock over the first ~100-300 ms of sustained matrix load; a
+    few-millisecond run started from idle measures that ramp, not the clock a
+    continuously serving GPU runs at.  The load is plain bf16 GEMMs on
+    buffers of their own (none of the measured path's data or kernels)."""
+    import torch
+    if ms <= 0:
+        return {"kind": None, "ms": 0.0}
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            a @ a
+        n += 4
+        torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) * 1e3
+    del a
+    return {"kind": "bf16 GEMM 8192x8192x8192 (not the measured path)", "gemms": n, "ms": el}
+
+
+def device_info(dev) -> dict:
+    """Software versions and the device's compute clock as the driver reports
+    it (the sclk levels of the card in sysfs, where readable)."""
+    import glob
+
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    info = {"torch": torch.__version__, "hip": torch.version.hip, "device": p.name,
+            "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "hbm_GiB": round(p.total_memory / 2 ** 30, 1)}
+    try:
+        info["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        info["rocm"] = None
+    sclk = []
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            lines = [ln.strip() for ln in open(f) if ln.strip()]
+        except OSError:
+            continue
+        if lines:
+            sclk.append({"card": f.split("/")[4], "levels": lines})
+    info["sclk"] = sclk or None
+    return info
 
 
 def copy_probe(mib: int) -> int:
@@ -263,6 +371,10 @@ def main() -> int:
     ap.add_argument("--no-append", action="store_true", help="skip the cache-producer measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the MHA-mode prefill measurement")
     ap.add_argument("--no-gqa", action="store_true", help="skip the GQA-path decode measurement")
+    ap.add_argument("--no-stream-probe", action="store_true", help="skip the device-copy bandwidth probe")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="milliseconds of bf16 GEMM load before the warm-up steps, to bring the device from its "
+                         "idle clock to the clock it holds under sustained load (0 = none)")
     ap.add_argument("--step-api", choices=("fused", "separate"), default="fused",
                     help="time the step as one mla_decode_step call (absorb, attention, merge fused with W^UV) "
                          "or as mla_absorb_q + mla_decode_absorbed + mla_up_proj_v")
@@ -319,32 +431,37 @@ def main() -> int:
 
     ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
           for k in ("a", "b", "c", "d", "k0", "k1")}
-    for lst in ev.values():  # materialise the HIP events before the library is handed their handles
-        for e in lst:
-            e.record()
-    torch.cuda.synchronize()
 
     qn4 = q_c.view(B, s_q, n_h, d_h)
     ws_step = binding.decode_step_workspace(B, s_q, n_h, d_c, table.shape[1], args.splits, device=dev)
+    step_args = lambda i: (qn4, w_uk, q_rope, caches[i % len(caches)], table, lens, w_uv, scale)  # noqa: E731
+    step_kw = dict(kv_dtype=kv_dtype, num_splits=args.splits, workspace=ws_step, out=o.view(B, s_q, n_h, d_h),
+                   lse=lse)
 
-    def fused_step(i, timed=False):
+    def fused_step(i):
         """absorb + attention + merge fused with W^UV: one library call, three launches"""
-        if timed:
-            binding.decode_kernel_events(ev["k0"][i], ev["k1"][i])
-        binding.decode_step(qn4, w_uk, q_rope, caches[i % len(caches)], table, lens, w_uv, scale,
-                            kv_dtype=kv_dtype, num_splits=args.splits, workspace=ws_step,
-                            out=o.view(B, s_q, n_h, d_h), lse=lse)
+        binding.decode_step(*step_args(i), **step_kw)
 
-    def step(i, timed=False):
-        if args.step_api == "fused" and not timed:
-            fused_step(i)
-            return
+    def staged_step(i, tag=("k0", "k1"), only_kernel=True):
+        """the same three launches as three calls of mla_decode_step_stages,
+        with this script's own events on the launch stream around the
+        attention stage (and, for the breakdown, around the other two)"""
+        if not only_kernel:
+            ev["a"][i].record()
+        binding.decode_step_stages(binding.MLA_STAGE_ABSORB, *step_args(i), **step_kw)
+        ev[tag[0]][i].record()
+        binding.decode_step_stages(binding.MLA_STAGE_ATTEND, *step_args(i), **step_kw)
+        ev[tag[1]][i].record()
+        binding.decode_step_stages(binding.MLA_STAGE_MERGE, *step_args(i), **step_kw)
+        if not only_kernel:
+            ev["d"][i].record()
+
+    def separate_step(i, timed=False):
         if timed:
             ev["a"][i].record()
         binding.absorb_q(q_c, w_uk, out=q_lat)
         if timed:
             ev["b"][i].record()
-            binding.decode_kernel_events(ev["k0"][i], ev["k1"][i])
         binding.decode(q_lat.view(B, s_q, n_h, d_c), q_rope, caches[i % len(caches)], table, lens, scale,
                        kv_dtype=kv_dtype, d_r=d_r, out=o_lat, lse=lse, workspace=ws, num_splits=args.splits)
         if timed:
@@ -353,12 +470,15 @@ def main() -> int:
         if timed:
             ev["d"][i].record()
 
+    step = fused_step if args.step_api == "fused" else separate_step
+    settle = settle_device(dev, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     def timed_loop(run_steps, n):
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         start.record()
         run_steps(n)
@@ -400,22 +520,33 @@ def main() -> int:
     if graph_ms is None:
         t_wall = t_eager
     ms_step = graph_ms if graph_ms is not None else eager_ms
-    # per-call breakdown and the attention kernel's own time (events between
-    # the calls; not part of the timed loops above)
+
+    # The attention kernel's own time: the step again, back to back for the
+    # same number of steps, as three stage calls with events recorded by this
+    # script on the launch stream around the attention launch (the library
+    # records nothing).  The events sit between launches, so this loop's
+    # ms/step is reported beside the headline one.
+    def kernel_steps(n):
+        for i in range(n):
+            staged_step(i)
+    staged_ms, _ = timed_loop(kernel_steps, args.steps)
+    kernel_all = [ev["k0"][i].elapsed_time(ev["k1"][i]) for i in range(args.steps)]
+    kernel_ms = float(np.mean(kernel_all))
+    kernel_med = float(np.median(kernel_all))
+    # per-stage breakdown (events around every stage; not a timed loop)
     for i in range(args.steps):
-        step(i, timed=True)
+        staged_step(i, only_kernel=False)
     torch.cuda.synchronize()
-    absorb_ms = float(np.mean([ev["a"][i].elapsed_time(ev["b"][i]) for i in range(args.steps)]))
+    absorb_ms = float(np.mean([ev["a"][i].elapsed_time(ev["k0"][i]) for i in range(args.steps)]))
+    merge_ms = float(np.mean([ev["k1"][i].elapsed_time(ev["d"][i]) for i in range(args.steps)]))
+    kernel_bd_ms = float(np.mean([ev["k0"][i].elapsed_time(ev["k1"][i]) for i in range(args.steps)]))
+    # the separate entry points (absorb, decode call with planner + merge, up-projection)
+    for i in range(args.steps):
+        separate_step(i, timed=True)
+    torch.cuda.synchronize()
     decode_ms = float(np.mean([ev["b"][i].elapsed_time(ev["c"][i]) for i in range(args.steps)]))
+    sep_absorb_ms = float(np.mean([ev["a"][i].elapsed_time(ev["b"][i]) for i in range(args.steps)]))
     up_ms = float(np.mean([ev["c"][i].elapsed_time(ev["d"][i]) for i in range(args.steps)]))
-    kernel_ms = float(np.mean([ev["k0"][i].elapsed_time(ev["k1"][i]) for i in range(args.steps)]))
-    if args.step_api == "fused":
-        # the fused step runs the same attention kernel; its time comes from
-        # the events the library records around it, in a pass of its own
-        for i in range(args.steps):
-            fused_step(i, timed=True)
-        torch.cuda.synchronize()
-        kernel_ms = float(np.mean([ev["k0"][i].elapsed_time(ev["k1"][i]) for i in range(args.steps)]))
 
     latent_bytes = case.latent_bytes
     value = latent_bytes / (ms_step * 1e-3) / 1e12
@@ -426,8 +557,8 @@ def main() -> int:
         for i in range(s_q):
             vis = L - s_q + i + 1
             flops += vis * (2 * n_h * (d_c + d_r) + 2 * n_h * d_c)
-    # roofline of the dominant kernel (the attention kernel alone, timed by
-    # HIP events the library records around its launch on this stream)
+    # roofline of the dominant kernel: the attention kernel alone, from the
+    # events this script records around its launch in the back-to-back loop
     if case.kv_dtype == "bf16":
         achieved = latent_bytes / (kernel_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -440,8 +571,12 @@ def main() -> int:
     roof["traffic"] = measured_traffic(args.workload)
     roof["kernel"] = kname
     roof["kernel_ms"] = kernel_ms
+    roof["kernel_ms_median"] = kernel_med
+    roof["timing"] = ("HIP events recorded by bench.py on the launch stream around every attention launch of a "
+                      "back-to-back loop of whole steps (mla_decode_step_stages, one stage per call)")
     roof["units_per_launch"] = {"tokens": int(case.seq_lens.sum()), "bytes_per_token": case.row_bytes,
                                 "flops": flops}
+    step_frac = value * 1e3 / HBM_PEAK_GBS
 
     rec = {
         "metric": METRIC, "value": value, "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
@@ -456,11 +591,20 @@ def main() -> int:
                    "cache_copies": len(caches), "launch": args.launch, "step_api": args.step_api},
         "decode_tok_s": tok_s, "latent_bytes": latent_bytes,
         "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
-        "roofline_frac_step": value * 1e3 / HBM_PEAK_GBS if case.kv_dtype == "bf16" else None,
-        "absorb_ms": absorb_ms, "decode_call_ms": decode_ms, "decode_kernel_ms": kernel_ms, "up_proj_ms": up_ms,
-        "decode_call_TBps": latent_bytes / (decode_ms * 1e-3) / 1e12, "wall_s": t_wall,
+        # call-level fraction: latent bytes over the whole step (planner,
+        # absorption, attention, merge, W^UV); roofline.frac is the kernel's
+        "roofline_frac_step": step_frac if case.kv_dtype == "bf16" else None,
+        "kernel_loop_ms_per_step": staged_ms,
+        "stages_ms": {"absorb_plan": absorb_ms, "attention": kernel_bd_ms, "merge_up": merge_ms},
+        "separate_calls_ms": {"absorb_q": sep_absorb_ms, "decode_absorbed": decode_ms, "up_proj_v": up_ms,
+                              "decode_absorbed_TBps": latent_bytes / (decode_ms * 1e-3) / 1e12},
+        "wall_s": t_wall,
+        "settle": settle,
         "roofline": roof,
+        "env": device_info(dev),
     }
+    if not args.no_stream_probe:
+        rec["stream_probe"] = stream_probe(dev)
     if case.kv_dtype in ("bf16", "fp8") and not args.no_append:
         rec["cache_append"] = bench_append(case, args.steps, dev)
     if not args.no_prefill:
@@ -472,6 +616,7 @@ def main() -> int:
         rec["cpu_baseline"]["cpu_model"] = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
                                                  if l.startswith("model name")), platform.processor())
         rec["cpu_baseline"]["affinity_cores"] = len(os.sched_getaffinity(0))
+        rec["cpu_baseline"]["numpy"] = np.__version__
     print(json.dumps(rec))
     return 0
 

@@ -14,8 +14,9 @@
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *    never allocates, frees or retains memory; it keeps no state between calls
- *    apart from a per-device cache of kernel attributes and the profiling
- *    events armed by mla_decode_kernel_events (per host thread).
+ *    apart from a per-device cache of kernel attributes (compute-unit count,
+ *    raised LDS limits).  Whatever one call leaves for a later one (a split
+ *    plan, partial results) lives in a caller-owned workspace.
  *  - Every call enqueues work on `stream` (a hipStream_t passed as void*; NULL
  *    is the default stream) and returns without synchronising.
  *  - Tensors are row-major with the last dimension contiguous.  Strides are
@@ -151,18 +152,6 @@ int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_ca
                         void* o_lat, float* lse, int flags, void* stream);
 
 /*
- * mla_decode_kernel_events -- profiling aid.  Arms two caller-owned HIP
- * events (hipEvent_t passed as void*) for the next mla_decode_absorbed call
- * made by the calling host thread: that call records `before` on its stream
- * just before it launches its attention kernel and `after` just after, so the
- * elapsed time between them covers that one kernel (the split planner and the
- * partial-result merge are outside), and then disarms.  NULL, NULL disarms.
- * The events must stay valid until that call has returned; the library does
- * not retain them afterwards.  Always returns MLA_OK.
- */
-int mla_decode_kernel_events(void* before, void* after);
-
-/*
  * mla_combine_lse -- merge split-KV partial results (log-sum-exp combine):
  *   lse[n] = log sum_s exp(lse_part[n,s]),
  *   out[n,:] = sum_s exp(lse_part[n,s] - lse[n]) * o_part[n,s,:]
@@ -255,8 +244,37 @@ int mla_decode_step(const void* q_nope, const void* w_uk, const void* q_rope, co
                     int kv_dtype, int num_splits, void* workspace, size_t workspace_bytes, void* o, float* lse,
                     void* stream);
 
+/* mla_decode_step_stages -- mla_decode_step one stage (or several) per
+ * call, for callers that put their own work or timing between the stages:
+ *   MLA_STAGE_ABSORB  q_lat = W^UK_h^T q_nope into the workspace, with the
+ *                     split plan of the batch (from seq_lens)
+ *   MLA_STAGE_ATTEND  the attention kernel over the paged cache: partial rows
+ *                     of split sequences, final latent rows of unsplit ones
+ *                     and their lse, all in the workspace (lse also in `lse`)
+ *   MLA_STAGE_MERGE   merge of the partitions fused with o = W^UV_h o_lat
+ * Stages run in this order within a call.  Arguments, alignment, workspace
+ * size and status codes are those of mla_decode_step, which equals one call
+ * with MLA_STAGE_ALL.  Every piece of state a stage leaves for the next
+ * (q_lat, plan, partial rows) is in the caller's workspace, so the stages
+ * of one step must be given the same workspace and arguments, in order, on
+ * one stream (or ordered by the caller); nothing is kept by the library.
+ * ATTEND without a preceding ABSORB on that workspace, or MERGE without a
+ * preceding ATTEND, gives meaningless results; the kernels check every plan
+ * entry against the call's shapes and the sequences' current lengths, so no
+ * access leaves the buffers.
+ * stages == 0 or bits outside MLA_STAGE_ALL: MLA_ERR_INVALID_ARG. */
+#define MLA_STAGE_ABSORB 1
+#define MLA_STAGE_ATTEND 2
+#define MLA_STAGE_MERGE 4
+#define MLA_STAGE_ALL 7
+int mla_decode_step_stages(const void* q_nope, const void* w_uk, const void* q_rope, const void* kv_cache,
+                           const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                           const void* w_uv, int B, int s_q, int n_h, int d_h, int d_c, int d_r, int block_size,
+                           float softmax_scale, int kv_dtype, int num_splits, void* workspace,
+                           size_t workspace_bytes, void* o, float* lse, int stages, void* stream);
+
 /* mla_decode_step_workspace_bytes -- workspace of mla_decode_step (the
- * decode workspace plus bf16 q_lat and merged-row buffers); 0 on bad sizes. */
+ * decode workspace plus a bf16 q_lat buffer); 0 on bad sizes. */
 size_t mla_decode_step_workspace_bytes(int B, int s_q, int n_h, int d_c, int max_blocks_per_seq, int num_splits);
 
 /* mla_expand_kv -- MHA-mode keys and values from the latent (itwiki

@@ -20,6 +20,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "mla_decode.h")
 
 MLA_F32, MLA_BF16, MLA_FP8_E4M3, MLA_INT4, MLA_INT2 = 0, 1, 2, 3, 4
 MLA_FLAG_FORCE_GENERIC = 1
+MLA_STAGE_ABSORB, MLA_STAGE_ATTEND, MLA_STAGE_MERGE, MLA_STAGE_ALL = 1, 2, 4, 7
 
 _lib = None
 
@@ -37,7 +38,6 @@ _SIGS = {
                                        _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
     "mla_combine_lse": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int,
                                    _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
-    "mla_decode_kernel_events": (_c.c_int, [_c.c_void_p, _c.c_void_p]),
     "mla_cache_append": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                     _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int,
                                     _c.c_int, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
@@ -46,6 +46,11 @@ _SIGS = {
                                    _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                    _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int, _c.c_void_p, _c.c_size_t,
                                    _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "mla_decode_step_stages": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                          _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int,
+                                          _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int,
+                                          _c.c_void_p, _c.c_size_t, _c.c_void_p, _c.c_void_p, _c.c_int,
+                                          _c.c_void_p]),
     "mla_decode_step_workspace_bytes": (_c.c_size_t, [_c.c_int] * 6),
     "mla_gqa_decode": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p,
                                   _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float,
@@ -199,16 +204,6 @@ def decode(q_lat: torch.Tensor, q_rope: torch.Tensor, kv_cache: torch.Tensor, bl
     return out, (lse if with_lse else None)
 
 
-def decode_kernel_events(before: torch.cuda.Event, after: torch.cuda.Event) -> None:
-    """Arm two timing events for the attention kernel of the next decode()
-    call on this thread (see mla_decode_kernel_events).  The events must
-    already exist on the device: record each once beforehand."""
-    h0, h1 = before.cuda_event, after.cuda_event
-    if not h0 or not h1:
-        raise RuntimeError("record the events once before arming them")
-    _check(lib().mla_decode_kernel_events(h0, h1), "mla_decode_kernel_events")
-
-
 def cache_append_workspace(T: int, d: int, d_c: int, d_r: int, device="cuda") -> torch.Tensor:
     n = lib().mla_cache_append_workspace_bytes(T, d, d_c, d_r)
     if n == 0:
@@ -248,6 +243,25 @@ def decode_step(q_nope: torch.Tensor, w_uk: torch.Tensor, q_rope: torch.Tensor, 
     """Whole absorbed decode step: absorb, attention, merge + up-projection.
     q_nope [B, s_q, n_h, d_h], q_rope [B, s_q, n_h, d_r], weights [n_h*d_h, d_c]
     (all bf16).  Returns (o [B, s_q, n_h, d_h] bf16, lse [B, s_q, n_h] or None)."""
+    return _step(None, q_nope, w_uk, q_rope, kv_cache, block_table, seq_lens, w_uv, softmax_scale, kv_dtype, d_c,
+                 block_size, num_splits, workspace, with_lse, out, lse)
+
+
+def decode_step_stages(stages: int, q_nope: torch.Tensor, w_uk: torch.Tensor, q_rope: torch.Tensor,
+                       kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, w_uv: torch.Tensor,
+                       softmax_scale: float, kv_dtype: int | None = None, d_c: int = 512, block_size: int = 64,
+                       num_splits: int = 0, workspace: torch.Tensor | None = None, with_lse: bool = True,
+                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """decode_step restricted to the MLA_STAGE_* bits in `stages`; the stages
+    of one step share `workspace` (required), `out` and `lse`."""
+    if workspace is None:
+        raise ValueError("decode_step_stages: the stages of a step share a caller-owned workspace")
+    return _step(stages, q_nope, w_uk, q_rope, kv_cache, block_table, seq_lens, w_uv, softmax_scale, kv_dtype, d_c,
+                 block_size, num_splits, workspace, with_lse, out, lse)
+
+
+def _step(stages, q_nope, w_uk, q_rope, kv_cache, block_table, seq_lens, w_uv, softmax_scale, kv_dtype, d_c,
+          block_size, num_splits, workspace, with_lse, out, lse):
     _gpu(q_nope, w_uk, q_rope, kv_cache, block_table, seq_lens, w_uv)
     B, s_q, n_h, d_h = q_nope.shape
     d_r = q_rope.shape[-1]
@@ -264,10 +278,13 @@ def decode_step(q_nope: torch.Tensor, w_uk: torch.Tensor, q_rope: torch.Tensor, 
         out = torch.empty((B, s_q, n_h, d_h), dtype=torch.bfloat16, device=q_nope.device)
     if with_lse and lse is None:
         lse = torch.empty((B, s_q, n_h), dtype=torch.float32, device=q_nope.device)
-    _check(lib().mla_decode_step(_ptr(q_nope), _ptr(w_uk), _ptr(q_rope), _ptr(kv_cache), _ptr(block_table),
-                                 max_blocks, _ptr(seq_lens), _ptr(w_uv), B, s_q, n_h, d_h, d_c, d_r, block_size,
-                                 float(softmax_scale), kv_dtype, num_splits, _ptr(workspace), workspace.numel(),
-                                 _ptr(out), _ptr(lse) if with_lse else None, _stream()), "mla_decode_step")
+    args = (_ptr(q_nope), _ptr(w_uk), _ptr(q_rope), _ptr(kv_cache), _ptr(block_table), max_blocks, _ptr(seq_lens),
+            _ptr(w_uv), B, s_q, n_h, d_h, d_c, d_r, block_size, float(softmax_scale), kv_dtype, num_splits,
+            _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse) if with_lse else None)
+    if stages is None:
+        _check(lib().mla_decode_step(*args, _stream()), "mla_decode_step")
+    else:
+        _check(lib().mla_decode_step_stages(*args, int(stages), _stream()), "mla_decode_step_stages")
     return out, (lse if with_lse else None)
 
 

@@ -143,7 +143,7 @@ void decode_pipe_kernel(DecodeArgs a) {
   const int qi = blockIdx.y;
   const int R = a.s_q * kHeads;
   const int head = w * 32 + l32;
-  const int n_units = ((const WsHeader*)a.ws_header)->n_units;
+  const int n_units = min(((const WsHeader*)a.ws_header)->n_units, a.units_max);
   const float scale2 = a.scale * kLog2e;
 
   int off_qk[4];
@@ -166,6 +166,11 @@ void decode_pipe_kernel(DecodeArgs a) {
   const int w_s = __builtin_amdgcn_readfirstlane(w);  // wave index as a scalar
   for (int unit = xcd_slot(blockIdx.x, gridDim.x); unit < n_units; unit += gridDim.x) {
     const int4 wk = a.work[unit];
+    // a plan entry outside this call's shapes (a workspace that holds no
+    // plan of this batch) is skipped: wrong results, never a stray access.
+    // (first > end is a planned empty partition: it still writes its empty
+    // partial result.)
+    if (wk.x < 0 || wk.x >= a.B || wk.y < 0 || wk.z > a.max_blocks || wk.z - wk.y > kMaxUnitPages) continue;
     const int b = wk.x;
     const bool final_out = wk.w < 0;           // the sequence is not split
     const int L = final_out ? ~wk.w : wk.w;    // its length
@@ -203,7 +208,11 @@ void decode_pipe_kernel(DecodeArgs a) {
       const int32_t* trow = a.table + (long long)b * a.max_blocks + wk.y;
       const int pg0 = tid < npg ? trow[tid] : 0;
       const int pg1 = tid + 256 < npg ? trow[tid + 256] : 0;
+      const int len_now = a.seq_lens[b];
       wait_vm<0>();
+      // table slots past the sequence's pages may hold anything: an entry
+      // reaching beyond them (not planned from these lengths) is skipped
+      if (wk.z > max(1, (len_now + kBlk - 1) / kBlk)) continue;
       if (tid < npg) tab[tid] = pg0;
       if (tid + 256 < npg) tab[tid + 256] = pg1;
 #pragma unroll
@@ -649,9 +658,13 @@ void decode_pipe_kernel(DecodeArgs a) {
     const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     const long long orow0 = ((long long)b * a.s_q + qi) * kHeads;  // first output row of this (b, qi)
     const long long prow0 = (long long)unit * R + qi * kHeads;  // partial slot = unit index
-    const bool bf16_out = final_out ? a.out_dtype != 0 : a.part_bf16 != 0;
-    float* o32 = final_out ? (float*)a.out + orow0 * kDc : a.o_part + prow0 * kDc;
-    uint16_t* o16 = final_out ? (uint16_t*)a.out + orow0 * kDc : (uint16_t*)a.o_part + prow0 * kDc;
+    // rows go to the output when the sequence is not split and an output is
+    // given; otherwise to the unit's partial slot (a decode step passes no
+    // output: its merge reads unsplit rows from there too)
+    const bool to_out = final_out && a.out != nullptr;
+    const bool bf16_out = to_out ? a.out_dtype != 0 : a.part_bf16 != 0;
+    float* o32 = to_out ? (float*)a.out + orow0 * kDc : a.o_part + prow0 * kDc;
+    uint16_t* o16 = to_out ? (uint16_t*)a.out + orow0 * kDc : (uint16_t*)a.o_part + prow0 * kDc;
     if (g == 0) {
       if (!final_out)
         a.lse_part[prow0 + head] = lse_v;

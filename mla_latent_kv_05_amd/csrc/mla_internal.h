@@ -85,6 +85,7 @@ struct DecodeArgs {
   int part_bf16;
   long long block_bytes;
   int max_blocks;
+  int units_max;  // plan entries the workspace has room for
   int B, s_q, n_h, d_c, d_r, block_size;
   float scale;
   int q_dtype, kv_dtype, out_dtype;
@@ -107,11 +108,12 @@ struct PlanArgs {
 struct CombineUpArgs {
   const int2* seq;
   const float* lse_part;
-  const uint16_t* o_part;  // bf16 partial rows [unit][s_q * n_h][512]
-  const uint16_t* o_fin;   // bf16 final rows of unsplit sequences [B * s_q][n_h][512]
+  const uint16_t* o_part;  // bf16 rows [unit][s_q * n_h][512]: partial rows of split
+                           // sequences, final rows of unsplit ones
   const uint16_t* w_uv;    // [n_h * 128, 512]
   uint16_t* out;           // [B * s_q][n_h][128]
   float* lse;              // [B * s_q][n_h] or null
+  int units_max;           // plan entries the workspace has room for
   int B, s_q, n_h;
 };
 

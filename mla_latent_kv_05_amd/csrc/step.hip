@@ -48,6 +48,9 @@ __global__ __launch_bounds__(512) void combine_up_kernel(CombineUpArgs c) {
   for (int j = 0; j < 4; ++j) {
     const int t = t0 + j * 8 + w;
     sq[j] = t < T ? c.seq[t / c.s_q] : make_int2(0, 0);
+    // a partition list outside the workspace (no plan of this batch there):
+    // read the unsplit row instead
+    if (sq[j].x < 0 || sq[j].y < 0 || sq[j].x > c.units_max - sq[j].y) sq[j] = make_int2(0, 1);
   }
   u32x4_t wv[16];
   {
@@ -67,8 +70,8 @@ __global__ __launch_bounds__(512) void combine_up_kernel(CombineUpArgs c) {
       pv[j][k] = u32x4_t{0, 0, 0, 0};
     }
     if (t >= T) continue;
-    if (sq[j].y <= 1) {  // unsplit: the attention kernel wrote the final row
-      pv[j][0] = *(const u32x4_t*)(c.o_fin + ((long long)t * c.n_h + h) * kCuDc + 8 * lane);
+    if (sq[j].y <= 1) {  // unsplit: the attention kernel wrote the final row into the unit's slot
+      pv[j][0] = *(const u32x4_t*)(c.o_part + first * kCuDc + 8 * lane);
     } else if (sq[j].y <= kCuMaxS) {
 #pragma unroll
       for (int k = 0; k < kCuMaxS; ++k)

@@ -19,8 +19,9 @@ OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE = 0, -1, -2, -3, -4
 def test_header_functions_exported():
     names = binding.header_functions()
     assert set(names) == {"mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_absorbed",
-                          "mla_combine_lse", "mla_up_proj_v", "mla_status_string", "mla_decode_kernel_events",
+                          "mla_combine_lse", "mla_up_proj_v", "mla_status_string",
                           "mla_cache_append", "mla_cache_append_workspace_bytes", "mla_expand_kv", "mla_gqa_decode", "mla_decode_step",
+                          "mla_decode_step_stages",
                           "mla_decode_step_workspace_bytes",
                           "mla_prefill_mha"}
     L = binding.lib()
@@ -171,7 +172,7 @@ def test_decode_step_argument_validation():
     base = L.mla_decode_workspace_bytes(4, 2, 128, 512, 16, 0)
     step = L.mla_decode_step_workspace_bytes(4, 2, 128, 512, 16, 0)
     if base:  # sizes need the device's compute-unit count
-        assert step >= base + 2 * 4 * 2 * 128 * 512 * 2
+        assert step >= base + 4 * 2 * 128 * 512 * 2
     else:
         assert step == 0
         step = 1 << 30
@@ -183,3 +184,10 @@ def test_decode_step_argument_validation():
     assert L.mla_decode_step(*args(n_h=64)) == UNSUPPORTED       # off the MFMA attention shape
     assert L.mla_decode_step(*args(o=FAKE + 8)) == MISALIGNED
     assert L.mla_decode_step(*args(ws=None)) == WORKSPACE
+    st = lambda stages, **k: L.mla_decode_step_stages(*args(**k)[:-1], stages, None)
+    assert st(0) == INVALID
+    assert st(8) == INVALID
+    assert st(-1) == INVALID
+    assert st(binding.MLA_STAGE_ATTEND, wuv=None) == INVALID
+    assert st(binding.MLA_STAGE_MERGE, d_h=64) == UNSUPPORTED
+    assert st(binding.MLA_STAGE_ALL, ws=None) == WORKSPACE

@@ -205,6 +205,40 @@ def test_determinism_and_paging_invariance():
     assert np.array_equal(a, c) and np.array_equal(al, cl)
 
 
+def _subbatch(case, rows):
+    """The same sequences (cache pages, queries) in another batch: row i of the
+    new batch is row rows[i] of `case` (repeats allowed)."""
+    import copy
+    c = copy.copy(case)
+    rows = np.asarray(rows)
+    c.B = len(rows)
+    c.seq_lens = case.seq_lens[rows].copy()
+    nblk = int(((c.seq_lens + case.block_size - 1) // case.block_size).max())
+    c.block_table = np.ascontiguousarray(case.block_table[rows, :nblk])
+    c.q_lat = np.ascontiguousarray(case.q_lat[rows])
+    c.q_rope = np.ascontiguousarray(case.q_rope[rows])
+    return c
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_batch_composition_invariance(splits):
+    """A sequence's result does not depend on the batch around it (its
+    neighbours, its position, the batch size, repeats of it).  With a fixed
+    split count every sequence is cut the same way in every batch, so the
+    results are bit-identical; automatic planning may cut it differently,
+    which changes only the merge's rounding."""
+    say(f"batch composition splits={splits}")
+    case = inputs.decode_case(31, B=6, seq_lens=np.array([3000, 65, 1, 777, 4096, 130]), **V3)
+    base, bl = run_decode(case, num_splits=splits)
+    for rows in ([3], [1, 3, 5], [4, 4, 0, 2, 3, 3, 1, 5, 4], [5, 4, 3, 2, 1, 0]):
+        g, gl = run_decode(_subbatch(case, rows), num_splits=splits)
+        if splits:
+            assert np.array_equal(g, base[rows]) and np.array_equal(gl, bl[rows]), rows
+        else:
+            assert np.abs(g - base[rows]).max() <= 2e-3, rows
+            assert np.abs(gl - bl[rows]).max() <= 1e-4, rows
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_long_sequence_many_splits(out_dtype):
     """One long sequence over the whole device: many partitions, merged by the
@@ -877,3 +911,67 @@ def test_decode_step_matches_separate_calls_and_oracle(kv, lens, s_q, splits):
     assert_bf16_close(g, ref_o, f"step {kv}")
     if kv != "int4":
         assert_lse_close(lse.cpu().numpy().astype(np.float64).reshape(case.B, s_q, 128), np.stack(ref_l), "step lse")
+
+
+@pytest.mark.parametrize("kv,lens,splits", [("bf16", [2, 33, 1500, 4096], 0), ("fp8", [700, 64], 2)])
+def test_decode_step_stages_equal_the_whole_step(kv, lens, splits):
+    """mla_decode_step_stages run one stage per call (on one workspace, with
+    the caller's own events between the calls) gives the bytes of the
+    single mla_decode_step call, and the attention stage's events bracket
+    that one launch."""
+    say(f"decode step stages {kv} splits={splits}")
+    lens = np.array(lens, dtype=np.int32)
+    case = inputs.decode_case(64, B=len(lens), seq_lens=lens, s_q=1, kv_dtype=kv, **V3)
+    P = inputs.projection_weights(65, T_q=case.B)
+    d = case_to_device(case)
+    qn, wuk, wuv = bf16_dev(P["q_c"]).view(case.B, 1, 128, 128), bf16_dev(P["w_uk"]), bf16_dev(P["w_uv"])
+    args = (qn, wuk, d["q_rope"], d["kv_cache"], d["block_table"], d["seq_lens"], wuv, d["softmax_scale"])
+    kw = dict(kv_dtype=d["kv_dtype"], num_splits=splits)
+    o, lse = binding.decode_step(*args, **kw)
+    ws = binding.decode_step_workspace(case.B, 1, 128, 512, d["block_table"].shape[1], splits)
+    ws.fill_(0xff)  # nothing carried over from an earlier call
+    o2 = torch.full_like(o, float("nan"))
+    lse2 = torch.full_like(lse, float("nan"))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for st in (binding.MLA_STAGE_ABSORB, binding.MLA_STAGE_ATTEND, binding.MLA_STAGE_MERGE):
+        if st == binding.MLA_STAGE_ATTEND:
+            e0.record()
+        binding.decode_step_stages(st, *args, workspace=ws, out=o2, lse=lse2, **kw)
+        if st == binding.MLA_STAGE_ATTEND:
+            e1.record()
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+    assert e0.elapsed_time(e1) > 0.0
+    # two stages in one call, then the third
+    o3 = torch.full_like(o, float("nan"))
+    binding.decode_step_stages(binding.MLA_STAGE_ABSORB | binding.MLA_STAGE_ATTEND, *args, workspace=ws, out=o3,
+                               lse=lse2, **kw)
+    binding.decode_step_stages(binding.MLA_STAGE_MERGE, *args, workspace=ws, out=o3, lse=lse2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o3.view(torch.int16))
+
+
+def test_decode_step_stages_without_a_plan_stay_in_bounds():
+    """The attention and merge stages on a workspace that holds no plan of
+    this batch (all bytes 0x7f or 0x80: huge or negative unit counts and
+    entries) skip every entry outside the call's shapes: the calls finish,
+    and a full step on the same workspace afterwards is correct."""
+    say("decode step stages on a workspace without a plan")
+    lens = np.array([100, 2000], dtype=np.int32)
+    case = inputs.decode_case(66, B=2, seq_lens=lens, s_q=1, **V3)
+    P = inputs.projection_weights(67, T_q=case.B)
+    d = case_to_device(case)
+    qn, wuk, wuv = bf16_dev(P["q_c"]).view(case.B, 1, 128, 128), bf16_dev(P["w_uk"]), bf16_dev(P["w_uv"])
+    args = (qn, wuk, d["q_rope"], d["kv_cache"], d["block_table"], d["seq_lens"], wuv, d["softmax_scale"])
+    ref, ref_l = binding.decode_step(*args, kv_dtype=d["kv_dtype"])
+    ws = binding.decode_step_workspace(case.B, 1, 128, 512, d["block_table"].shape[1], 0)
+    out = torch.empty_like(ref)
+    for fill in (0x7f, 0x80):
+        ws.fill_(fill)
+        binding.decode_step_stages(binding.MLA_STAGE_ATTEND | binding.MLA_STAGE_MERGE, *args, workspace=ws,
+                                   out=out, kv_dtype=d["kv_dtype"])
+        torch.cuda.synchronize()
+    binding.decode_step(*args, kv_dtype=d["kv_dtype"], workspace=ws, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int16), out.view(torch.int16))
