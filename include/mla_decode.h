@@ -53,6 +53,7 @@ extern "C" {
 #define MLA_ERR_MISALIGNED (-3)  /* a pointer/stride breaks the 16-byte alignment rule */
 #define MLA_ERR_WORKSPACE (-4)   /* workspace missing or smaller than required */
 #define MLA_ERR_LAUNCH (-5)      /* the HIP runtime rejected a kernel launch */
+#define MLA_ERR_TOO_LARGE (-6)   /* more than the fixed scratch of mla_decode_step_noalloc */
 
 /* flags for mla_decode_absorbed */
 #define MLA_FLAG_FORCE_GENERIC 1 /* use the portable fp32 kernel even when the
@@ -272,6 +273,36 @@ int mla_decode_step_stages(const void* q_nope, const void* w_uk, const void* q_r
                            const void* w_uv, int B, int s_q, int n_h, int d_h, int d_c, int d_r, int block_size,
                            float softmax_scale, int kv_dtype, int num_splits, void* workspace,
                            size_t workspace_bytes, void* o, float* lse, int stages, void* stream);
+
+/* mla_decode_step_noalloc -- mla_decode_step for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same step with no workspace
+ * argument.  Its plan, bf16 partial rows and absorbed queries live in one
+ * fixed device array of MLA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library
+ * holds on every GPU it runs on until the process ends; the call allocates
+ * and frees nothing.
+ *  - Arguments, requirements and status codes as mla_decode_step, and
+ *    MLA_ERR_TOO_LARGE (nothing enqueued) when the step needs more scratch:
+ *    bf16 q_lat (B*s_q*n_h*d_c*2 bytes) plus room for the partial rows of
+ *    max(compute units / s_q, B * ceil(max_blocks_per_seq / 512)) partitions
+ *    (B * max(num_splits, that ceil) with explicit splits), each
+ *    s_q*n_h*d_c*2 bytes.  That covers B = 64 at 8K or 16K context with
+ *    s_q <= 2, B = 128 up to 32K and B = 4 at 128K on a 256-unit GPU.
+ *  - Automatic planning is limited to one wave of partitions (at most one
+ *    per compute unit and query token, unless the 512-page cap per
+ *    partition needs more), so its plan, and with it the rounding of the
+ *    merge, can differ from mla_decode_step's where that one would plan
+ *    more; with an explicit num_splits the results are bit-identical.
+ *  - Every call on a GPU shares that GPU's scratch and leaves its contents
+ *    there: calls that overlap on one GPU (two streams, two host threads)
+ *    race and must be ordered by the caller.  No part of the scratch needs
+ *    to start at zero: every byte a call reads is written earlier in the
+ *    same call. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int mla_decode_step_noalloc(const void* q_nope, const void* w_uk, const void* q_rope, const void* kv_cache,
+                            const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                            const void* w_uv, int B, int s_q, int n_h, int d_h, int d_c, int d_r, int block_size,
+                            float softmax_scale, int kv_dtype, int num_splits, void* o, float* lse, void* stream);
 
 /* mla_decode_step_workspace_bytes -- workspace of mla_decode_step (the
  * decode workspace plus a bf16 q_lat buffer); 0 on bad sizes. */

@@ -52,6 +52,10 @@ _SIGS = {
                                           _c.c_void_p, _c.c_size_t, _c.c_void_p, _c.c_void_p, _c.c_int,
                                           _c.c_void_p]),
     "mla_decode_step_workspace_bytes": (_c.c_size_t, [_c.c_int] * 6),
+    "mla_decode_step_noalloc": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                           _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int,
+                                           _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float, _c.c_int, _c.c_int,
+                                           _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "mla_gqa_decode": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p,
                                   _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float,
                                   _c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
@@ -258,6 +262,31 @@ def decode_step_stages(stages: int, q_nope: torch.Tensor, w_uk: torch.Tensor, q_
         raise ValueError("decode_step_stages: the stages of a step share a caller-owned workspace")
     return _step(stages, q_nope, w_uk, q_rope, kv_cache, block_table, seq_lens, w_uv, softmax_scale, kv_dtype, d_c,
                  block_size, num_splits, workspace, with_lse, out, lse)
+
+
+def decode_step_noalloc(q_nope: torch.Tensor, w_uk: torch.Tensor, q_rope: torch.Tensor, kv_cache: torch.Tensor,
+                        block_table: torch.Tensor, seq_lens: torch.Tensor, w_uv: torch.Tensor, softmax_scale: float,
+                        out: torch.Tensor, lse: torch.Tensor | None = None, kv_dtype: int | None = None,
+                        d_c: int = 512, block_size: int = 64, num_splits: int = 0):
+    """decode_step without a workspace (mla_decode_step_noalloc): `out` (and
+    `lse`, if wanted) must be given, since nothing is allocated here either."""
+    _gpu(q_nope, w_uk, q_rope, kv_cache, block_table, seq_lens, w_uv, out)
+    B, s_q, n_h, d_h = q_nope.shape
+    d_r = q_rope.shape[-1]
+    for t in (q_nope, w_uk, q_rope, w_uv, kv_cache, block_table, out):
+        assert t.is_contiguous()
+    assert q_rope.shape == (B, s_q, n_h, d_r) and w_uk.shape == (n_h * d_h, d_c) and w_uv.shape == (n_h * d_h, d_c)
+    assert out.shape == (B, s_q, n_h, d_h) and out.dtype == torch.bfloat16
+    if lse is not None:
+        assert lse.shape == (B, s_q, n_h) and lse.dtype == torch.float32 and lse.is_contiguous()
+    if kv_dtype is None:
+        kv_dtype = _dt(kv_cache)
+    _check(lib().mla_decode_step_noalloc(_ptr(q_nope), _ptr(w_uk), _ptr(q_rope), _ptr(kv_cache), _ptr(block_table),
+                                         block_table.shape[1], _ptr(seq_lens), _ptr(w_uv), B, s_q, n_h, d_h, d_c, d_r,
+                                         block_size, float(softmax_scale), kv_dtype, num_splits, _ptr(out),
+                                         _ptr(lse) if lse is not None else None, _stream()),
+           "mla_decode_step_noalloc")
+    return out, lse
 
 
 def _step(stages, q_nope, w_uk, q_rope, kv_cache, block_table, seq_lens, w_uv, softmax_scale, kv_dtype, d_c,

@@ -5,6 +5,7 @@
 #include <algorithm>
 
 #include <atomic>
+#include <mutex>
 
 namespace mla {
 int mfma_max_unit_pages();
@@ -71,6 +72,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_MISALIGNED: return "pointer or stride is not 16-byte aligned";
     case MLA_ERR_WORKSPACE: return "workspace missing or too small";
     case MLA_ERR_LAUNCH: return "kernel launch failed";
+    case MLA_ERR_TOO_LARGE: return "problem needs more than the fixed scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -293,6 +295,7 @@ int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_ca
   p.min_chunk = fast ? 8 : 4;
   p.max_chunk = mfma_max_unit_pages();
   p.units_max = L.units_max;
+  p.max_waves = kMaxAutoWaves;
   hipError_t e = launch_plan(p, st);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   e = fast ? launch_decode_mfma(a, grid_x, st) : launch_decode_generic(a, grid_x, st);
@@ -304,6 +307,9 @@ int mla_decode_absorbed(const void* q_lat, const void* q_rope, const void* kv_ca
   return launch_status(e);
 }
 
+// workgroups of the step's attention launch (one per compute unit and query token)
+static int step_grid(int n_cu, int s_q) { return n_cu / s_q > 0 ? n_cu / s_q : 1; }
+
 static size_t step_extra_bytes(int B, int s_q, int n_h, int d_c) {
   return align256((size_t)B * s_q * n_h * d_c * 2);  // the absorbed queries (bf16)
 }
@@ -313,40 +319,47 @@ size_t mla_decode_step_workspace_bytes(int B, int s_q, int n_h, int d_c, int max
   return base ? align256(base) + step_extra_bytes(B, s_q, n_h, d_c) : 0;
 }
 
-int mla_decode_step_stages(const void* q_nope, const void* w_uk, const void* q_rope, const void* kv_cache,
-                           const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
-                           const void* w_uv, int B, int s_q, int n_h, int d_h, int d_c, int d_r, int block_size,
-                           float softmax_scale, int kv_dtype, int num_splits, void* workspace,
-                           size_t workspace_bytes, void* o, float* lse, int stages, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the step entry points (everything but the
+// workspace / scratch).
+int step_check(const void* q_nope, const void* w_uk, const void* q_rope, const void* kv_cache,
+               const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens, const void* w_uv, int B,
+               int s_q, int n_h, int d_h, int d_c, int d_r, int block_size, float softmax_scale, int kv_dtype,
+               int num_splits, const void* o) {
   if (B <= 0 || s_q <= 0 || n_h <= 0 || d_h <= 0 || d_c <= 0 || d_r < 0 || block_size <= 0 ||
       max_blocks_per_seq <= 0 || num_splits < 0)
     return MLA_ERR_INVALID_ARG;
-  if (stages <= 0 || (stages & ~MLA_STAGE_ALL)) return MLA_ERR_INVALID_ARG;
   if (!q_nope || !w_uk || !q_rope || !kv_cache || !block_table || !seq_lens || !w_uv || !o)
     return MLA_ERR_INVALID_ARG;
   if (kv_dtype < MLA_F32 || kv_dtype > MLA_INT2) return MLA_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return MLA_ERR_INVALID_ARG;
-  if (!workspace) return MLA_ERR_WORKSPACE;
   DecodeShape shp{B, s_q, n_h, d_c, d_r, block_size, max_blocks_per_seq, num_splits};
   if (!mfma_eligible(shp, MLA_BF16, kv_dtype) || d_h != 128 || s_q > 16) return MLA_ERR_UNSUPPORTED;
   if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_rope) || !aligned16(kv_cache) || !aligned16(w_uv) ||
-      !aligned16(o) || !aligned16(workspace))
+      !aligned16(o))
     return MLA_ERR_MISALIGNED;
-  const int n_cu = current_cu_count();
-  if (n_cu <= 0) return MLA_ERR_LAUNCH;
-  const WsLayout L = layout_for(shp, n_cu);
-  const size_t dec_bytes = align256(L.total);
-  if (workspace_bytes < dec_bytes + step_extra_bytes(B, s_q, n_h, d_c)) return MLA_ERR_WORKSPACE;
-  uint8_t* ws = (uint8_t*)workspace;
+  return MLA_OK;
+}
+
+// The step's launches on a checked set of arguments, with its plan, partial
+// rows and absorbed queries in `ws` laid out as L (partials in bf16) followed
+// by q_lat at dec_bytes.
+//   1. absorption into ws (bf16 q_lat), the split planner riding in the same
+//      launch (automatic plans of at most max_waves waves of units);
+//   2. the attention kernel (every unit writes its rows to its partial slot,
+//      final rows for unsplit sequences);
+//   3. merge + up-projection.
+// Everything one stage leaves for the next lives in ws.
+int step_launch(const void* q_nope, const void* w_uk, const void* q_rope, const void* kv_cache,
+                const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens, const void* w_uv, int B,
+                int s_q, int n_h, int d_h, int d_c, int d_r, int block_size, float softmax_scale, int kv_dtype,
+                int num_splits, void* o, float* lse, uint8_t* ws, const WsLayout& L, size_t dec_bytes, int n_cu,
+                int max_waves, int stages, hipStream_t st) {
   const int T_q = B * s_q;
   uint16_t* q_lat = (uint16_t*)(ws + dec_bytes);
-  hipStream_t st = (hipStream_t)stream;
-
-  // 1. absorption into the workspace (bf16 q_lat), the split planner riding
-  //    in the same launch; 2. the attention kernel (every unit writes its
-  //    rows to its partial slot, final rows for unsplit sequences); 3. merge
-  //    + up-projection.  Everything one stage leaves for the next lives in
-  //    the workspace.
   DecodeArgs a{};
   a.q_lat = q_lat;
   a.q_rope = q_rope;
@@ -367,7 +380,7 @@ int mla_decode_step_stages(const void* q_nope, const void* w_uk, const void* q_r
   a.B = B; a.s_q = s_q; a.n_h = n_h; a.d_c = d_c; a.d_r = d_r; a.block_size = block_size;
   a.scale = softmax_scale;
   a.q_dtype = MLA_BF16; a.kv_dtype = kv_dtype; a.out_dtype = MLA_BF16;
-  const int grid_x = n_cu / s_q > 0 ? n_cu / s_q : 1;
+  const int grid_x = step_grid(n_cu, s_q);
   if (stages & MLA_STAGE_ABSORB) {
     PlanArgs p{};
     p.seq_lens = seq_lens;
@@ -381,6 +394,7 @@ int mla_decode_step_stages(const void* q_nope, const void* w_uk, const void* q_r
     p.min_chunk = 8;
     p.max_chunk = mfma_max_unit_pages();
     p.units_max = L.units_max;
+    p.max_waves = max_waves;
     if (launch_absorb_plan(q_nope, (long long)n_h * d_h, w_uk, q_lat, (long long)n_h * d_c, T_q, n_h, d_h, d_c, p,
                            st) != hipSuccess)
       return MLA_ERR_LAUNCH;
@@ -402,6 +416,62 @@ int mla_decode_step_stages(const void* q_nope, const void* w_uk, const void* q_r
   return MLA_OK;
 }
 
+// ------------------------------------------------ scratch of the no-allocation step
+// Device memory of mla_decode_step_noalloc: plan, bf16 partial rows and the
+// absorbed queries of one step.  A file-scope device array, so the library
+// holds one on every GPU it runs on until the process ends and no call
+// allocates.  In host code `scratch` only names the symbol; its device
+// address (one per GPU) comes from hipGetSymbolAddress with that GPU current.
+constexpr size_t kNoAllocScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// the current device's address of `scratch` (looked up once per device)
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_LAUNCH;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_LAUNCH;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_step_stages(const void* q_nope, const void* w_uk, const void* q_rope, const void* kv_cache,
+                           const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                           const void* w_uv, int B, int s_q, int n_h, int d_h, int d_c, int d_r, int block_size,
+                           float softmax_scale, int kv_dtype, int num_splits, void* workspace,
+                           size_t workspace_bytes, void* o, float* lse, int stages, void* stream) {
+  if (stages <= 0 || (stages & ~MLA_STAGE_ALL)) return MLA_ERR_INVALID_ARG;
+  if (const int e = step_check(q_nope, w_uk, q_rope, kv_cache, block_table, max_blocks_per_seq, seq_lens, w_uv, B,
+                               s_q, n_h, d_h, d_c, d_r, block_size, softmax_scale, kv_dtype, num_splits, o);
+      e != MLA_OK)
+    return e;
+  if (!workspace) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_MISALIGNED;
+  const int n_cu = current_cu_count();
+  if (n_cu <= 0) return MLA_ERR_LAUNCH;
+  DecodeShape shp{B, s_q, n_h, d_c, d_r, block_size, max_blocks_per_seq, num_splits};
+  const WsLayout L = layout_for(shp, n_cu);
+  const size_t dec_bytes = align256(L.total);
+  if (workspace_bytes < dec_bytes + step_extra_bytes(B, s_q, n_h, d_c)) return MLA_ERR_WORKSPACE;
+  return step_launch(q_nope, w_uk, q_rope, kv_cache, block_table, max_blocks_per_seq, seq_lens, w_uv, B, s_q, n_h,
+                     d_h, d_c, d_r, block_size, softmax_scale, kv_dtype, num_splits, o, lse, (uint8_t*)workspace, L,
+                     dec_bytes, n_cu, kMaxAutoWaves, stages, (hipStream_t)stream);
+}
+
 int mla_decode_step(const void* q_nope, const void* w_uk, const void* q_rope, const void* kv_cache,
                     const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens, const void* w_uv,
                     int B, int s_q, int n_h, int d_h, int d_c, int d_r, int block_size, float softmax_scale,
@@ -410,6 +480,34 @@ int mla_decode_step(const void* q_nope, const void* w_uk, const void* q_rope, co
   return mla_decode_step_stages(q_nope, w_uk, q_rope, kv_cache, block_table, max_blocks_per_seq, seq_lens, w_uv, B,
                                 s_q, n_h, d_h, d_c, d_r, block_size, softmax_scale, kv_dtype, num_splits, workspace,
                                 workspace_bytes, o, lse, MLA_STAGE_ALL, stream);
+}
+
+int mla_decode_step_noalloc(const void* q_nope, const void* w_uk, const void* q_rope, const void* kv_cache,
+                            const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                            const void* w_uv, int B, int s_q, int n_h, int d_h, int d_c, int d_r, int block_size,
+                            float softmax_scale, int kv_dtype, int num_splits, void* o, float* lse, void* stream) {
+  if (const int e = step_check(q_nope, w_uk, q_rope, kv_cache, block_table, max_blocks_per_seq, seq_lens, w_uv, B,
+                               s_q, n_h, d_h, d_c, d_r, block_size, softmax_scale, kv_dtype, num_splits, o);
+      e != MLA_OK)
+    return e;
+  const int n_cu = current_cu_count();
+  if (n_cu <= 0) return MLA_ERR_LAUNCH;
+  // room for every plan the capped planner can make: one wave of units, or
+  // one per page-capped partition of each sequence, or the explicit count
+  const long long cap = mfma_max_unit_pages();
+  const long long per_seq_min = (max_blocks_per_seq + cap - 1) / cap;
+  const long long per_seq = num_splits > 0 ? (num_splits > per_seq_min ? num_splits : per_seq_min) : per_seq_min;
+  long long units = (long long)B * per_seq;
+  if (num_splits <= 0 && units < step_grid(n_cu, s_q)) units = step_grid(n_cu, s_q);
+  if (units > (1ll << 30)) return MLA_ERR_TOO_LARGE;
+  const WsLayout L = ws_layout_units(B, s_q, n_h, d_c, units, 2);
+  const size_t dec_bytes = align256(L.total);
+  if (dec_bytes + step_extra_bytes(B, s_q, n_h, d_c) > kNoAllocScratchBytes) return MLA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (const int e = scratch_address(&ws); e != MLA_OK) return e;
+  return step_launch(q_nope, w_uk, q_rope, kv_cache, block_table, max_blocks_per_seq, seq_lens, w_uv, B, s_q, n_h,
+                     d_h, d_c, d_r, block_size, softmax_scale, kv_dtype, num_splits, o, lse, (uint8_t*)ws, L,
+                     dec_bytes, n_cu, 1, MLA_STAGE_ALL, (hipStream_t)stream);
 }
 
 int mla_combine_lse(const float* o_part, const float* lse_part, const int32_t* splits_per_row, int N, int S,

@@ -50,22 +50,24 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // -> up to `max_waves` waves of `slots` units plus one rounding unit per sequence.
 constexpr int kMaxAutoWaves = 3;
 
-inline WsLayout ws_layout(int B, int s_q, int n_h, int d_c, int num_splits, int n_cu) {
+// layout for room for `units` plan entries, partial rows of `part_elem`
+// bytes per value
+inline WsLayout ws_layout_units(int B, int s_q, int n_h, int d_c, long long units, int part_elem) {
   WsLayout L{};
-  long long units;
-  if (num_splits > 0)
-    units = (long long)B * num_splits;
-  else
-    units = (long long)kMaxAutoWaves * n_cu + B;
   L.units_max = (int)units;
   size_t R = (size_t)s_q * n_h;
   size_t off = align256(sizeof(WsHeader));
   L.work = off; off = align256(off + (size_t)units * 16);
   L.seq = off; off = align256(off + (size_t)B * 8);
   L.lse_part = off; off = align256(off + (size_t)units * R * 4);
-  L.o_part = off; off = align256(off + (size_t)units * R * d_c * 4);
+  L.o_part = off; off = align256(off + (size_t)units * R * d_c * part_elem);
   L.total = off;
   return L;
+}
+
+inline WsLayout ws_layout(int B, int s_q, int n_h, int d_c, int num_splits, int n_cu) {
+  const long long units = num_splits > 0 ? (long long)B * num_splits : (long long)kMaxAutoWaves * n_cu + B;
+  return ws_layout_units(B, s_q, n_h, d_c, units, 4);
 }
 
 // ---------------------------------------------------------------- parameters
@@ -101,6 +103,8 @@ struct PlanArgs {
   int min_chunk;       // smallest partition (blocks) automatic planning uses
   int max_chunk;       // largest partition (blocks) any unit may have
   int units_max;
+  int max_waves;       // automatic planning: at most this many waves of units
+                       // (1 .. kMaxAutoWaves) unless even the largest partition needs more
 };
 
 // fused merge + W^UV up-projection of a decode step (bf16 partial rows,

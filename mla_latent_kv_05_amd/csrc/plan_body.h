@@ -2,7 +2,7 @@
 // that carries it).  Cuts each sequence into contiguous block ranges
 // ("units"); automatic mode picks the partition length c (in blocks) that
 // minimises an estimated makespan  waves(c) * (c + overhead)  over
-// 1..kMaxAutoWaves waves of `slots_per_wave` concurrent units, where overhead
+// 1..max_waves waves of `slots_per_wave` concurrent units, where overhead
 // stands for the partial-result write and merge of a split sequence.
 #pragma once
 #include "device_util.h"
@@ -67,7 +67,7 @@ __device__ __forceinline__ int units_of(const PlanArgs& a, int n, int chunk) {
 // Every candidate partition length c in [lo, hi] (at most 2048 of them) is
 // scored in parallel: units(c) = sum_b ceil(n_b / c), waves = ceil(units /
 // slots), cost = waves * (c + overhead), overhead charged when any sequence
-// is split.  The cheapest c with waves <= kMaxAutoWaves wins (ties: larger c,
+// is split.  The cheapest c with waves <= max_waves wins (ties: larger c,
 // i.e. fewer partial results); if none fits, c = hi.
 // The planner's body for a workgroup of NT threads (NT / 64 >= kMaxAutoWaves + 1
 // waves); `lds` points at plan_lds_bytes(NT) bytes of the workgroup's LDS
@@ -106,7 +106,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, __attribute__((addr
     // waves(c) does not grow with c and the cost grows with c inside each
     // interval of equal waves, except where the split overhead drops (c >=
     // the longest sequence).  So the cheapest c is the smallest c reaching
-    // waves <= w for some w in 1..kMaxAutoWaves (a binary search each, one
+    // waves <= w for some w in 1..max_waves (a binary search each, one
     // wave per w), or c = min(hi, max_n), or the forced fallback c = hi.
     unsigned long long best = ~0ull;  // key = cost << 32 | (0xffff - c) << 8 | waves
     const int nb_lane = (in_lds && lane < a.B) ? nb[lane] : 0;
@@ -121,14 +121,14 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, __attribute__((addr
     };
     auto consider = [&](int c, int u) {
       const int waves = (u + a.slots_per_wave - 1) / a.slots_per_wave;
-      if (waves > kMaxAutoWaves && c != hi) return;
+      if (waves > a.max_waves && c != hi) return;
       const unsigned long long cost = (unsigned long long)waves * (unsigned)(c + (u > a.B ? overhead : 0));
       // ties on cost go to the larger c; the low byte carries waves (diagnostic)
       const unsigned long long key = (cost << 32) | ((unsigned long long)(0xffffu - (unsigned)c) << 8) |
                                      (unsigned)min(waves, 255);
       best = key < best ? key : best;
     };
-    if (wv < kMaxAutoWaves) {
+    if (wv < a.max_waves) {
       const long long cap = (long long)(wv + 1) * a.slots_per_wave;
       int l = lo, h = hi;  // smallest c in [l, h] with units(c) <= cap, if units(hi) <= cap
       if (units_at(hi) <= cap) {

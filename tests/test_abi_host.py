@@ -21,7 +21,7 @@ def test_header_functions_exported():
     assert set(names) == {"mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_absorbed",
                           "mla_combine_lse", "mla_up_proj_v", "mla_status_string",
                           "mla_cache_append", "mla_cache_append_workspace_bytes", "mla_expand_kv", "mla_gqa_decode", "mla_decode_step",
-                          "mla_decode_step_stages",
+                          "mla_decode_step_stages", "mla_decode_step_noalloc",
                           "mla_decode_step_workspace_bytes",
                           "mla_prefill_mha"}
     L = binding.lib()
@@ -41,7 +41,7 @@ def test_library_is_gfx950_code():
 
 
 def test_status_strings():
-    for code in (OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, -5):
+    for code in (OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, -5, -6):
         s = binding.status_string(code)
         assert s and s != "unknown status"
     assert binding.status_string(12345) == "unknown status"
@@ -191,3 +191,20 @@ def test_decode_step_argument_validation():
     assert st(binding.MLA_STAGE_ATTEND, wuv=None) == INVALID
     assert st(binding.MLA_STAGE_MERGE, d_h=64) == UNSUPPORTED
     assert st(binding.MLA_STAGE_ALL, ws=None) == WORKSPACE
+
+
+def test_decode_step_noalloc_argument_validation():
+    """The no-allocation step checks its arguments like mla_decode_step
+    before it looks at the device (no workspace arguments to check)."""
+    L = binding.lib()
+    args = lambda **k: tuple({**dict(qn=FAKE, wuk=FAKE, qr=FAKE, kv=FAKE, tab=FAKE, mb=16, lens=FAKE, wuv=FAKE, B=4,
+                                     s_q=2, n_h=128, d_h=128, d_c=512, d_r=64, bs=64, sc=0.07, kd=1, ns=0, o=FAKE,
+                                     lse=None, st=None), **k}.values())
+    assert L.mla_decode_step_noalloc(*args(o=None)) == INVALID
+    assert L.mla_decode_step_noalloc(*args(B=0)) == INVALID
+    assert L.mla_decode_step_noalloc(*args(kd=9)) == INVALID
+    assert L.mla_decode_step_noalloc(*args(sc=0.0)) == INVALID
+    assert L.mla_decode_step_noalloc(*args(d_h=64)) == UNSUPPORTED
+    assert L.mla_decode_step_noalloc(*args(n_h=64)) == UNSUPPORTED
+    assert L.mla_decode_step_noalloc(*args(qn=FAKE + 8)) == MISALIGNED
+    assert L.mla_decode_step_noalloc(*args(o=FAKE + 8)) == MISALIGNED
