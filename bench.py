@@ -1,26 +1,28 @@
 #!/usr/bin/env python
 """Absorbed-MLA decode benchmark on one MI355X.
 
-One step = the whole hot path for one batch, as one mla_decode_step call:
-W^UK absorption into the query with the split planner in the same launch ->
-paged split-KV attention over the latent cache -> partition merge fused with
-the W^UV up-projection.  Inputs are seeded synthetic tensors already resident
-in HBM; the timed region rotates through several physically distinct copies
-of the latent cache so repeated steps cannot be served from the 256 MB
-last-level cache.
+One step = the whole hot path for one batch: W^UK absorption into the query
+with the split planner in the same launch -> paged split-KV attention over
+the latent cache -> partition merge fused with the W^UV up-projection, issued
+as three mla_decode_step_stages calls with HIP events recorded by this script
+on the launch stream around every attention launch, so the step time and the
+attention kernel's own time come from the same timed steps.  Inputs are
+seeded synthetic tensors already resident in HBM; the timed region rotates
+through several physically distinct copies of the latent cache so repeated
+steps cannot be served from the 256 MB last-level cache.
 
-Before the W warm-up steps the device is settled with ~300 ms of bf16 GEMMs
-(none of the measured path's data or kernels): started from idle, MI355X
-needs that long under matrix load to reach the clock it holds while serving,
-and a few-millisecond run would otherwise time the ramp.
+Before the W warm-up steps the device is settled: started from idle, MI355X
+runs this step 10-20 % slower for its first ~100-200 executions (20-40 ms;
+GEMM or copy loads do not bring it there), so a few-millisecond run would
+time that ramp instead of the serving state.  The step runs untimed until
+the time per 10 steps is stable (at most --settle-ms); the JSON line reports
+the settle (steps, ms) beside the W warm-up and K timed steps.
 
-A second back-to-back loop of the same steps, issued one stage per call,
-carries HIP events recorded by this script around every attention launch:
-they give the kernel's own time for the roofline object.  A per-stage
-breakdown and the separate entry points (mla_absorb_q, mla_decode_absorbed,
-mla_up_proj_v) follow, then the secondary paths (cache producer, MHA-mode
-prefill, GQA-path decode), an HBM copy probe and the float64 oracle on a
-bounded sample of the workload on the host cores.
+After the timed steps: the same steps as one mla_decode_step call each (for
+comparison), a per-stage breakdown, the separate entry points (mla_absorb_q,
+mla_decode_absorbed, mla_up_proj_v), the secondary paths (cache producer,
+MHA-mode prefill, GQA-path decode), an HBM copy probe and the float64 oracle
+on a bounded sample of the workload on the host cores.
 
 Prints one JSON line.  Metric: latent-cache bytes read per second (TB/s) of
 the whole step, with decode tokens/s and the roofline fractions alongside.
@@ -156,27 +158,36 @@ def stream_probe(dev, mib: int = 2048, reps: int = 10) -> dict:
             "frac_of_peak": 2 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
-def settle_device(dev, ms: float) -> dict:
-    """Bring the device out of idle before the warm-up steps.  MI355X raises
-    its compute clock over the first ~100-300 ms of sustained matrix load; a
-    few-millisecond run started from idle measures that ramp, not the clock a
-    continuously serving GPU runs at.  The load is plain bf16 GEMMs on
-    buffers of their own (none of the measured path's data or kernels)."""
+def settle_device(run_step, max_ms: float, min_ms: float = 50.0, window: int = 10, tol: float = 0.02) -> dict:
+    """Bring the device from idle to the state it holds while serving before
+    the warm-up steps.  Started from idle, MI355X runs this step 10-20 %
+    slower for its first ~100-200 executions (~20-40 ms); GEMM or copy loads of
+    any length do not reach that state, the step itself does.  So the step
+    runs untimed in windows of `window` until two consecutive windows agree
+    within `tol` (at least `min_ms`, at most `max_ms`); the JSON line reports
+    how many steps and milliseconds that took."""
     import torch
-    if ms <= 0:
-        return {"kind": None, "ms": 0.0}
-    a = torch.randn(8192, 8192, device=dev, dtype=torch.float32).to(torch.bfloat16)
-    torch.cuda.synchronize()
+    if max_ms <= 0:
+        return {"kind": None, "steps": 0, "ms": 0.0}
     t0 = time.perf_counter()
-    n = 0
-    while (time.perf_counter() - t0) * 1e3 < ms:
-        for _ in range(4):
-            a @ a
-        n += 4
+    prev, n, stable = None, 0, False
+    while True:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(window):
+            run_step(n)
+            n += 1
+        e1.record()
         torch.cuda.synchronize()
-    el = (time.perf_counter() - t0) * 1e3
-    del a
-    return {"kind": "bf16 GEMM 8192x8192x8192 (not the measured path)", "gemms": n, "ms": el}
+        cur = e0.elapsed_time(e1) / window
+        el = (time.perf_counter() - t0) * 1e3
+        stable = prev is not None and abs(cur - prev) <= tol * prev
+        if (stable and el >= min_ms) or el >= max_ms:
+            break
+        prev = cur
+    return {"kind": "the measured step, untimed, until two consecutive windows of "
+                    f"{window} steps agree within {tol:.0%}", "steps": n, "ms": el, "stable": stable,
+            "last_window_ms_per_step": cur}
 
 
 def device_info(dev) -> dict:
@@ -372,12 +383,13 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true", help="skip the MHA-mode prefill measurement")
     ap.add_argument("--no-gqa", action="store_true", help="skip the GQA-path decode measurement")
     ap.add_argument("--no-stream-probe", action="store_true", help="skip the device-copy bandwidth probe")
-    ap.add_argument("--settle-ms", type=float, default=300.0,
-                    help="milliseconds of bf16 GEMM load before the warm-up steps, to bring the device from its "
-                         "idle clock to the clock it holds under sustained load (0 = none)")
-    ap.add_argument("--step-api", choices=("fused", "separate"), default="fused",
-                    help="time the step as one mla_decode_step call (absorb, attention, merge fused with W^UV) "
-                         "or as mla_absorb_q + mla_decode_absorbed + mla_up_proj_v")
+    ap.add_argument("--settle-ms", type=float, default=400.0,
+                    help="at most this many milliseconds of untimed steps before the warm-up steps, ending once the "
+                         "per-step time is stable, to bring the device from idle to its serving state (0 = none)")
+    ap.add_argument("--step-api", choices=("staged", "fused", "separate"), default="staged",
+                    help="time the step as three mla_decode_step_stages calls with events around the attention "
+                         "launch (default: step and kernel times from the same steps), as one mla_decode_step "
+                         "call, or as mla_absorb_q + mla_decode_absorbed + mla_up_proj_v")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference kernel "
                          "for scaling HBM traffic counters) and exit")
@@ -446,6 +458,7 @@ def main() -> int:
         """the same three launches as three calls of mla_decode_step_stages,
         with this script's own events on the launch stream around the
         attention stage (and, for the breakdown, around the other two)"""
+        i %= args.steps + 1
         if not only_kernel:
             ev["a"][i].record()
         binding.decode_step_stages(binding.MLA_STAGE_ABSORB, *step_args(i), **step_kw)
@@ -470,8 +483,12 @@ def main() -> int:
         if timed:
             ev["d"][i].record()
 
-    step = fused_step if args.step_api == "fused" else separate_step
-    settle = settle_device(dev, args.settle_ms)
+    # the timed step: by default the three stage calls with events around the
+    # attention launch, so the step time and the kernel's own time come from
+    # the same timed steps (HIP graphs replay the single call instead)
+    api = "fused" if (args.launch == "graph" and args.step_api == "staged") else args.step_api
+    step = {"staged": staged_step, "fused": fused_step, "separate": separate_step}[api]
+    settle = settle_device(step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -521,15 +538,23 @@ def main() -> int:
         t_wall = t_eager
     ms_step = graph_ms if graph_ms is not None else eager_ms
 
-    # The attention kernel's own time: the step again, back to back for the
-    # same number of steps, as three stage calls with events recorded by this
-    # script on the launch stream around the attention launch (the library
-    # records nothing).  The events sit between launches, so this loop's
-    # ms/step is reported beside the headline one.
+    # The attention kernel's own time: the events this script recorded on the
+    # launch stream around every attention launch of the timed steps (the
+    # library records nothing).  When the timed step was not the staged one,
+    # a second back-to-back loop of staged steps supplies them.
     def kernel_steps(n):
         for i in range(n):
             staged_step(i)
-    staged_ms, _ = timed_loop(kernel_steps, args.steps)
+
+    def fused_steps(n):
+        for i in range(n):
+            fused_step(i)
+    if api == "staged":
+        staged_ms = ms_step
+        fused_ms, _ = timed_loop(fused_steps, args.steps)  # the single-call API, for comparison
+    else:
+        staged_ms, _ = timed_loop(kernel_steps, args.steps)
+        fused_ms = ms_step if api == "fused" else None
     kernel_all = [ev["k0"][i].elapsed_time(ev["k1"][i]) for i in range(args.steps)]
     kernel_ms = float(np.mean(kernel_all))
     kernel_med = float(np.median(kernel_all))
@@ -572,8 +597,9 @@ def main() -> int:
     roof["kernel"] = kname
     roof["kernel_ms"] = kernel_ms
     roof["kernel_ms_median"] = kernel_med
-    roof["timing"] = ("HIP events recorded by bench.py on the launch stream around every attention launch of a "
-                      "back-to-back loop of whole steps (mla_decode_step_stages, one stage per call)")
+    roof["timing"] = ("HIP events recorded by bench.py on the launch stream around every attention launch of the "
+                      + ("timed steps" if api == "staged" else "a second back-to-back loop of whole steps")
+                      + " (mla_decode_step_stages, one stage per call)")
     roof["units_per_launch"] = {"tokens": int(case.seq_lens.sum()), "bytes_per_token": case.row_bytes,
                                 "flops": flops}
     step_frac = value * 1e3 / HBM_PEAK_GBS
@@ -588,14 +614,14 @@ def main() -> int:
         "config": {"workload": args.workload, "n_h": n_h, "d_c": d_c, "d_r": d_r, "d_h": d_h, "B": B,
                    "s_q": s_q, "ctx": int(case.seq_lens.max()) if w["lens"][0] == "fixed" else "log-uniform",
                    "page_tokens": case.block_size, "kv_dtype": case.kv_dtype, "splits": args.splits or "auto",
-                   "cache_copies": len(caches), "launch": args.launch, "step_api": args.step_api},
+                   "cache_copies": len(caches), "launch": args.launch, "step_api": api},
         "decode_tok_s": tok_s, "latent_bytes": latent_bytes,
         "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
         # call-level fraction: latent bytes over the whole step (planner,
         # absorption, attention, merge, W^UV); roofline.frac is the kernel's
         "roofline_frac_step": step_frac if case.kv_dtype == "bf16" else None,
-        "kernel_loop_ms_per_step": staged_ms,
-        "stages_ms": {"absorb_plan": absorb_ms, "attention": kernel_bd_ms, "merge_up": merge_ms},
+        "staged_ms_per_step": staged_ms, "fused_call_ms_per_step": fused_ms,
+        "stages_ms_events_between": {"absorb_plan": absorb_ms, "attention": kernel_bd_ms, "merge_up": merge_ms},
         "separate_calls_ms": {"absorb_q": sep_absorb_ms, "decode_absorbed": decode_ms, "up_proj_v": up_ms,
                               "decode_absorbed_TBps": latent_bytes / (decode_ms * 1e-3) / 1e12},
         "wall_s": t_wall,

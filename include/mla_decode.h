@@ -120,7 +120,11 @@ size_t mla_decode_workspace_bytes(int B, int s_q, int n_h, int d_c, int max_bloc
  *             groups first, then RoPE groups) decodes as code * scale + min.
  *             Codes are packed in little-endian 32-bit words of 32/b values:
  *             value 2k at bit k*b, value 2k+1 at bit 16 + k*b.  Needs
- *             d_c % 32 == 0 and d_r % 32 == 0.
+ *             d_c % 32 == 0 and d_r % 32 == 0.  The MFMA kernel decodes to
+ *             fp16 and multiplies fp16 operands (queries and softmax weights
+ *             rounded to fp16, fp32 accumulation): queries and decoded values
+ *             must lie inside the fp16 range (|x| < 65504); the portable
+ *             kernel decodes to fp32.
  *  block_table [B, max_blocks_per_seq] int32: logical block k of sequence b
  *           is physical block block_table[b*max_blocks_per_seq + k].
  *  seq_lens [B] int32 (device).

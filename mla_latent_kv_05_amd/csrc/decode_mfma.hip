@@ -1,8 +1,8 @@
 // Software-pipelined MFMA decode kernel for the DeepSeek-V2/V3 shape of
 // absorbed MLA (itwiki "Multi-head latent attention": sections "Decoupled
 // RoPE", "Matrix absorption" and the V2/V3 dimension table): n_h = 128 heads
-// sharing one latent row [c^KV 512 | k^R 64] per token, 64-token pages, bf16
-// or fp8-e4m3 content.
+// sharing one latent row [c^KV 512 | k^R 64] per token, 64-token pages, bf16,
+// fp8-e4m3 or grouped int4 / int2 content.
 //
 // Work decomposition
 //   * grid.x = persistent workgroups looping over planned units (sequence,
@@ -54,7 +54,9 @@ constexpr int kF8QrOff = kF8SlotOff + 2 * kTileB;           // 136192
 constexpr int kF8TabOff = kF8QrOff + kHeads * kQrStride;    // 154624
 // low-bit caches (int4 / int2 content, int4 RoPE; groups of 32 values with
 // an fp16 (scale, min) pair): 3 staging stages of [content codes | RoPE codes
-// | parameters] per subtile, expanded into two bf16 tile slots like fp8
+// | parameters] per subtile, decoded into two fp16 tile slots (fp16 keeps 11
+// mantissa bits of code * scale + min where bf16 would keep 8; the products
+// then run on the fp16 MFMA, queries and P converted to fp16)
 constexpr int kFmtBf16 = 0, kFmtFp8 = 1, kFmtInt4 = 2, kFmtInt2 = 3;
 constexpr int kIntCodeB(int fmt) { return fmt == kFmtInt4 ? kSub * kDc / 2 : kSub * kDc / 4; }  // 8192 / 4096
 constexpr int kIntRopeB = kSub * kDr / 2;                    // 1024
@@ -81,35 +83,56 @@ constexpr int kPipeLds(int fmt) {
 static_assert(kPipeLds(kFmtFp8) <= 160 * 1024 && kPipeLds(kFmtInt4) <= 160 * 1024, "LDS budget");
 static_assert(kIntMiscChunks <= 256, "one misc DMA instruction per thread");
 
-// fp16 (scale, min) pair of a group, packed in one dword
-__device__ __forceinline__ void int_params(uint32_t pr, float& sc, float& mn) {
-  sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(pr & 0xffffu));
-  mn = (float)__builtin_bit_cast(_Float16, (uint16_t)(pr >> 16));
+// fp16 (scale, min) pair of a group, packed in one dword -> the scale in
+// both halves of one dword, the minimum in both halves of another
+__device__ __forceinline__ void int_params_x2(uint32_t pr, uint32_t& sc2, uint32_t& mn2) {
+  sc2 = (pr & 0xffffu) | (pr << 16);
+  mn2 = (pr >> 16) | (pr & 0xffff0000u);
 }
-__device__ __forceinline__ float ubyte_f(uint32_t x, int k) { return (float)((x >> (8 * k)) & 0xffu); }
+// Two codes -> two fp16 values code * scale + min.  The codes sit in the low
+// bits of each 16-bit half of x (`mask` keeps them); or-ing in the exponent
+// of 1024 makes each half the fp16 number 1024 + code (exact: the spacing
+// there is 1), subtracting 1024 leaves the code, and one packed fp16 fma
+// rounds code * scale + min once.
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t x, uint32_t mask, uint32_t sc2, uint32_t mn2) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 c = __builtin_bit_cast(f16x2, (x & mask) | 0x64006400u) - (f16x2){(_Float16)1024, (_Float16)1024};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, __builtin_bit_cast(f16x2, sc2),
+                                                                __builtin_bit_cast(f16x2, mn2)));
+}
 // one packed word of 8 int4 codes (value 2k at bit 4k, 2k+1 at bit 16+4k) ->
-// 8 bf16 values code*sc + mn in value order.  Masking the low / high nibbles
-// leaves whole bytes (the high ones 16x the code) for byte-to-float converts.
-__device__ __forceinline__ u32x4_t int4_word_bf16(uint32_t wd, float sc, float mn) {
-  const uint32_t lo = wd & 0x0F0F0F0Fu, hi = wd & 0xF0F0F0F0u;
-  const float s16 = sc * 0.0625f;
+// 8 fp16 values in value order: nibble k of both halves is the pair (2k, 2k+1)
+__device__ __forceinline__ u32x4_t int4_word_f16(uint32_t wd, uint32_t sc2, uint32_t mn2) {
   u32x4_t o;
-  o[0] = pack_bf16x2(__builtin_fmaf(ubyte_f(lo, 0), sc, mn), __builtin_fmaf(ubyte_f(lo, 2), sc, mn));
-  o[1] = pack_bf16x2(__builtin_fmaf(ubyte_f(hi, 0), s16, mn), __builtin_fmaf(ubyte_f(hi, 2), s16, mn));
-  o[2] = pack_bf16x2(__builtin_fmaf(ubyte_f(lo, 1), sc, mn), __builtin_fmaf(ubyte_f(lo, 3), sc, mn));
-  o[3] = pack_bf16x2(__builtin_fmaf(ubyte_f(hi, 1), s16, mn), __builtin_fmaf(ubyte_f(hi, 3), s16, mn));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = dequant_pair(wd >> (4 * k), 0x000F000Fu, sc2, mn2);
   return o;
 }
 // one packed word of 16 int2 codes (value 2k at bit 2k, 2k+1 at bit 16+2k)
-// -> values 0..7 (a) and 8..15 (b) as bf16
-__device__ __forceinline__ void int2_word_bf16(uint32_t wd, float sc, float mn, u32x4_t& a, u32x4_t& b) {
+// -> values 0..7 (a) and 8..15 (b) as fp16
+__device__ __forceinline__ void int2_word_f16(uint32_t wd, uint32_t sc2, uint32_t mn2, u32x4_t& a, u32x4_t& b) {
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {  // bit pair f of every byte: codes x 4^f
-    const uint32_t mk = wd & (0x03030303u << (2 * f));
-    const float sf = sc * (f == 0 ? 1.f : f == 1 ? 0.25f : f == 2 ? 0.0625f : 0.015625f);
-    a[f] = pack_bf16x2(__builtin_fmaf(ubyte_f(mk, 0), sf, mn), __builtin_fmaf(ubyte_f(mk, 2), sf, mn));
-    b[f] = pack_bf16x2(__builtin_fmaf(ubyte_f(mk, 1), sf, mn), __builtin_fmaf(ubyte_f(mk, 3), sf, mn));
+  for (int k = 0; k < 4; ++k) {
+    a[k] = dequant_pair(wd >> (2 * k), 0x00030003u, sc2, mn2);
+    b[k] = dequant_pair(wd >> (2 * k + 8), 0x00030003u, sc2, mn2);
   }
+}
+// the 8 bf16 query values of a fragment as fp16 (exact inside the fp16 range)
+__device__ __forceinline__ bf16x8_t bf16x8_as_f16(bf16x8_t v) {
+  typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+  f16x8 h;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = (_Float16)(float)v[e];
+  return __builtin_bit_cast(bf16x8_t, h);
+}
+// one operand value of the products: bf16, or fp16 (int caches) carried in
+// the bf16 vector type
+template <bool F16>
+__device__ __forceinline__ __bf16 op16(float x) {
+  if constexpr (F16)
+    return __builtin_bit_cast(__bf16, (_Float16)x);
+  else
+    return (__bf16)x;
 }
 
 // s_waitcnt vmcnt for "at most n DMA groups of G instructions still in flight"
@@ -130,7 +153,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_pipe_kernel(DecodeArgs a) {
   constexpr bool FP8 = FMT == kFmtFp8;      // per-token scaled e4m3 content codes
   constexpr bool INT = FMT >= kFmtInt4;     // grouped low-bit codes
-  constexpr bool STAGED = FMT != kFmtBf16;  // codes staged, expanded into bf16 tile slots
+  constexpr bool STAGED = FMT != kFmtBf16;  // codes staged, expanded into 16-bit tile slots
+  constexpr bool F16 = INT;                 // fp16 operands (tiles, queries, P); bf16 otherwise
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
   lds_i32* tab = (lds_i32*)(smem + kPipeTabOff(FMT));
@@ -215,6 +239,12 @@ void decode_pipe_kernel(DecodeArgs a) {
       if (wk.z > max(1, (len_now + kBlk - 1) / kBlk)) continue;
       if (tid < npg) tab[tid] = pg0;
       if (tid + 256 < npg) tab[tid + 256] = pg1;
+      if (F16) {  // int caches: the products run on fp16 operands
+#pragma unroll
+        for (int kb = 0; kb < 32; ++kb) q[kb] = bf16x8_as_f16(q[kb]);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qrv[kb] = bf16x8_as_f16(qrv[kb]);
+      }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         if (FP8)
@@ -284,7 +314,7 @@ void decode_pipe_kernel(DecodeArgs a) {
       return *(const __attribute__((address_space(3))) f32x4_t*)(smem + kF8ScaleOff + (s % kF8ScaleSlots) * 128 +
                                                                   16 * g + 32 * qd);
     };
-    // int4 / int2: expand staged subtile s into its bf16 tile slot (rows past
+    // int4 / int2: decode staged subtile s into its fp16 tile slot (rows past
     // nv -> 0).  A job is one 16-byte chunk of codes: int4 content 2 per
     // thread (32 values, one group each), int2 content 1 per thread (64
     // values, two groups); the 64 RoPE chunks (int4, one group each) go to
@@ -326,27 +356,27 @@ void decode_pipe_kernel(DecodeArgs a) {
       for (int i = 0; i < nj; ++i) {
         const int job = tid + 256 * i, t = job / cpr, j = job % cpr;
         if (cbits == 4) {
-          float sc, mn;
-          int_params(pw[i][0], sc, mn);
+          uint32_t sc2, mn2;
+          int_params_x2(pw[i][0], sc2, mn2);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) put(t, 4 * j + k, int4_word_bf16(cw[i][k], sc, mn));
+          for (int k = 0; k < 4; ++k) put(t, 4 * j + k, int4_word_f16(cw[i][k], sc2, mn2));
         } else {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            float sc, mn;
-            int_params(pw[i][k >> 1], sc, mn);
+            uint32_t sc2, mn2;
+            int_params_x2(pw[i][k >> 1], sc2, mn2);
             u32x4_t va, vb;
-            int2_word_bf16(cw[i][k], sc, mn, va, vb);
+            int2_word_f16(cw[i][k], sc2, mn2, va, vb);
             put(t, 8 * j + 2 * k, va);
             put(t, 8 * j + 2 * k + 1, vb);
           }
         }
       }
       if (tid < 64) {
-        float sc, mn;
-        int_params(rp, sc, mn);
+        uint32_t sc2, mn2;
+        int_params_x2(rp, sc2, mn2);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) put(tr, kDc / 8 + 4 * jr + k, int4_word_bf16(rw[k], sc, mn));
+        for (int k = 0; k < 4; ++k) put(tr, kDc / 8 + 4 * jr + k, int4_word_f16(rw[k], sc2, mn2));
       }
     };
     // fp8: expand staged subtile s into its bf16 tile slot (rows past nv -> 0).
@@ -510,7 +540,7 @@ void decode_pipe_kernel(DecodeArgs a) {
         for (int e = 0; e < 4; ++e) P[q4 >> 1][(q4 & 1) * 4 + e] = (__bf16)(t0 + e < nv ? sp[4 * q4 + e] * ts[e] : 0.f);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) P[q4 >> 1][(q4 & 1) * 4 + e] = (__bf16)sp[4 * q4 + e];
+        for (int e = 0; e < 4; ++e) P[q4 >> 1][(q4 & 1) * 4 + e] = op16<F16>(sp[4 * q4 + e]);
       }
     };
     auto sm_stage = [&](int st) {  // stages 0..10
@@ -562,7 +592,7 @@ void decode_pipe_kernel(DecodeArgs a) {
       bf16x8_t ka[2] = {kfrag(tile, 0), kfrag(tile, 1)};
 #pragma unroll
       for (int f = 0; f < 36; ++f) {
-        if (FP8 && f >= 32) sr = mfma(ka[f & 1], qfrag(f), sr); else sc = mfma(ka[f & 1], qfrag(f), sc);
+        if (FP8 && f >= 32) sr = mfma_op<F16>(ka[f & 1], qfrag(f), sr); else sc = mfma_op<F16>(ka[f & 1], qfrag(f), sc);
         if (f + 2 < 36) ka[f & 1] = kfrag(tile, f + 2);
       }
       form_scores(0);
@@ -605,7 +635,7 @@ void decode_pipe_kernel(DecodeArgs a) {
       bf16x8_t ka[2] = {kfrag(tile_n, 0), kfrag(tile_n, 1)};
 #pragma unroll
       for (int f = 0; f < kQkA; ++f) {
-        sc = mfma(ka[f & 1], qfrag(f), sc);
+        sc = mfma_op<F16>(ka[f & 1], qfrag(f), sc);
         ka[f & 1] = kfrag(tile_n, f + 2);
         if (f <= 10) sm_stage(f);
         if (f == 8) asm volatile("" : "+v"(P[0]));  // keep the conversions in place
@@ -621,12 +651,12 @@ void decode_pipe_kernel(DecodeArgs a) {
       int step = 0;
 #pragma unroll
       for (int f = kQkA; f < 36; ++f) {
-        if (FP8 && f >= 32) sr = mfma(ka[f & 1], qfrag(f), sr); else sc = mfma(ka[f & 1], qfrag(f), sc);
+        if (FP8 && f >= 32) sr = mfma_op<F16>(ka[f & 1], qfrag(f), sr); else sc = mfma_op<F16>(ka[f & 1], qfrag(f), sc);
         if (f + 2 < 36) ka[f & 1] = kfrag(tile_n, f + 2);
         const int npv = (f - kQkA) < 12 ? 2 : 1;
 #pragma unroll
         for (int u = 0; u < npv; ++u) {
-          mfma_acc(acc[step & 15], va[step & 1], P[step >> 4]);
+          mfma_acc_op<F16>(acc[step & 15], va[step & 1], P[step >> 4]);
           if (step + 2 < 32) va[step & 1] = vfrag(tile, step + 2);
           ++step;
         }
@@ -646,7 +676,7 @@ void decode_pipe_kernel(DecodeArgs a) {
       bf16x8_t va[2] = {vfrag(tile, 0), vfrag(tile, 1)};
 #pragma unroll
       for (int step = 0; step < 32; ++step) {
-        mfma_acc(acc[step & 15], va[step & 1], P[step >> 4]);
+        mfma_acc_op<F16>(acc[step & 15], va[step & 1], P[step >> 4]);
         if (step + 2 < 32) va[step & 1] = vfrag(tile, step + 2);
       }
     }

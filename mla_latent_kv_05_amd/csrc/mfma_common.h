@@ -102,6 +102,31 @@ __device__ __forceinline__ void mfma_acc(f32x16_t& acc, const bf16x8_t& a, const
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// The same two products on fp16 operands (int caches; the bits travel in the
+// bf16 vector type), chosen at compile time
+__device__ __forceinline__ f32x16_t mfma_f16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
+}
+__device__ __forceinline__ void mfma_acc_f16(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+template <bool F16>
+__device__ __forceinline__ f32x16_t mfma_op(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  if constexpr (F16)
+    return mfma_f16(a, b, c);
+  else
+    return mfma(a, b, c);
+}
+template <bool F16>
+__device__ __forceinline__ void mfma_acc_op(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  if constexpr (F16)
+    mfma_acc_f16(acc, a, b);
+  else
+    mfma_acc(acc, a, b);
+}
+
 // Orders VALU/accvgpr access to the AGPR accumulator after (or before) the
 // asm MFMAs above: 24 wait states cover the MFMA-writes-AGPR ->
 // v_accvgpr_read and v_accvgpr_write -> MFMA-reads-SrcC hazards.

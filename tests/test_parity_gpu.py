@@ -118,41 +118,22 @@ def test_v3_fp8_cache_sq2(force_generic):
         assert_lse_close(gl, ol, "lse")
 
 
-def _bf16_operand_lse_bound(case):
-    """Bound on |lse_gpu - lse| when the kernel rounds the decoded cache values
-    to bf16 before the products (relative error <= 2^-9 per value): every
-    score moves by at most scale * 2^-9 * (|q_lat|.|c_j| + |q_rope|.|k^R_j|),
-    and the lse by at most the largest such move over the visible keys."""
-    out = np.zeros((case.B, case.s_q, case.n_h))
-    for b in range(case.B):
-        ql, qr, c, kr = oracle.decode_case_rows(case, b)
-        L = c.shape[0]
-        m = np.abs(ql) @ np.abs(c).T + np.abs(qr) @ np.abs(kr).T       # [s_q, n_h, L]
-        for i in range(case.s_q):
-            out[b, i] = m[i, :, :L - case.s_q + i + 1].max(axis=-1)
-    return case.softmax_scale * 2.0 ** -9 * out
-
-
 @pytest.mark.parametrize("force_generic", [False, True])
 @pytest.mark.parametrize("kv", ["int4", "int2"])
 @pytest.mark.parametrize("s_q", [1, 2])
 def test_v3_int_cache(kv, s_q, force_generic):
     """Low-bit caches (grouped fp16 scale/min, packed codes) against the
-    oracle's decoding of the same bytes: the MFMA kernel (values expanded to
-    bf16 in LDS, so its lse is held to the bound that rounding implies) and
-    the portable kernel (fp32 values)."""
+    oracle's decoding of the same bytes: the MFMA kernel (values decoded to
+    fp16 in LDS, fp16 products with fp32 accumulation) and the portable
+    kernel (fp32 values), both at the bf16 output bars and |dlse| <= 1e-3."""
     say(f"v3 {kv} s_q={s_q} generic={force_generic}")
     lens = np.array([2, 33, 64, 129, 1500], dtype=np.int32)
     case = inputs.decode_case(26 + s_q, B=len(lens), seq_lens=lens, s_q=s_q, kv_dtype=kv, **V3)
     o, ol = oracle.mqa_decode_case(case)
-    bound = _bf16_operand_lse_bound(case)
     for splits in (0, 3):
         g, gl = run_decode(case, num_splits=splits, force_generic=force_generic)
         assert_bf16_close(g, o, f"{kv} splits={splits}")
-        if force_generic:
-            assert_lse_close(gl, ol, "lse")
-        else:
-            assert np.all(np.abs(gl - ol) <= bound + 1e-4), float(np.max(np.abs(gl - ol) - bound))
+        assert_lse_close(gl, ol, "lse")
 
 
 @pytest.mark.parametrize("kv", ["int4", "int2"])
@@ -283,11 +264,7 @@ def test_full_size_workloads_sampled(name, seqs):
     o, ol = oracle.mqa_decode_case(case, seqs)
     assert np.all(np.isfinite(g))
     assert_bf16_close(g[seqs], o, name)
-    if case.kv_dtype in ("int4", "int2"):  # bf16 operands of decoded values: the lse bound they imply
-        bound = _bf16_operand_lse_bound(case)[seqs]
-        assert np.all(np.abs(gl[seqs] - ol) <= bound + 1e-4)
-    else:
-        assert_lse_close(gl[seqs], ol, name)
+    assert_lse_close(gl[seqs], ol, name)
 
 
 @pytest.mark.parametrize("name,seqs", [
@@ -909,8 +886,7 @@ def test_decode_step_matches_separate_calls_and_oracle(kv, lens, s_q, splits):
         ref_l.append(l)
     ref_o = np.stack(ref_o).reshape(T_q, 128, 128)
     assert_bf16_close(g, ref_o, f"step {kv}")
-    if kv != "int4":
-        assert_lse_close(lse.cpu().numpy().astype(np.float64).reshape(case.B, s_q, 128), np.stack(ref_l), "step lse")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64).reshape(case.B, s_q, 128), np.stack(ref_l), "step lse")
 
 
 @pytest.mark.parametrize("kv,lens,splits", [("bf16", [2, 33, 1500, 4096], 0), ("fp8", [700, 64], 2)])
