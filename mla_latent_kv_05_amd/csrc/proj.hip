@@ -46,16 +46,20 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(const void* A, long l
 // W^UK_h[0:d_h, c0:c0+128] is staged in LDS (row stride padded to 144
 // elements) and read transposed with ds_read_tr16_b64 as the B operand.
 // Query rows (A operand) are staged 32 at a time in LDS from whole-row
-// loads, and each 32 x 128 output tile goes back through LDS so that global
-// stores write whole 16-byte pieces of rows.  Wave w covers columns
-// c0 + 32w .. +31.
+// loads, and each 32 x 128 output tile goes back through LDS (into the
+// query area once every wave is done with it) so that global stores write
+// whole 16-byte pieces of rows.  Wave w covers columns c0 + 32w .. +31.
+// The staging is kept under 53 KB so that three workgroups fit on a compute
+// unit: the 4 * n_h tiles of V2/V3 shapes (plus the planner's row when it
+// rides along) then run in one wave.
 constexpr int kAbsCols = 128;
 constexpr int kAbsStride = 144;  // bf16 elements per staged weight row
 constexpr int kAbsQStride = 136; // bf16 elements per staged query row
 constexpr int kAbsMaxKb = 8;     // d_h / 16 up to d_h = 128
 
 constexpr size_t absorb_lds_bytes(int d_h, bool out_bf16) {
-  return (size_t)d_h * kAbsStride * 2 + 32 * kAbsQStride * 2 + 32 * (kAbsCols + 8) * (out_bf16 ? 2 : 4);
+  const size_t q = 32 * kAbsQStride * 2, o = 32 * (kAbsCols + 8) * (out_bf16 ? 2 : 4);
+  return (size_t)d_h * kAbsStride * 2 + (q > o ? q : o);
 }
 
 // one workgroup's tile: head h, column block cblk
@@ -66,7 +70,7 @@ __device__ __forceinline__ void absorb_tile(const uint16_t* q, long long q_st, c
   typedef __attribute__((address_space(3))) u32x4_t lds_u4;
   lds_u8* wl = (lds_u8*)smem_raw;
   lds_u8* ql = wl + d_h * kAbsStride * 2;
-  lds_u8* ol = ql + 32 * kAbsQStride * 2;
+  lds_u8* ol = ql;  // the output tile reuses the query rows' space
   constexpr int kOutElem = OUT_BF16 ? 2 : 4;
   constexpr int kORow = (kAbsCols + 8) * kOutElem;  // staged output row (bytes)
   const int c0 = cblk * kAbsCols;
@@ -131,8 +135,8 @@ __device__ __forceinline__ void absorb_tile(const uint16_t* q, long long q_st, c
     bf[kb][4] = hi[0]; bf[kb][5] = hi[1]; bf[kb][6] = hi[2]; bf[kb][7] = hi[3];
   }
   for (int t0 = 0; t0 < T; t0 += 32) {
+    f32x16_t acc;
     if (active) {
-      f32x16_t acc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
@@ -141,6 +145,9 @@ __device__ __forceinline__ void absorb_tile(const uint16_t* q, long long q_st, c
         const bf16x8_t av = *(const __attribute__((address_space(3))) bf16x8_t*)(ql + (l32 * kAbsQStride + kb * 16 + g * 8) * 2);
         acc = mfma16(av, bf[kb], acc);
       }
+    }
+    __syncthreads();  // every wave has read the query rows: their space takes the output tile
+    if (active) {
       // D[i = t][j = column]: lane column cw + l32, rows 8(r/4) + 4g + r%4
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -161,7 +168,10 @@ __device__ __forceinline__ void absorb_tile(const uint16_t* q, long long q_st, c
         *(u32x4_t*)((uint8_t*)out + ((long long)(t0 + row) * o_st + (long long)h * d_c + c0) * kOutElem + pc * 16) =
             *(const lds_u4*)(ol + row * kORow + pc * 16);
     }
-    if (t0 + 32 < T) store_q();
+    if (t0 + 32 < T) {
+      __syncthreads();  // every thread has copied the output tile out of the query area
+      store_q();
+    }
     __syncthreads();
   }
 }
