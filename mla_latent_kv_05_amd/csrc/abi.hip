@@ -411,7 +411,7 @@ int step_launch(const void* q_nope, const void* w_uk, const void* q_rope, const 
     c.lse = lse;
     c.units_max = L.units_max;
     c.B = B; c.s_q = s_q; c.n_h = n_h;
-    if (launch_combine_up(c, st) != hipSuccess) return MLA_ERR_LAUNCH;
+    if (launch_combine_up(c, n_cu, st) != hipSuccess) return MLA_ERR_LAUNCH;
   }
   return MLA_OK;
 }

@@ -122,7 +122,7 @@ struct CombineUpArgs {
 };
 
 // launchers (return hipError_t of the launch)
-hipError_t launch_combine_up(const CombineUpArgs& c, hipStream_t s);
+hipError_t launch_combine_up(const CombineUpArgs& c, int n_cu, hipStream_t s);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_decode_generic(const DecodeArgs& a, int units_max, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t s);
