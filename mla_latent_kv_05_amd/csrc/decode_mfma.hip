@@ -135,19 +135,6 @@ __device__ __forceinline__ __bf16 op16(float x) {
     return (__bf16)x;
 }
 
-// s_waitcnt vmcnt for "at most n DMA groups of G instructions still in flight"
-template <int G>
-__device__ __forceinline__ void wait_dma_groups(int n) {
-  if (n >= 3)
-    wait_vm<3 * G>();
-  else if (n == 2)
-    wait_vm<2 * G>();
-  else if (n == 1)
-    wait_vm<G>();
-  else
-    wait_vm<0>();
-}
-
 template <int FMT>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_pipe_kernel(DecodeArgs a) {
@@ -298,8 +285,12 @@ void decode_pipe_kernel(DecodeArgs a) {
         }
       }
     };
+    // past the unit's last subtile the group is issued through a descriptor
+    // with no records (no memory traffic; zeros at most land in a ring slot
+    // that is free at that point), so every iteration issues the same
+    // instructions and every wait below has a constant count
     auto issue = [&](int s) {
-      const i32x4_t rs = page_rsrc(s);
+      const i32x4_t rs = s < n_sub ? page_rsrc(s) : empty_rsrc();
       const int m0b = dma_dst(s);
       dma_fence();
 #pragma unroll
@@ -439,9 +430,8 @@ void decode_pipe_kernel(DecodeArgs a) {
 
     if (n_sub > 0) {
 #pragma unroll
-      for (int s = 0; s <= kAhead; ++s)
-        if (s < n_sub) issue(s);
-      wait_dma_groups<kDma>(min(kAhead, n_sub - 1));
+      for (int s = 0; s <= kAhead; ++s) issue(s);
+      wait_vm<kAhead * kDma>();  // subtile 0 landed
       __syncthreads();
       if (STAGED) {
         convert(0, nvalid_of(0));
@@ -605,7 +595,7 @@ void decode_pipe_kernel(DecodeArgs a) {
     constexpr int kQkA = 16;  // QK steps overlapped with the softmax
     for (int it = 0; it + 1 < n_sub; ++it) {
       // ---- (A) next subtile resident; refill the stage subtile it-1 used
-      wait_dma_groups<kDma>(min(kAhead - 1, n_sub - 2 - it));
+      wait_vm<(kAhead - 1) * kDma>();  // subtile it+1 landed (one group, it+2, may fly)
       __syncthreads();
       if (STAGED) {  // expand subtile it+1 into the slot subtile it-1 used
         convert(it + 1, nvalid_of(it + 1));
@@ -617,14 +607,9 @@ void decode_pipe_kernel(DecodeArgs a) {
       // subtile it+kAhead+1 goes to the stage subtile it-1 (bf16) / it (fp8)
       // used; its DMA instructions are spread over the QK steps below
       const int s_dma = it + kAhead + 1;
-      const bool dma_on = s_dma < n_sub;
-      i32x4_t dma_rs = {0, 0, 0, 0};
-      int dma_m0 = 0;
-      if (dma_on) {
-        dma_rs = page_rsrc(s_dma);
-        dma_m0 = dma_dst(s_dma);
-        dma_fence();
-      }
+      const i32x4_t dma_rs = s_dma < n_sub ? page_rsrc(s_dma) : empty_rsrc();
+      const int dma_m0 = dma_dst(s_dma);
+      dma_fence();
       const lds_u8* tile = tile_of(it);
       const lds_u8* tile_n = tile_of(it + 1);
 
@@ -660,7 +645,7 @@ void decode_pipe_kernel(DecodeArgs a) {
           if (step + 2 < 32) va[step & 1] = vfrag(tile, step + 2);
           ++step;
         }
-        if (((f - kQkA) & 1) == 0 && (f - kQkA) / 2 < kDma && dma_on) dma_one(dma_rs, dma_m0, s_dma, (f - kQkA) / 2);
+        if (((f - kQkA) & 1) == 0 && (f - kQkA) / 2 < kDma) dma_one(dma_rs, dma_m0, s_dma, (f - kQkA) / 2);
         __builtin_amdgcn_sched_barrier(0);
       }
       form_scores(it + 1);
@@ -682,6 +667,9 @@ void decode_pipe_kernel(DecodeArgs a) {
     }
 
     // ---- finalize: normalise, stage rows through LDS, store whole rows
+    // (the staging overlaps the ring: the empty groups issued past the last
+    // subtile complete first)
+    wait_vm<0>();
     acc_fence(acc);
     const float l_tot = half_swap_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;

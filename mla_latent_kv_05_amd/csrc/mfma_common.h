@@ -42,6 +42,18 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base) {
   return r;
 }
 
+// A buffer descriptor with no records: every load through it is out of
+// range, so the memory system is never touched (a DMA issued through it
+// only keeps the instruction count of a loop branch-free).
+__device__ __forceinline__ i32x4_t empty_rsrc() {
+  i32x4_t r;
+  r[0] = 0;
+  r[1] = 0;
+  r[2] = 0;           // num_records 0
+  r[3] = 0x00020000;  // gfx9 raw buffer config
+  return r;
+}
+
 // 16-byte global -> LDS DMA (buffer_load_dwordx4 ... lds): lane l's 16 bytes
 // from rsrc.base + voff land at LDS address m0 + 16*l, m0 being computed with
 // scalar arithmetic from a wave-uniform base.  Issued as inline asm so that
