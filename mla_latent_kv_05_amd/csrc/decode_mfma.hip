@@ -534,22 +534,38 @@ void decode_pipe_kernel(DecodeArgs a) {
       }
     };
     auto sm_stage = [&](int st) {  // stages 0..10
-      if (st == 0) {
+      // max tree over the 16 scores of the lane as three-input maxima:
+      // 16 -> 6 -> 2 -> 1 (stage 3 is left empty: every dependent step
+      // stays one MFMA after its producer).  The int4 kernel keeps the
+      // two-input tree: with the other its register allocation spills one
+      // value inside the loop, and that reload waits for every DMA in flight.
+      if (FMT == kFmtInt4) {
+        if (st == 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m8[i] = fmaxf(sp[2 * i], sp[2 * i + 1]);
+          for (int i = 0; i < 8; ++i) m8[i] = fmaxf(sp[2 * i], sp[2 * i + 1]);
+        } else if (st == 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m8[i] = fmaxf(m8[i], m8[i + 4]);
+        } else if (st == 2) {
+          m8[0] = fmaxf(m8[0], m8[2]);
+          m8[1] = fmaxf(m8[1], m8[3]);
+        } else if (st == 3) {
+          m8[0] = fmaxf(m8[0], m8[1]);
+        }
+      } else if (st == 0) {
+#pragma unroll
+        for (int i = 0; i < 5; ++i) m8[i] = max3_raw(sp[3 * i], sp[3 * i + 1], sp[3 * i + 2]);
       } else if (st == 1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m8[i] = fmaxf(m8[i], m8[i + 4]);
+        m8[0] = max3_raw(m8[0], m8[1], m8[2]);
+        m8[1] = max3_raw(m8[3], m8[4], sp[15]);
       } else if (st == 2) {
-        m8[0] = fmaxf(m8[0], m8[2]);
-        m8[1] = fmaxf(m8[1], m8[3]);
-      } else if (st == 3) {
-        m8[0] = fmaxf(m8[0], m8[1]);
-      } else if (st == 4) {
-        const float mx = half_swap_max(m8[0]) * scale2;
+        m8[0] = max3_raw(m8[0], m8[1], m8[1]);
+      }
+      if (st == 4) {
+        const float mx = (FMT == kFmtInt4 ? half_swap_max(m8[0]) : half_swap_max_raw(m8[0])) * scale2;
         m_new = mx > m_run + kTau ? mx : m_run;  // lazy: keep the reference unless far behind
         ps0 = ps1 = 0.f;
-      } else {
+      } else if (st >= 5) {
         const int k = st - 5;  // shift of group k, exp2 of group k-1, sums and P of group k-2
         if (k >= 2) sm_cvt(k - 2);
         if (k >= 1 && k <= 4) sm_ex(k - 1);

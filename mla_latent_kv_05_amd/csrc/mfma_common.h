@@ -149,11 +149,27 @@ __device__ __forceinline__ void acc_fence(f32x16_t* acc) {
                  "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]), "+a"(acc[15]));
 }
 
+// Maximum of three scores, one v_max3_f32.  Written as asm because the
+// compiler quiets each operand of fmaxf first (a v_max x, x, x per value it
+// cannot prove canonical, as MFMA results are), which more than doubles a
+// max tree; the scores here are finite or -inf, never NaN.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // max / sum of a value with the lane 32 apart (the other half of the wave):
 // one VALU permlane swap instead of an LDS-routed shuffle
 __device__ __forceinline__ float half_swap_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// the same with the raw maximum (scores: never NaN)
+__device__ __forceinline__ float half_swap_max_raw(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return max3_raw(a, b, b);
 }
 __device__ __forceinline__ float half_swap_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
