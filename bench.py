@@ -5,8 +5,10 @@ One step = the whole hot path for one batch: W^UK absorption into the query
 with the split planner in the same launch -> paged split-KV attention over
 the latent cache -> partition merge fused with the W^UV up-projection, issued
 as three mla_decode_step_stages calls with HIP events recorded by this script
-on the launch stream around every attention launch, so the step time and the
-attention kernel's own time come from the same timed steps.  Inputs are
+on the launch stream around the attention launch of every 4th step, so the
+step time and the attention kernel's own time come from the same timed steps
+(a pair of events adds ~4 us to its step; sampling keeps that under 1 us per
+step on average).  Inputs are
 seeded synthetic tensors already resident in HBM; the timed region rotates
 through several physically distinct copies of the latent cache so repeated
 steps cannot be served from the 256 MB last-level cache.
@@ -383,6 +385,9 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true", help="skip the MHA-mode prefill measurement")
     ap.add_argument("--no-gqa", action="store_true", help="skip the GQA-path decode measurement")
     ap.add_argument("--no-stream-probe", action="store_true", help="skip the device-copy bandwidth probe")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="record the kernel's events around the attention launch of every N-th timed step "
+                         "(each pair adds ~4 us to its step)")
     ap.add_argument("--settle-ms", type=float, default=400.0,
                     help="at most this many milliseconds of untimed steps before the warm-up steps, ending once the "
                          "per-step time is stable, to bring the device from idle to its serving state (0 = none)")
@@ -394,6 +399,8 @@ def main() -> int:
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference kernel "
                          "for scaling HBM traffic counters) and exit")
     args = ap.parse_args()
+    if args.event_every < 1:
+        ap.error("--event-every must be at least 1")
     if args.copy_probe:
         return copy_probe(args.copy_probe)
 
@@ -457,14 +464,19 @@ def main() -> int:
     def staged_step(i, tag=("k0", "k1"), only_kernel=True):
         """the same three launches as three calls of mla_decode_step_stages,
         with this script's own events on the launch stream around the
-        attention stage (and, for the breakdown, around the other two)"""
+        attention stage of every --event-every'th step (a pair of events
+        costs ~4 us of step time) and, for the breakdown, around every stage
+        of every step"""
+        sample = not only_kernel or i % args.event_every == 0
         i %= args.steps + 1
         if not only_kernel:
             ev["a"][i].record()
         binding.decode_step_stages(binding.MLA_STAGE_ABSORB, *step_args(i), **step_kw)
-        ev[tag[0]][i].record()
+        if sample:
+            ev[tag[0]][i].record()
         binding.decode_step_stages(binding.MLA_STAGE_ATTEND, *step_args(i), **step_kw)
-        ev[tag[1]][i].record()
+        if sample:
+            ev[tag[1]][i].record()
         binding.decode_step_stages(binding.MLA_STAGE_MERGE, *step_args(i), **step_kw)
         if not only_kernel:
             ev["d"][i].record()
@@ -555,7 +567,7 @@ def main() -> int:
     else:
         staged_ms, _ = timed_loop(kernel_steps, args.steps)
         fused_ms = ms_step if api == "fused" else None
-    kernel_all = [ev["k0"][i].elapsed_time(ev["k1"][i]) for i in range(args.steps)]
+    kernel_all = [ev["k0"][i].elapsed_time(ev["k1"][i]) for i in range(0, args.steps, args.event_every)]
     kernel_ms = float(np.mean(kernel_all))
     kernel_med = float(np.median(kernel_all))
     # per-stage breakdown (events around every stage; not a timed loop)
@@ -597,7 +609,8 @@ def main() -> int:
     roof["kernel"] = kname
     roof["kernel_ms"] = kernel_ms
     roof["kernel_ms_median"] = kernel_med
-    roof["timing"] = ("HIP events recorded by bench.py on the launch stream around every attention launch of the "
+    roof["timing"] = (f"HIP events recorded by bench.py on the launch stream around the attention launch of every "
+                      f"{args.event_every}th step ({len(kernel_all)} launches) of the "
                       + ("timed steps" if api == "staged" else "a second back-to-back loop of whole steps")
                       + " (mla_decode_step_stages, one stage per call)")
     roof["units_per_launch"] = {"tokens": int(case.seq_lens.sum()), "bytes_per_token": case.row_bytes,
