@@ -21,7 +21,8 @@
 //   O^T[dim, query] += V^T[dim, key] . P^T[key, query]  (8 MFMAs; A = value
 //                     columns by ds_read_b64_tr_b16, B = P from the S layout)
 // Workgroups are dealt to the 8 XCDs so that all query blocks of a head run
-// on one XCD (its L2 keeps that head's keys and values), longest first.
+// on one XCD (its L2 keeps that head's keys and values), in windows of a few
+// heads with the longest query blocks first.
 #include <type_traits>
 
 #include "mfma_common.h"
@@ -40,6 +41,12 @@ constexpr int kPfStage = kPfKcB + kPfKrB + kPfVB;              // 20480
 constexpr int kPfRing = 2;
 constexpr int kPfDma = 5;                                      // DMA instructions per thread per subtile
 constexpr float kPfTau = 8.f;                                  // lazy-max slack (log2 units)
+// heads per scheduling window: inside a window the query blocks go longest
+// first, so the last workgroups dealt are short ones (one head per window
+// left its longest block running alone at the end: 710 -> 673 us at 4096
+// tokens x 128 heads); 8 heads beat 4 and 16, whose wider key/value working
+// set raises the L2 misses
+constexpr int kPfWin = 8;
 
 // LDS swizzles (64 banks of 4 bytes: a 256-byte line per cycle).  Content
 // key and value rows are 256 bytes (16 chunks of 16 bytes): chunk c of row t
@@ -62,13 +69,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   lds_u8* smem = (lds_u8*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31, j16 = lane & 15, G = lane >> 4;
-  // XCD-aware work item: the k-th workgroup dealt to XCD x takes head
-  // (k / nqb) * 8 + x and query block nqb - 1 - k % nqb
+  // XCD-aware work item: XCD x owns heads x, x + 8, ...; its k-th workgroup
+  // takes them in windows of kPfWin heads, and inside a window the query
+  // blocks longest first across the window's heads
   int h, qblk;
   {
     const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
-    h = (k / nqb) * 8 + x;
-    qblk = nqb - 1 - k % nqb;
+    const int hpx = (n_h + 7) >> 3;  // heads per XCD
+    const int win = k / (kPfWin * nqb), r = k - win * (kPfWin * nqb);
+    const int wh = min(kPfWin, hpx - win * kPfWin);  // heads in this window
+    qblk = nqb - 1 - r / wh;
+    h = (win * kPfWin + r % wh) * 8 + x;
   }
   if (h >= n_h) return;  // the grid is padded to a multiple of 8 heads
   const int w_s = __builtin_amdgcn_readfirstlane(w);
@@ -103,6 +114,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   }
   const int rw_r = tid >> 3, cb_r = ((tid & 7) ^ pf_f8(tid >> 3)) * 16;
   const int kstride = (int)(ldk * 2);  // bytes between key rows of k^C / v^C
+  // source offsets of a full subtile (every row inside the sequence): loop
+  // invariant, the subtile's position goes into the resource base
+  const int vo_c0 = rw[0] * kstride + cb[0], vo_c1 = rw[1] * kstride + cb[1];
+  const int vo_r = rw_r * (kPfDr * 2) + cb_r;
   const int lds0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)smem);
   auto issue = [&](int s, int slot) {
     const int j0 = s * kPfSub, last = T - 1 - j0;
@@ -111,13 +126,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const i32x4_t rv = make_rsrc(v + (long long)j0 * ldk + (long long)h * kPfDh);
     const int m0b = lds0 + slot * kPfStage;
     dma_fence();
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma16_m0(rkc, min(rw[i], last) * kstride + cb[i], m0b + i * 4096 + w_s * 1024);
-    dma16_m0(rkr, min(rw_r, last) * (kPfDr * 2) + cb_r, m0b + kPfKcB + w_s * 1024);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma16_m0(rv, min(rw[i], last) * kstride + cb[i], m0b + kPfKcB + kPfKrB + i * 4096 + w_s * 1024);
+    int o0 = vo_c0, o1 = vo_c1, orr = vo_r;
+    if (last < kPfSub - 1) {  // the sequence's last subtile (uniform): clamp the rows
+      o0 = min(rw[0], last) * kstride + cb[0];
+      o1 = min(rw[1], last) * kstride + cb[1];
+      orr = min(rw_r, last) * (kPfDr * 2) + cb_r;
+    }
+    dma16_m0(rkc, o0, m0b + w_s * 1024);
+    dma16_m0(rkc, o1, m0b + 4096 + w_s * 1024);
+    dma16_m0(rkr, orr, m0b + kPfKcB + w_s * 1024);
+    dma16_m0(rv, o0, m0b + kPfKcB + kPfKrB + w_s * 1024);
+    dma16_m0(rv, o1, m0b + kPfKcB + kPfKrB + 4096 + w_s * 1024);
   };
 
   // LDS read offsets (relative to a ring slot, which is a compile-time
@@ -179,13 +198,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
           if (key > qrow || key >= T) sc[r] = -INFINITY;
         }
       }
-      float mx = sc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale2;
-      }
+      // row maximum as a tree of raw three-input maxima (scores are finite or
+      // -inf, never NaN, so fmaxf's quieting of each operand is not needed)
+      const float m0 = max3_raw(sc[0], sc[1], sc[2]), m1 = max3_raw(sc[3], sc[4], sc[5]);
+      const float m2 = max3_raw(sc[6], sc[7], sc[8]), m3 = max3_raw(sc[9], sc[10], sc[11]);
+      const float m4 = max3_raw(sc[12], sc[13], sc[14]);
+      const float m5 = max3_raw(m0, m1, m2), m6 = max3_raw(m3, m4, sc[15]);
+      const float mx = half_swap_max_raw(max3_raw(m5, m6, m6)) * scale2;
       // lazy reference: it moves only when some query's max exceeds it by
       // more than 2^kPfTau (numerator and denominator share it, so the result
       // is exact; p stays below 2^kPfTau)
