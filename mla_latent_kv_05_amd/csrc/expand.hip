@@ -207,24 +207,25 @@ __global__ __launch_bounds__(256) void expand_gemm_kernel(const uint16_t* a, lon
     const bool tile_end = c_ks == nk - 1;
     frags(s % kExRing, 1, fa1, fb1);
     mma(fa0, fb0);
-    if (s + 1 < total) {
-      // slice s + 1 landed: after it come the DMA of the slices issued
-      // later and, if issued after it, the last tile's stores
-      wait_at_most((n_issued - (s + 2)) * kExDma + (st_mark >= s + 2 ? kStores : 0));
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of slot s are done
-      __syncthreads();                     // ... and every wave's: slot s may be refilled
-      // three slices ahead (slot s % 4 takes slice s + 4), except that at a
-      // tile end slot s % 4 stages the results and is refilled one slice later
-      const int target = min(total, s + 5 - (tile_end ? 1 : 0));
-      while (n_issued < target) issue();
-      frags((s + 1) % kExRing, 0, fa0, fb0);
-    }
+    // The same straight-line step on every slice, the last included (a
+    // branch here leaves the compiler unsure on the join whether the second
+    // fragments have landed, and it then waits for the next slice's reads
+    // before the second MFMA group); on the last slice the wait covers every
+    // outstanding operation, nothing is issued and the fragment reads of the
+    // next slot stay inside LDS, unused.
+    // Slice s + 1 landed: after it come the DMA of the slices issued later
+    // and, if issued after it, the last tile's stores.
+    wait_at_most((n_issued - (s + 2)) * kExDma + (st_mark >= s + 2 ? kStores : 0));
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of slot s are done
+    __syncthreads();                     // ... and every wave's: slot s may be refilled
+    // kExRing - 1 slices ahead (slot s % kExRing takes slice s + kExRing),
+    // except that at a tile end slot s % kExRing stages the results and is
+    // refilled one slice later
+    const int target = min(total, s + kExRing + 1 - (tile_end ? 1 : 0));
+    while (n_issued < target) issue();
+    frags((s + 1) % kExRing, 0, fa0, fb0);
     mma(fa1, fb1);
     if (tile_end) {
-      if (s + 1 == total) {  // no barrier above: wait until every wave has read slot s
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __syncthreads();
-      }
       store_tile(c_tile, s % kExRing);
       zero_acc(acc);
       st_mark = n_issued;
