@@ -194,12 +194,22 @@ void decode_pipe_kernel(DecodeArgs a) {
     auto nvalid_of = [&](int t) { return t == n_sub - 1 ? n_last : kSub; };
 
     __syncthreads();  // the previous unit is done with LDS
-    // queries, their RoPE part and the unit's page ids in one round trip;
-    // everything is complete before the first DMA is issued, so the
-    // compiler's own vmcnt accounting never waits on a DMA
+    // the unit's page ids and the sequence's length first, then the queries
+    // and their RoPE part: the first DMA waits for the page ids alone and
+    // the query rows arrive under it.  Everything is complete (an explicit
+    // full wait) before the subtile loop, so the compiler's own vmcnt
+    // accounting never places a wait in the loop, where it would also wait
+    // for the DMA ring.
     bf16x8_t q[kQReg];
+    bf16x8_t qrv[4];
     lds_u8* qr_lds = smem + kF8QrOff;  // fp8: RoPE query rows, kQrStride bytes per head
     {
+      static_assert(kMaxUnitPages <= 512, "two page ids per thread");
+      const int npg = (n_sub * kSub + kBlk - 1) / kBlk;
+      const int32_t* trow = a.table + (long long)b * a.max_blocks + wk.y;
+      const int pg0 = tid < npg ? trow[tid] : 0;
+      const int pg1 = tid + 256 < npg ? trow[tid + 256] : 0;
+      const int len_now = a.seq_lens[b];
       // uniform row base + 32-bit per-lane offset (scalar base addressing)
       const long long row0 = ((long long)b * a.s_q + qi) * kHeads;
       const uint8_t* ql = (const uint8_t*)a.q_lat + row0 * (kDc * 2);
@@ -211,27 +221,29 @@ void decode_pipe_kernel(DecodeArgs a) {
       const int ol = hd * (kDc * 2) + gg * 16, orp = hd * (kDr * 2) + gg * 16;
 #pragma unroll
       for (int kb = 0; kb < 32; ++kb) q[kb] = *(const bf16x8_t*)(ql + ol + kb * 32);
-      bf16x8_t qrv[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) qrv[kb] = *(const bf16x8_t*)(qr + orp + kb * 32);
-      static_assert(kMaxUnitPages <= 512, "two page ids per thread");
-      const int npg = (n_sub * kSub + kBlk - 1) / kBlk;
-      const int32_t* trow = a.table + (long long)b * a.max_blocks + wk.y;
-      const int pg0 = tid < npg ? trow[tid] : 0;
-      const int pg1 = tid + 256 < npg ? trow[tid + 256] : 0;
-      const int len_now = a.seq_lens[b];
-      wait_vm<0>();
       // table slots past the sequence's pages may hold anything: an entry
       // reaching beyond them (not planned from these lengths) is skipped
       if (wk.z > max(1, (len_now + kBlk - 1) / kBlk)) continue;
       if (tid < npg) tab[tid] = pg0;
       if (tid + 256 < npg) tab[tid + 256] = pg1;
+    }
+    __syncthreads();  // page ids visible
+    // the queries in their operand form, after a full wait: below, once the
+    // first subtiles are in flight; the int formats (whose fp16 conversion
+    // would otherwise stay live across the DMA issue and spill into the
+    // loop) before any DMA
+    auto place_queries = [&]() {
       if (F16) {  // int caches: the products run on fp16 operands
 #pragma unroll
         for (int kb = 0; kb < 32; ++kb) q[kb] = bf16x8_as_f16(q[kb]);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) qrv[kb] = bf16x8_as_f16(qrv[kb]);
       }
+      int hl = threadIdx.x;
+      asm volatile("" : "+v"(hl));
+      const int hd = (hl >> 6) * 32 + (hl & 31), gg = (hl >> 5) & 1;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         if (FP8)
@@ -239,8 +251,11 @@ void decode_pipe_kernel(DecodeArgs a) {
         else
           q[(32 + kb) % kQReg] = qrv[kb];
       }
+    };
+    if (INT) {
+      wait_vm<0>();
+      place_queries();
     }
-    __syncthreads();  // page ids (and fp8 RoPE queries) visible
     // DMA instruction i (0 .. kDma-1) of subtile s for this wave; the bf16
     // tile lands swizzled, the fp8 staging (codes, k^R, scales) linear
     auto page_rsrc = [&](int s) {
@@ -254,9 +269,13 @@ void decode_pipe_kernel(DecodeArgs a) {
                                              : INT ? (s % kIntStages3) * kIntStageB(FMT)
                                                    : (s % kB16Stages) * kTileB)));
     };
-    auto dma_one = [&](const i32x4_t& rs, int m0b, int s, int i) {
+    // tv: the thread index the source offsets derive from (the prologue
+    // passes a copy the compiler cannot see through, so that its offsets
+    // are computed there instead of being the loop's, one of which the
+    // prologue's register pressure would spill and reload between DMAs)
+    auto dma_one = [&](const i32x4_t& rs, int m0b, int s, int i, int tv) {
       if (!STAGED) {
-        dma16_m0_stream(rs, dma_src_offset(i * 256 + tid), m0b + i * 4096 + w_s * 1024);
+        dma16_m0_stream(rs, dma_src_offset(i * 256 + tv), m0b + i * 4096 + w_s * 1024);
       } else if (INT) {
         // block: [64 x content codes | 64 x RoPE codes | 64 x parameters];
         // subtile half s & 1 of each part
@@ -289,12 +308,12 @@ void decode_pipe_kernel(DecodeArgs a) {
     // with no records (no memory traffic; zeros at most land in a ring slot
     // that is free at that point), so every iteration issues the same
     // instructions and every wait below has a constant count
-    auto issue = [&](int s) {
+    auto issue = [&](int s, int tv) {
       const i32x4_t rs = s < n_sub ? page_rsrc(s) : empty_rsrc();
       const int m0b = dma_dst(s);
       dma_fence();
 #pragma unroll
-      for (int i = 0; i < kDma; ++i) dma_one(rs, m0b, s, i);
+      for (int i = 0; i < kDma; ++i) dma_one(rs, m0b, s, i, tv);
     };
     auto tile_of = [&](int s) {
       return smem + (FP8 ? kF8SlotOff + (s & 1) * kTileB
@@ -429,10 +448,17 @@ void decode_pipe_kernel(DecodeArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
 
     if (n_sub > 0) {
+      int tv = threadIdx.x;
+      asm volatile("" : "+v"(tv));
 #pragma unroll
-      for (int s = 0; s <= kAhead; ++s) issue(s);
-      wait_vm<kAhead * kDma>();  // subtile 0 landed
-      __syncthreads();
+      for (int s = 0; s <= kAhead; ++s) issue(s, tv);
+      if (INT) {
+        wait_vm<kAhead * kDma>();  // subtile 0 landed
+      } else {
+        wait_vm<0>();  // the queries and subtiles 0 .. kAhead landed
+        place_queries();
+      }
+      __syncthreads();  // subtile 0 (and fp8 RoPE queries) visible
       if (STAGED) {
         convert(0, nvalid_of(0));
         __syncthreads();
@@ -661,7 +687,7 @@ void decode_pipe_kernel(DecodeArgs a) {
           if (step + 2 < 32) va[step & 1] = vfrag(tile, step + 2);
           ++step;
         }
-        if (((f - kQkA) & 1) == 0 && (f - kQkA) / 2 < kDma) dma_one(dma_rs, dma_m0, s_dma, (f - kQkA) / 2);
+        if (((f - kQkA) & 1) == 0 && (f - kQkA) / 2 < kDma) dma_one(dma_rs, dma_m0, s_dma, (f - kQkA) / 2, tid);
         __builtin_amdgcn_sched_barrier(0);
       }
       form_scores(it + 1);
