@@ -713,6 +713,13 @@ void decode_pipe_kernel(DecodeArgs a) {
     // subtile complete first)
     wait_vm<0>();
     acc_fence(acc);
+    // the finalize's lane indices and addresses derive from a copy of the
+    // thread index the compiler cannot see through, so that they are formed
+    // here: hoisted to the kernel start they live across the subtile loop
+    // and are spilled to scratch
+    int tf = threadIdx.x;
+    asm volatile("" : "+v"(tf));
+    const int wf = tf >> 6, gf = (tf >> 5) & 1, l32f = tf & 31, headf = wf * 32 + l32f;
     const float l_tot = half_swap_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
@@ -725,11 +732,11 @@ void decode_pipe_kernel(DecodeArgs a) {
     const bool bf16_out = to_out ? a.out_dtype != 0 : a.part_bf16 != 0;
     float* o32 = to_out ? (float*)a.out + orow0 * kDc : a.o_part + prow0 * kDc;
     uint16_t* o16 = to_out ? (uint16_t*)a.out + orow0 * kDc : (uint16_t*)a.o_part + prow0 * kDc;
-    if (g == 0) {
+    if (gf == 0) {
       if (!final_out)
-        a.lse_part[prow0 + head] = lse_v;
+        a.lse_part[prow0 + headf] = lse_v;
       else if (a.lse)
-        a.lse[orow0 + head] = lse_v;
+        a.lse[orow0 + headf] = lse_v;
     }
     __syncthreads();  // every wave is done with the tiles
     typedef __attribute__((address_space(3))) f32x4_t lds_f4;
@@ -737,7 +744,7 @@ void decode_pipe_kernel(DecodeArgs a) {
     typedef __attribute__((address_space(3))) u32x4_t lds_u4;
     if (bf16_out) {
       // all 128 rows at once in bf16, then 16-byte stores of whole rows
-      lds_u8* rowp = smem + (size_t)(w * 32 + l32) * kOutRowH;
+      lds_u8* rowp = smem + (size_t)(wf * 32 + l32f) * kOutRowH;
 #pragma unroll
       for (int db = 0; db < 16; ++db) {
         asm volatile("" : "+a"(acc[db]));  // one block at a time
@@ -747,12 +754,12 @@ void decode_pipe_kernel(DecodeArgs a) {
           u32x2_t pk;
           pk[0] = pack_bf16x2(t[4 * qd] * inv, t[4 * qd + 1] * inv);
           pk[1] = pack_bf16x2(t[4 * qd + 2] * inv, t[4 * qd + 3] * inv);
-          *(lds_u2*)(rowp + (db * 32 + 8 * qd + 4 * g) * 2) = pk;
+          *(lds_u2*)(rowp + (db * 32 + 8 * qd + 4 * gf) * 2) = pk;
         }
       }
       __syncthreads();
 #pragma unroll 4
-      for (int e = tid; e < kHeads * (kDc / 8); e += 256) {
+      for (int e = tf; e < kHeads * (kDc / 8); e += 256) {
         const int r = e / (kDc / 8), c8 = e % (kDc / 8);
         const u32x4_t v = *(const lds_u4*)(smem + (size_t)r * kOutRowH + c8 * 16);
         *(u32x4_t*)(o16 + (long long)r * kDc + 8 * c8) = v;
@@ -761,8 +768,8 @@ void decode_pipe_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
-      if ((w >> 1) == pass) {
-        lds_u8* rowp = smem + (size_t)((w & 1) * 32 + l32) * kOutRowF * 4;
+      if ((wf >> 1) == pass) {
+        lds_u8* rowp = smem + (size_t)((wf & 1) * 32 + l32f) * kOutRowF * 4;
 #pragma unroll
         for (int db = 0; db < 16; ++db) {
           asm volatile("" : "+a"(acc[db]));  // one block at a time
@@ -771,14 +778,14 @@ void decode_pipe_kernel(DecodeArgs a) {
           for (int qd = 0; qd < 4; ++qd) {
             f32x4_t v;
             v[0] = t[4 * qd] * inv; v[1] = t[4 * qd + 1] * inv; v[2] = t[4 * qd + 2] * inv; v[3] = t[4 * qd + 3] * inv;
-            *(lds_f4*)(rowp + (db * 32 + 8 * qd + 4 * g) * 4) = v;
+            *(lds_f4*)(rowp + (db * 32 + 8 * qd + 4 * gf) * 4) = v;
           }
         }
       }
       __syncthreads();
       // 64 staged rows (heads 64*pass ..) x 512 floats: 128 threads per row, 16 B each
 #pragma unroll 4
-      for (int e = tid; e < 64 * (kDc / 4); e += 256) {
+      for (int e = tf; e < 64 * (kDc / 4); e += 256) {
         const int r = e / (kDc / 4), c4 = e % (kDc / 4);
         const f32x4_t v = *(const lds_f4*)(smem + ((size_t)r * kOutRowF + 4 * c4) * 4);
         const long long row = 64 * pass + r;
