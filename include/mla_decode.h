@@ -319,9 +319,12 @@ size_t mla_decode_step_workspace_bytes(int B, int s_q, int n_h, int d_c, int max
  *  c_kv      [T, d_c], token stride c_stride_t, dtype act_dtype
  *  w_uk/w_uv [n_h*d_h, d_c] ([out, in]; head i = rows i*d_h ..), dtype w_dtype
  *  k_c, v_c  [T, n_h, d_h] contiguous, dtype out_dtype
- *  bf16 inputs take the MFMA up-projection kernel (same limits and
- *  alignment rules as mla_up_proj_v), other combinations a plain fp32 kernel.
- *  T == 0 is a no-op. */
+ *  bf16 inputs with n_h*d_h a multiple of 256, d_c a multiple of 32, the
+ *  token stride a multiple of 8 elements and 16-byte aligned pointers (8 for
+ *  bf16 outputs) take the expansion GEMM kernel (both products in one
+ *  launch); other bf16 shapes the MFMA up-projection kernel (same limits and
+ *  alignment rules as mla_up_proj_v), other combinations a plain fp32
+ *  kernel.  T == 0 is a no-op. */
 int mla_expand_kv(const void* c_kv, int64_t c_stride_t, const void* w_uk, const void* w_uv, void* k_c,
                   void* v_c, int T, int n_h, int d_c, int d_h, int act_dtype, int w_dtype, int out_dtype,
                   void* stream);
