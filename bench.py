@@ -193,8 +193,8 @@ def settle_device(run_step, max_ms: float, min_ms: float = 50.0, window: int = 1
 
 
 def device_info(dev) -> dict:
-    """Software versions and the device's compute clock as the driver reports
-    it (the sclk levels of the card in sysfs, where readable)."""
+    """Software versions and the device's compute clock as the amdgpu kernel
+    module lists it (the sclk levels of the card in sysfs, where readable)."""
     import glob
 
     import torch
