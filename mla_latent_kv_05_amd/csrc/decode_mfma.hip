@@ -258,11 +258,14 @@ void decode_pipe_kernel(DecodeArgs a) {
     }
     // DMA instruction i (0 .. kDma-1) of subtile s for this wave; the bf16
     // tile lands swizzled, the fp8 staging (codes, k^R, scales) linear
-    auto page_rsrc = [&](int s) {
-      const int pg = __builtin_amdgcn_readfirstlane(tab[s >> 1]);
+    // descriptor of subtile s's half of its page pg (a page id read from the
+    // unit's table in LDS)
+    auto page_rsrc_of = [&](int s, int pg_lds) {
+      const int pg = __builtin_amdgcn_readfirstlane(pg_lds);
       const uint8_t* blk = (const uint8_t*)a.kv + (long long)pg * a.block_bytes;
       return make_rsrc(STAGED ? blk : blk + (s & 1) * kTileB);
     };
+    auto page_rsrc = [&](int s) { return page_rsrc_of(s, tab[s >> 1]); };
     auto dma_dst = [&](int s) {  // LDS base (scalar) of subtile s's DMA landing area for this wave
       return __builtin_amdgcn_readfirstlane(
           (int)(uint32_t)(uintptr_t)(smem + (FP8   ? (s % kF8Stages3) * kF8StageB
@@ -635,6 +638,28 @@ void decode_pipe_kernel(DecodeArgs a) {
     }
 
     constexpr int kQkA = 16;  // QK steps overlapped with the softmax
+    // The last kCarry P.V steps of a subtile run at the start of the next
+    // iteration: their value fragments are read into vc before the barrier,
+    // so after it the MFMA pipe has work while the first key fragments of
+    // the next subtile come from LDS (alone, the softmax phase's first steps
+    // waited out the pipe drain, the barrier and that LDS latency).  Their
+    // slot is refilled only in the next P.V phase, after the reads have
+    // completed at the barrier.  Zero operands before the first subtile.
+    // (The int formats' registers spill with it.)
+    constexpr int kCarry = INT ? 0 : 4;
+    bf16x8_t vc[kCarry > 0 ? kCarry : 1];
+#pragma unroll
+    for (int j = 0; j < (kCarry > 0 ? kCarry : 1); ++j) vc[j] = bf16x8_t{};
+    P[0] = bf16x8_t{};
+    P[1] = bf16x8_t{};
+    auto carried_pv = [&]() {
+#pragma unroll
+      for (int j = 0; j < kCarry; ++j) mfma_acc_op<F16>(acc[(32 - kCarry + j) & 15], vc[j], P[1]);
+    };
+    // the page id of the loop's DMA one iteration ahead (an LDS read at the
+    // top of the iteration that uses it put its latency before the key
+    // fragments' reads); entries past the unit's pages are read, not used
+    int pg_next = tab[min((kAhead + 1) >> 1, kMaxUnitPages - 1)];
     for (int it = 0; it + 1 < n_sub; ++it) {
       // ---- (A) next subtile resident; refill the stage subtile it-1 used
       wait_vm<(kAhead - 1) * kDma>();  // subtile it+1 landed (one group, it+2, may fly)
@@ -649,7 +674,8 @@ void decode_pipe_kernel(DecodeArgs a) {
       // subtile it+kAhead+1 goes to the stage subtile it-1 (bf16) / it (fp8)
       // used; its DMA instructions are spread over the QK steps below
       const int s_dma = it + kAhead + 1;
-      const i32x4_t dma_rs = s_dma < n_sub ? page_rsrc(s_dma) : empty_rsrc();
+      const i32x4_t dma_rs = s_dma < n_sub ? page_rsrc_of(s_dma, pg_next) : empty_rsrc();
+      pg_next = tab[min((s_dma + 1) >> 1, kMaxUnitPages - 1)];
       const int dma_m0 = dma_dst(s_dma);
       dma_fence();
       const lds_u8* tile = tile_of(it);
@@ -660,6 +686,9 @@ void decode_pipe_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) { sc[r] = 0.f; sr[r] = 0.f; }
       bf16x8_t ka[2] = {kfrag(tile_n, 0), kfrag(tile_n, 1)};
+      __builtin_amdgcn_sched_barrier(0);
+      carried_pv();  // subtile it's last P.V steps, under the key fragments' latency
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int f = 0; f < kQkA; ++f) {
         sc = mfma_op<F16>(ka[f & 1], qfrag(f), sc);
@@ -680,22 +709,26 @@ void decode_pipe_kernel(DecodeArgs a) {
       for (int f = kQkA; f < 36; ++f) {
         if (FP8 && f >= 32) sr = mfma_op<F16>(ka[f & 1], qfrag(f), sr); else sc = mfma_op<F16>(ka[f & 1], qfrag(f), sc);
         if (f + 2 < 36) ka[f & 1] = kfrag(tile_n, f + 2);
-        const int npv = (f - kQkA) < 12 ? 2 : 1;
+        // 32 - kCarry P.V steps here: two per QK step first, then one
+        const int npv = (f - kQkA) < 12 - kCarry ? 2 : 1;
 #pragma unroll
         for (int u = 0; u < npv; ++u) {
           mfma_acc_op<F16>(acc[step & 15], va[step & 1], P[step >> 4]);
-          if (step + 2 < 32) va[step & 1] = vfrag(tile, step + 2);
+          if (step + 2 < 32 - kCarry) va[step & 1] = vfrag(tile, step + 2);
           ++step;
         }
         if (((f - kQkA) & 1) == 0 && (f - kQkA) / 2 < kDma) dma_one(dma_rs, dma_m0, s_dma, (f - kQkA) / 2, tid);
         __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int j = 0; j < kCarry; ++j) vc[j] = vfrag(tile, 32 - kCarry + j);
       form_scores(it + 1);
       sp = sc;
       sp_sub = it + 1;
       mask_tail(sp, nvalid_of(it + 1));
     }
     if (n_sub > 0) {  // the last subtile: softmax and P.V only
+      carried_pv();  // the previous subtile's (before its P is overwritten)
       const lds_u8* tile = tile_of(n_sub - 1);
 #pragma unroll
       for (int st = 0; st <= 10; ++st) sm_stage(st);
