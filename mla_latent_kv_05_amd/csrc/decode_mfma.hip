@@ -637,7 +637,7 @@ void decode_pipe_kernel(DecodeArgs a) {
       m_run = row_max(sp);
     }
 
-    constexpr int kQkA = 16;  // QK steps overlapped with the softmax
+    constexpr int kQkA = 20;  // QK steps overlapped with the softmax
     // The last kCarry P.V steps of a subtile run at the start of the next
     // iteration: their value fragments are read into vc before the barrier,
     // so after it the MFMA pipe has work while the first key fragments of
@@ -709,15 +709,19 @@ void decode_pipe_kernel(DecodeArgs a) {
       for (int f = kQkA; f < 36; ++f) {
         if (FP8 && f >= 32) sr = mfma_op<F16>(ka[f & 1], qfrag(f), sr); else sc = mfma_op<F16>(ka[f & 1], qfrag(f), sc);
         if (f + 2 < 36) ka[f & 1] = kfrag(tile_n, f + 2);
-        // 32 - kCarry P.V steps here: two per QK step first, then one
-        const int npv = (f - kQkA) < 12 - kCarry ? 2 : 1;
+        // 32 - kCarry P.V steps over the 36 - kQkA QK steps here: two per
+        // QK step first, then one
+        const int npv = (f - kQkA) < (32 - kCarry) - (36 - kQkA) ? 2 : 1;
 #pragma unroll
         for (int u = 0; u < npv; ++u) {
           mfma_acc_op<F16>(acc[step & 15], va[step & 1], P[step >> 4]);
           if (step + 2 < 32 - kCarry) va[step & 1] = vfrag(tile, step + 2);
           ++step;
         }
-        if (((f - kQkA) & 1) == 0 && (f - kQkA) / 2 < kDma) dma_one(dma_rs, dma_m0, s_dma, (f - kQkA) / 2, tid);
+        // the DMA group: one instruction every kDmaSp QK steps
+        constexpr int kDmaSp = 36 - kQkA >= 2 * kDma ? 2 : 1;
+        if ((f - kQkA) % kDmaSp == 0 && (f - kQkA) / kDmaSp < kDma)
+          dma_one(dma_rs, dma_m0, s_dma, (f - kQkA) / kDmaSp, tid);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
