@@ -27,8 +27,10 @@
 //     denominator share the reference, so the result is exact).
 //
 // Pipeline (iteration i; subtile i+1 resident before it starts)
-//   phase 1: QK(i+1) steps 0..15  ||  softmax of subtile i (max, exp2, P)
-//   phase 2: QK(i+1) steps 16..35 interleaved with the 32 P.V steps of
+//   phase 1: the last P.V steps of subtile i-1 (value fragments read before
+//            the barrier), then QK(i+1) steps 0..19  ||  softmax of subtile
+//            i (max, exp2, P)
+//   phase 2: QK(i+1) steps 20..35 interleaved with the other P.V steps of
 //            subtile i; the DMA of a later subtile rides along
 //
 // LDS tile layout: row t (token) is 1152 B = 72 chunks of 16 B; logical chunk
@@ -681,8 +683,8 @@ void decode_pipe_kernel(DecodeArgs a) {
       const lds_u8* tile = tile_of(it);
       const lds_u8* tile_n = tile_of(it + 1);
 
-      // ---- phase 1: QK(it+1) steps 0..15 (one dependent chain) with the
-      //      softmax of subtile it in the gaps
+      // ---- phase 1: QK(it+1) steps 0..kQkA-1 (one dependent chain) with
+      //      the softmax of subtile it in the gaps
 #pragma unroll
       for (int r = 0; r < 16; ++r) { sc[r] = 0.f; sr[r] = 0.f; }
       bf16x8_t ka[2] = {kfrag(tile_n, 0), kfrag(tile_n, 1)};
@@ -700,9 +702,9 @@ void decode_pipe_kernel(DecodeArgs a) {
       }
       sm_commit();
 
-      // ---- phase 2: QK(it+1) steps 16..35 interleaved with the 32 P.V
-      //      steps of subtile it (12 x [QK, PV, PV] + 8 x [QK, PV]); the
-      //      DMA of subtile it+3 rides along
+      // ---- phase 2: QK(it+1) steps kQkA..35 interleaved with the first
+      //      32 - kCarry P.V steps of subtile it; the DMA of subtile it+3
+      //      rides along
       bf16x8_t va[2] = {vfrag(tile, 0), vfrag(tile, 1)};
       int step = 0;
 #pragma unroll
