@@ -260,7 +260,8 @@ def make_lengths(kind: str, B: int, rng, L: int | None = None,
 def decode_case(seed: int, B: int, seq_lens, s_q: int = 1, n_h: int = 128,
                 d_c: int = 512, d_r: int = 64, d_h: int = 128, kv_dtype: str = "bf16",
                 q_dtype: str = "bf16", block_size: int = BLOCK, q_lat_std: float | None = None,
-                extra_blocks: int = 0, tail_fill: str = "random") -> DecodeCase:
+                extra_blocks: int = 0, tail_fill: str = "random",
+                rope0_shift: list | None = None) -> DecodeCase:
     """Paged absorbed-decode inputs.
 
     ``seq_lens`` is an int, or an array of per-sequence lengths.  Physical
@@ -268,7 +269,11 @@ def decode_case(seed: int, B: int, seq_lens, s_q: int = 1, n_h: int = 128,
     (sequence, logical block) order.  ``extra_blocks`` adds unreferenced
     physical blocks; ``tail_fill`` = "nan" poisons the unused tail rows of each
     sequence's last block (bf16/f32 caches) to show they are never read into
-    the result."""
+    the result.  ``rope0_shift`` (one array of length seq_lens[b] per
+    sequence) is added to dimension 0 of each row's k^R before the row is
+    encoded: with a query whose RoPE dimension 0 is non-zero it shapes the
+    scores along the sequence (steps, ramps) without touching the stream of
+    random draws."""
     rng = np.random.Generator(np.random.PCG64(seed))
     lens = np.full(B, seq_lens, dtype=np.int32) if np.isscalar(seq_lens) else \
         np.asarray(seq_lens, dtype=np.int32)
@@ -297,10 +302,22 @@ def decode_case(seed: int, B: int, seq_lens, s_q: int = 1, n_h: int = 128,
         cache = np.empty((num_blocks, block_size * int_row_bytes(d_c, d_r, cbits)), dtype=np.uint8)
     else:
         raise ValueError(kv_dtype)
+    shift = None
+    if rope0_shift is not None:
+        assert len(rope0_shift) == B
+        shift = np.zeros((num_blocks, block_size))
+        for b in range(B):
+            sb = np.asarray(rope0_shift[b], dtype=np.float64)
+            assert sb.shape == (lens[b],)
+            for j in range(nblk[b]):
+                part = sb[j * block_size: (j + 1) * block_size]
+                shift[table[b, j], : part.size] = part
     chunk = 32
     for i0 in range(0, num_blocks, chunk):
         i1 = min(num_blocks, i0 + chunk)
         rows = _draw(rng, (i1 - i0, block_size, D), 1.0, kind)
+        if shift is not None:
+            rows[..., d_c] += shift[i0:i1].astype(rows.dtype)
         if kv_dtype == "bf16":
             cache[i0:i1] = f32_to_bf16_bits(rows)
         elif kv_dtype == "f32":

@@ -136,6 +136,49 @@ def test_v3_int_cache(kv, s_q, force_generic):
         assert_lse_close(gl, ol, "lse")
 
 
+# Scores that climb in steps along each sequence: RoPE dimension 0 of every
+# query is 1 (its other RoPE dimensions are scaled by 1/4) and k^R dimension 0
+# of the row at position p holds 84 times the number of step positions <= p
+# less the number of steps (the last level is 0), so each step lifts the
+# log2-domain score by 84 * log2(e) / sqrt(192) ~ 8.75 while the random parts
+# spread it by ~0.3.  Ending at 0 keeps the heavy rows' scores small: the int
+# caches' values, rounded to fp16 when decoded, carry a relative error of
+# 2^-11 into each score, which at the top level of a staircase that climbs
+# from 0 (scores ~28) would alone move the LSE by 1.5e-3.  The running reference max of the
+# online softmax then has to move by more than the lazy threshold (2^8) at
+# every step past the first subtile, inside units and in their last subtile,
+# while the rows before a step keep 1-8 % of the weight (the last step comes
+# 30-70 rows before the end): a rescale factor off by 2x moves o_lat by that
+# much, and a P.V step applied on the wrong side of a rescale by far more.
+STEP_LENS = np.array([4096, 2049, 1500, 700, 300, 129, 3333, 97], dtype=np.int32)
+STEP_AT = [[1024, 2048, 3000, 4060], [64, 1000, 2010], [33, 97, 700, 1460], [300, 660],
+           [100, 264], [90], [5, 2000, 3300], [60]]
+
+
+def _stepped_case(seed, kv, s_q):
+    shift = [84.0 * (np.searchsorted(np.asarray(at), np.arange(n), side="right") - len(at))
+             for n, at in zip(STEP_LENS, STEP_AT)]
+    case = inputs.decode_case(seed, B=len(STEP_LENS), seq_lens=STEP_LENS, s_q=s_q, kv_dtype=kv,
+                              rope0_shift=shift, **V3)
+    qr = inputs.bf16_bits_as_f32(case.q_rope)
+    qr[..., 0] = 1.0
+    qr[..., 1:] *= 0.25
+    case.q_rope = inputs.f32_to_bf16_bits(qr)
+    return case
+
+
+@pytest.mark.parametrize("force_generic", [False, True])
+@pytest.mark.parametrize("kv,s_q", [("bf16", 1), ("fp8", 2), ("int4", 1)])
+def test_v3_rising_scores_rescale(kv, s_q, force_generic):
+    say(f"v3 {kv} s_q={s_q} stepped scores generic={force_generic}")
+    case = _stepped_case(31, kv, s_q)
+    o, ol = oracle.mqa_decode_case(case)
+    for splits in (0, 1, 3):
+        g, gl = run_decode(case, num_splits=splits, force_generic=force_generic)
+        assert_bf16_close(g, o, f"{kv} stepped splits={splits}")
+        assert_lse_close(gl, ol, "lse")
+
+
 @pytest.mark.parametrize("kv", ["int4", "int2"])
 def test_toy_int_cache_fp32_queries(kv):
     """fp32 queries at the toy dimensions (n_h 8, d_c 128, d_r 32): the
