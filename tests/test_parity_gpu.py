@@ -155,9 +155,13 @@ STEP_AT = [[1024, 2048, 3000, 4060], [64, 1000, 2010], [33, 97, 700, 1460], [300
            [100, 264], [90], [5, 2000, 3300], [60]]
 
 
+def _stair(n, at):
+    """Per position 0..n-1: 84 x (steps at or before it - all steps)."""
+    return 84.0 * (np.searchsorted(np.asarray(at), np.arange(n), side="right") - len(at))
+
+
 def _stepped_case(seed, kv, s_q):
-    shift = [84.0 * (np.searchsorted(np.asarray(at), np.arange(n), side="right") - len(at))
-             for n, at in zip(STEP_LENS, STEP_AT)]
+    shift = [_stair(n, at) for n, at in zip(STEP_LENS, STEP_AT)]
     case = inputs.decode_case(seed, B=len(STEP_LENS), seq_lens=STEP_LENS, s_q=s_q, kv_dtype=kv,
                               rope0_shift=shift, **V3)
     qr = inputs.bf16_bits_as_f32(case.q_rope)
@@ -617,6 +621,29 @@ def test_prefill_mha_bf16_v3(T):
         assert np.all(np.abs(g[0] - v0) <= 1e-6 * np.abs(v0))
 
 
+def test_prefill_mha_bf16_rising_scores():
+    """Causal prefill with scores that climb in steps along the keys (the
+    staircase of the decode test on k^R dimension 0, query RoPE dimension 0
+    = 1, the other query dimensions scaled by 1/4): every query block's
+    reference max has to move as the key stream enters each new level."""
+    say("prefill bf16 stepped scores")
+    T, at = 300, [40, 100, 170, 260, 290]
+    inp = inputs.prefill_inputs(131, T, n_h=16, d_c=64)
+    d_h = inp["d_h"]
+    kr = inputs.bf16_bits_as_f32(inp["k_r"])
+    kr[:, 0] += _stair(T, at)
+    inp["k_r"] = inputs.f32_to_bf16_bits(kr)
+    q = inputs.bf16_bits_as_f32(inp["q"]) * np.float32(0.25)
+    q[..., d_h] = 1.0
+    inp["q"] = inputs.f32_to_bf16_bits(q)
+    q_, k_c, k_r, v_c = _pf_dev(inp, "q", "k_c", "k_r", "v_c")
+    o, lse = binding.prefill_mha(q_, k_c, k_r, v_c, inp["scale"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = _pf_oracle(inp)
+    assert_bf16_close(o.cpu().numpy().astype(np.float64), ref_o, "prefill stepped")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64), ref_lse, "prefill stepped lse")
+
+
 @pytest.mark.parametrize("T,n_h", [(200, 3), (129, 9)])
 def test_prefill_mha_bf16_head_counts_off_the_xcd_multiple(T, n_h):
     """MFMA kernel with head counts that are not a multiple of the 8 XCDs
@@ -808,6 +835,29 @@ def test_gqa_decode_bf16_v3(s_q, n_g, lens, force_generic):
     assert_lse_close(gl, ol, "gqa lse")
     g16, _ = _gqa_gpu(case, force_generic, out_dtype=torch.bfloat16)
     assert_bf16_close(g16, o, "gqa o bf16")
+
+
+@pytest.mark.parametrize("force_generic", [False, True])
+def test_gqa_decode_bf16_rising_scores(force_generic):
+    """GQA path with the decode test's stepped scores (k^R dimension 0 of each
+    cached row raised by the staircase, query RoPE dimension 0 = 1, the other
+    query dimensions scaled by 1/4), two new tokens."""
+    say(f"gqa bf16 stepped scores generic={force_generic}")
+    case = inputs.gqa_case(47, B=len(STEP_LENS), seq_lens=STEP_LENS, s_q=2, n_g=8)
+    bs, off = case.block_size, 2 * case.n_g * case.block_size * case.d_h
+    vals = inputs.bf16_bits_as_f32(case.cache)
+    for b, (n, at) in enumerate(zip(STEP_LENS, STEP_AT)):
+        pos = np.arange(n)
+        vals[case.block_table[b, pos // bs], off + (pos % bs) * case.d_r] += _stair(n, at)
+    case.cache = inputs.f32_to_bf16_bits(vals)
+    case.q_c = inputs.f32_to_bf16_bits(inputs.bf16_bits_as_f32(case.q_c) * np.float32(0.25))
+    qr = inputs.bf16_bits_as_f32(case.q_r) * np.float32(0.25)
+    qr[..., 0] = 1.0
+    case.q_r = inputs.f32_to_bf16_bits(qr)
+    g, gl = _gqa_gpu(case, force_generic)
+    o, ol = _gqa_oracle(case)
+    assert_bf16_close(g, o, "gqa stepped o")
+    assert_lse_close(gl, ol, "gqa stepped lse")
 
 
 def test_gqa_decode_bf16_four_tokens_of_eight_heads():
