@@ -457,8 +457,15 @@ void decode_pipe_kernel(DecodeArgs a) {
       asm volatile("" : "+v"(tv));
 #pragma unroll
       for (int s = 0; s <= kAhead; ++s) issue(s, tv);
-      if (INT) {
-        wait_vm<kAhead * kDma>();  // subtile 0 landed
+      if (INT || !STAGED) {
+        // the queries (issued first) and subtile 0 landed; subtiles
+        // 1 .. kAhead may still fly.  bf16: the first subtile's QK steps
+        // start under their arrival (the compiler's own waits before the
+        // later query fragments' first uses count only the query loads, so
+        // they also wait for the DMAs issued after them: those steps keep
+        // pace with the arrivals, and every load is complete by the last
+        // step, before the loop)
+        wait_vm<kAhead * kDma>();
       } else {
         wait_vm<0>();  // the queries and subtiles 0 .. kAhead landed
         place_queries();
@@ -627,11 +634,15 @@ void decode_pipe_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) { sc[r] = 0.f; sr[r] = 0.f; }
       bf16x8_t ka[2] = {kfrag(tile, 0), kfrag(tile, 1)};
+      // bf16: the RoPE query fragments straight from their loads (placed
+      // into the query array after this subtile)
+      auto qfrag0 = [&](int f) { return !STAGED && f >= 32 ? qrv[f - 32] : qfrag(f); };
 #pragma unroll
       for (int f = 0; f < 36; ++f) {
-        if (FP8 && f >= 32) sr = mfma_op<F16>(ka[f & 1], qfrag(f), sr); else sc = mfma_op<F16>(ka[f & 1], qfrag(f), sc);
+        if (FP8 && f >= 32) sr = mfma_op<F16>(ka[f & 1], qfrag0(f), sr); else sc = mfma_op<F16>(ka[f & 1], qfrag0(f), sc);
         if (f + 2 < 36) ka[f & 1] = kfrag(tile, f + 2);
       }
+      if (!STAGED) place_queries();
       form_scores(0);
       sp = sc;
       sp_sub = 0;
