@@ -660,6 +660,7 @@ void decode_pipe_kernel(DecodeArgs a) {
     // completed at the barrier.  Zero operands before the first subtile.
     // (The int formats' registers spill with it.)
     constexpr int kCarry = INT ? 0 : 4;
+    static_assert(32 - kCarry <= 2 * (36 - kQkA), "at most two P.V steps per QK step of the second phase");
     bf16x8_t vc[kCarry > 0 ? kCarry : 1];
 #pragma unroll
     for (int j = 0; j < (kCarry > 0 ? kCarry : 1); ++j) vc[j] = bf16x8_t{};
