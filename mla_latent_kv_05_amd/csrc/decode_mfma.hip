@@ -198,10 +198,13 @@ void decode_pipe_kernel(DecodeArgs a) {
     __syncthreads();  // the previous unit is done with LDS
     // the unit's page ids and the sequence's length first, then the queries
     // and their RoPE part: the first DMA waits for the page ids alone and
-    // the query rows arrive under it.  Everything is complete (an explicit
-    // full wait) before the subtile loop, so the compiler's own vmcnt
-    // accounting never places a wait in the loop, where it would also wait
-    // for the DMA ring.
+    // the query rows arrive under it.  Every query load is complete before
+    // the subtile loop (an explicit full wait, or for bf16 the compiler's own
+    // waits in the first subtile's QK chain, which also cover the DMAs issued
+    // after the queries), so the compiler's vmcnt accounting never places a
+    // wait in the loop, where it would also wait for the DMA ring.  (Its
+    // waits are conservative: it does not count the DMAs, which are all
+    // younger than the queries; the loop's explicit waits stay exact.)
     bf16x8_t q[kQReg];
     bf16x8_t qrv[4];
     lds_u8* qr_lds = smem + kF8QrOff;  // fp8: RoPE query rows, kQrStride bytes per head
