@@ -94,7 +94,7 @@ def test_v3_bf16_output_dtype_bf16():
     assert_lse_close(gl, ol, "lse")
 
 
-@pytest.mark.parametrize("s_q", [2, 3])
+@pytest.mark.parametrize("s_q", [2, 3, 4])
 def test_v3_bf16_multi_token_causal(s_q):
     say(f"v3 bf16 s_q={s_q}")
     lens = np.array([s_q, 40, 64, 65, 300], dtype=np.int32)
