@@ -138,10 +138,10 @@ size_t mla_decode_workspace_bytes(int B, int s_q, int n_h, int d_c, int max_bloc
  *           bytes; its contents need no initialisation and are clobbered.
  *  flags    0 or MLA_FLAG_FORCE_GENERIC.
  *
- * Kernel selection: bf16 queries, bf16 or fp8 cache, n_h == 128, d_c == 512,
- * d_r == 64, block_size == 64 and 16-byte aligned cache/query pointers take
- * the MFMA kernel; everything else (fp32, other shapes) takes a portable
- * fp32 kernel.  Constraints: 1 <= s_q <= 16, d_c <= 2048, d_r <= 256,
+ * Kernel selection: bf16 queries, a bf16, fp8, int4 or int2 cache, n_h == 128,
+ * d_c == 512, d_r == 64, block_size == 64 and 16-byte aligned cache/query
+ * pointers take the MFMA kernel; everything else (fp32, other shapes) takes a
+ * portable fp32 kernel.  Constraints: 1 <= s_q <= 16, d_c <= 2048, d_r <= 256,
  * d_c % 4 == 0.
  * Device-side preconditions (not checked, they would need a synchronisation):
  *   s_q <= seq_lens[b] <= max_blocks_per_seq*block_size, and every table
