@@ -297,7 +297,9 @@ def test_more_partitions_than_the_merge_caches():
     ("v3_bf16_B128_ctxlogU128-32768", None),
     ("v3_bf16_B4_ctx131072", [2]),
     ("v3_fp8_B64_ctx16384_sq2", [0, 63]),
+    ("v3_bf16_B64_ctx8192_sq2", [3, 61]),
     ("v3_int4_B64_ctx8192", [5, 60]),
+    ("v3_int2_B64_ctx8192", [7, 58]),
 ])
 def test_full_size_workloads_sampled(name, seqs):
     """Full workload shape in the automatic split configuration the benchmark
