@@ -268,7 +268,8 @@ def decode_case(seed: int, B: int, seq_lens, s_q: int = 1, n_h: int = 128,
     block ids are one seeded permutation of 0..num_blocks-1 handed out in
     (sequence, logical block) order.  ``extra_blocks`` adds unreferenced
     physical blocks; ``tail_fill`` = "nan" poisons the unused tail rows of each
-    sequence's last block (bf16/f32 caches) to show they are never read into
+    sequence's last block (bf16 / f32 rows; fp8 codes, RoPE keys and scales;
+    int4 / int2 group scales and minima) to show they are never read into
     the result.  ``rope0_shift`` (one array of length seq_lens[b] per
     sequence) is added to dimension 0 of each row's k^R before the row is
     encoded: with a query whose RoPE dimension 0 is non-zero it shapes the
@@ -333,12 +334,26 @@ def decode_case(seed: int, B: int, seq_lens, s_q: int = 1, n_h: int = 128,
             cache[i0:i1, :o1] = codes.reshape(n, -1)
             cache[i0:i1, o1:o2] = kr.reshape(n, -1).view(np.uint8).reshape(n, -1)
             cache[i0:i1, o2:] = scale.reshape(n, -1).view(np.uint8).reshape(n, -1)
-    if tail_fill == "nan" and kv_dtype in ("bf16", "f32"):
+    if tail_fill == "nan":
         for b in range(B):
             used = lens[b] - (nblk[b] - 1) * block_size
-            if used < block_size:
-                pb = table[b, nblk[b] - 1]
+            if used == block_size:
+                continue
+            pb = table[b, nblk[b] - 1]
+            if kv_dtype in ("bf16", "f32"):
                 cache[pb, used:] = 0x7FC0 if kv_dtype == "bf16" else np.nan
+            elif kv_dtype == "fp8":  # NaN codes (0x7F), NaN bf16 k^R, NaN fp32 scales
+                o1 = block_size * d_c
+                o2 = o1 + block_size * d_r * 2
+                blk = cache[pb]
+                blk[used * d_c: o1] = 0x7F
+                blk[o1 + used * d_r * 2: o2].view(np.uint16)[:] = 0x7FC0
+                blk[o2 + used * 4: o2 + block_size * 4].view(np.float32)[:] = np.nan
+            else:  # int4 / int2: NaN fp16 scale and minimum of every group of the tail rows
+                cb = 4 if kv_dtype == "int4" else 2
+                o2 = block_size * (d_c * cb // 8 + d_r // 2)
+                prow = (d_c + d_r) // INT_GROUP * 4
+                cache[pb, o2 + used * prow: o2 + block_size * prow].view(np.uint16)[:] = 0x7E00
     if q_lat_std is None:
         q_lat_std = 1.0 / math.sqrt(d_c)
     ql = _draw(rng, (B, s_q, n_h, d_c), q_lat_std, kind)

@@ -57,3 +57,39 @@ def test_workload_shapes():
     f = inputs.workload_case("v3_fp8_B64_ctx16384_sq2", B=2, L=128)
     assert f.cache.shape == (4, 64 * 644) and f.s_q == 2
     assert f.latent_bytes == 2 * 128 * 644
+
+
+def test_nan_tail_poisons_only_the_unused_rows():
+    """tail_fill="nan": every format's unused rows of a sequence's last block
+    hold NaN patterns (bf16 rows; fp8 codes, RoPE keys, scales; int group
+    scales and minima), while the rows the sequence uses decode to finite
+    values."""
+    import oracle
+    lens = np.array([1, 33, 64, 100], dtype=np.int32)
+    bs = inputs.BLOCK
+    for kv in ("bf16", "fp8", "int4", "int2"):
+        c = inputs.decode_case(41, B=len(lens), seq_lens=lens, kv_dtype=kv, tail_fill="nan",
+                               n_h=2, d_c=64, d_r=32, d_h=16)
+        for b, L in enumerate(lens):
+            ck, kr = oracle.paged_rows(c.cache, c.block_table[b], int(L), kv, 64, 32, bs)
+            assert np.isfinite(ck).all() and np.isfinite(kr).all()
+            used = int(L) - ((int(L) + bs - 1) // bs - 1) * bs
+            blk = c.cache[c.block_table[b, (int(L) - 1) // bs]]
+            if used == bs:
+                continue
+            if kv == "bf16":
+                assert (blk[used:] == 0x7FC0).all() and not (blk[:used] == 0x7FC0).all()
+            elif kv == "fp8":
+                raw = blk.view(np.uint8)
+                o1, o2 = bs * 64, bs * 64 + bs * 32 * 2
+                assert (raw[used * 64: o1] == 0x7F).all()
+                assert (raw[o1 + used * 64: o2].view(np.uint16) == 0x7FC0).all()
+                assert np.isnan(raw[o2 + used * 4: o2 + bs * 4].view(np.float32)).all()
+                assert np.isfinite(raw[o2: o2 + used * 4].view(np.float32)).all()
+            else:
+                cb = 4 if kv == "int4" else 2
+                o2 = bs * (64 * cb // 8 + 32 // 2)
+                prow = (64 + 32) // inputs.INT_GROUP * 4
+                prm = blk.view(np.uint8)[o2: o2 + bs * prow].view(np.float16)
+                assert np.isnan(prm[used * prow // 2:]).all()
+                assert np.isfinite(prm[: used * prow // 2]).all()

@@ -183,6 +183,22 @@ def test_v3_rising_scores_rescale(kv, s_q, force_generic):
         assert_lse_close(gl, ol, "lse")
 
 
+@pytest.mark.parametrize("force_generic", [False, True])
+@pytest.mark.parametrize("kv,s_q", [("fp8", 1), ("fp8", 2), ("int4", 1), ("int2", 2)])
+def test_v3_low_precision_caches_nan_tails(kv, s_q, force_generic):
+    """The unused rows of each sequence's last block hold NaN codes, RoPE keys
+    and scales (fp8) or NaN group scales and minima (int4 / int2): nothing of
+    them may reach the result, in ragged last subtiles of every length."""
+    say(f"v3 {kv} s_q={s_q} nan tails generic={force_generic}")
+    lens = np.array([2, 33, 63, 65, 100, 129, 700, 1029], dtype=np.int32)
+    case = inputs.decode_case(35 + s_q, B=len(lens), seq_lens=lens, s_q=s_q, kv_dtype=kv, tail_fill="nan", **V3)
+    o, ol = oracle.mqa_decode_case(case)
+    for splits in (0, 3):
+        g, gl = run_decode(case, num_splits=splits, force_generic=force_generic)
+        assert_bf16_close(g, o, f"{kv} nan tails splits={splits}")
+        assert_lse_close(gl, ol, "lse")
+
+
 @pytest.mark.parametrize("kv", ["int4", "int2"])
 def test_toy_int_cache_fp32_queries(kv):
     """fp32 queries at the toy dimensions (n_h 8, d_c 128, d_r 32): the
