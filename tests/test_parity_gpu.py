@@ -856,6 +856,29 @@ def test_gqa_decode_bf16_v3(s_q, n_g, lens, force_generic):
 
 
 @pytest.mark.parametrize("force_generic", [False, True])
+def test_gqa_decode_bf16_nan_tails(force_generic):
+    """GQA path: the unused rows of each sequence's last block (every group's
+    k^C and v^C rows and the shared k^R rows) hold NaN; nothing of them may
+    reach the result."""
+    say(f"gqa bf16 nan tails generic={force_generic}")
+    lens = np.array([2, 33, 63, 65, 130, 1029], dtype=np.int32)
+    case = inputs.gqa_case(48, B=len(lens), seq_lens=lens, s_q=2, n_g=8)
+    bs, n_g, d_h, d_r = case.block_size, case.n_g, case.d_h, case.d_r
+    for b, L in enumerate(lens):
+        used = int(L) - (int(L) - 1) // bs * bs
+        if used == bs:
+            continue
+        blk = case.cache[case.block_table[b, (int(L) - 1) // bs]]
+        kv = blk[: 2 * n_g * bs * d_h].reshape(2 * n_g, bs, d_h)
+        kv[:, used:] = 0x7FC0
+        blk[2 * n_g * bs * d_h:].reshape(bs, d_r)[used:] = 0x7FC0
+    g, gl = _gqa_gpu(case, force_generic)
+    o, ol = _gqa_oracle(case)
+    assert_bf16_close(g, o, "gqa nan tails o")
+    assert_lse_close(gl, ol, "gqa nan tails lse")
+
+
+@pytest.mark.parametrize("force_generic", [False, True])
 def test_gqa_decode_bf16_rising_scores(force_generic):
     """GQA path with the decode test's stepped scores (k^R dimension 0 of each
     cached row raised by the staircase, query RoPE dimension 0 = 1, the other
