@@ -199,6 +199,25 @@ def test_v3_low_precision_caches_nan_tails(kv, s_q, force_generic):
         assert_lse_close(gl, ol, "lse")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int4"])
+def test_v3_zero_queries_closed_form(kv):
+    """Zero queries give equal scores: o_lat is the plain mean of the visible
+    latent rows and lse = ln(number of visible keys), for every query token
+    (a closed form, checked beside the oracle)."""
+    say(f"v3 {kv} zero queries")
+    lens = np.array([3, 64, 65, 1000, 4097], dtype=np.int32)
+    case = inputs.decode_case(39, B=len(lens), seq_lens=lens, s_q=2, kv_dtype=kv, **V3)
+    case.q_lat[:] = 0
+    case.q_rope[:] = 0
+    g, gl = run_decode(case, num_splits=3)
+    for b, L in enumerate(lens):
+        c, _ = oracle.paged_rows(case.cache, case.block_table[b], int(L), kv, 512, 64, case.block_size)
+        for i in range(2):
+            n = int(L) - 2 + i + 1  # keys visible to query token i
+            assert_bf16_close(g[b, i], np.broadcast_to(c[:n].mean(0), (128, 512)), f"{kv} b={b} i={i}")
+            assert np.max(np.abs(gl[b, i] - math.log(n))) <= 1e-3
+
+
 @pytest.mark.parametrize("kv", ["int4", "int2"])
 def test_toy_int_cache_fp32_queries(kv):
     """fp32 queries at the toy dimensions (n_h 8, d_c 128, d_r 32): the
