@@ -23,8 +23,9 @@ the settle (steps, ms) beside the W warm-up and K timed steps.
 After the timed steps: the same steps as one mla_decode_step call each (for
 comparison), a per-stage breakdown, the separate entry points (mla_absorb_q,
 mla_decode_absorbed, mla_up_proj_v), the secondary paths (cache producer,
-MHA-mode prefill, GQA-path decode), an HBM copy probe and the float64 oracle
-on a bounded sample of the workload on the host cores.
+MHA-mode prefill, GQA-path decode; each settled on itself the same way before
+it is timed), an HBM copy probe and the float64 oracle on a bounded sample of
+the workload on the host cores.
 
 Prints one JSON line.  Metric: latent-cache bytes read per second (TB/s) of
 the whole step, with decode tokens/s and the roofline fractions alongside.
