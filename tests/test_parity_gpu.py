@@ -218,6 +218,28 @@ def test_v3_zero_queries_closed_form(kv):
             assert np.max(np.abs(gl[b, i] - math.log(n))) <= 1e-3
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_v3_randomized_configurations(seed):
+    """Seeded random configurations at V3 shapes (every cache format with
+    both kernels): new tokens per sequence, batch size, log-uniform lengths
+    and split count drawn per case, NaN in the unused tail rows, each
+    against the oracle."""
+    rng = np.random.default_rng(900 + seed)
+    kv = ["bf16", "fp8", "int4", "int2"][seed % 4]  # each format with both kernels
+    generic = seed >= 4
+    s_q = int(rng.integers(1, 4))
+    B = int(rng.integers(1, 7))
+    lens = np.exp(rng.uniform(np.log(s_q), np.log(5000), size=B)).astype(np.int32)
+    lens = np.maximum(lens, s_q)
+    splits = int(rng.choice([0, 1, 2, 5]))
+    say(f"random v3 seed={seed}: {kv} s_q={s_q} B={B} lens={lens.tolist()} splits={splits} generic={generic}")
+    case = inputs.decode_case(950 + seed, B=B, seq_lens=lens, s_q=s_q, kv_dtype=kv, tail_fill="nan", **V3)
+    g, gl = run_decode(case, num_splits=splits, force_generic=generic)
+    o, ol = oracle.mqa_decode_case(case)
+    assert_bf16_close(g, o, f"random seed={seed}")
+    assert_lse_close(gl, ol, "lse")
+
+
 @pytest.mark.parametrize("kv", ["int4", "int2"])
 def test_toy_int_cache_fp32_queries(kv):
     """fp32 queries at the toy dimensions (n_h 8, d_c 128, d_r 32): the
