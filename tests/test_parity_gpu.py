@@ -1064,6 +1064,56 @@ def test_decode_step_matches_separate_calls_and_oracle(kv, lens, s_q, splits):
     assert_lse_close(lse.cpu().numpy().astype(np.float64).reshape(case.B, s_q, 128), np.stack(ref_l), "step lse")
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_decode_step_randomized_configurations(seed):
+    """mla_decode_step on seeded random configurations (cache format, s_q,
+    batch, log-uniform lengths, splits) against the oracle's absorbed layer."""
+    rng = np.random.default_rng(970 + seed)
+    kv = ["bf16", "fp8", "int4", "int2"][seed]
+    s_q = int(rng.integers(1, 3))
+    B = int(rng.integers(1, 9))
+    lens = np.maximum(np.exp(rng.uniform(np.log(s_q), np.log(6000), size=B)).astype(np.int32), s_q)
+    splits = int(rng.choice([0, 2, 7]))
+    say(f"random step seed={seed}: {kv} s_q={s_q} B={B} lens={lens.tolist()} splits={splits}")
+    case = inputs.decode_case(980 + seed, B=B, seq_lens=lens, s_q=s_q, kv_dtype=kv, tail_fill="nan", **V3)
+    T_q = B * s_q
+    P = inputs.projection_weights(990 + seed, T_q=T_q)
+    d = case_to_device(case)
+    qn = bf16_dev(P["q_c"]).view(B, s_q, 128, 128)
+    o, lse = binding.decode_step(qn, bf16_dev(P["w_uk"]), d["q_rope"], d["kv_cache"], d["block_table"],
+                                 d["seq_lens"], bf16_dev(P["w_uv"]), d["softmax_scale"], kv_dtype=d["kv_dtype"],
+                                 num_splits=splits)
+    torch.cuda.synchronize()
+    g = o.float().cpu().numpy().astype(np.float64).reshape(T_q, 128, 128)
+    ql = oracle.absorb_q(oracle.bf16_to_f64(P["q_c"]), oracle.bf16_to_f64(P["w_uk"]), 128, 128)
+    ql = oracle.bf16_to_f64(oracle.bf16_round_bits(ql)).reshape(B, s_q, 128, 512)
+    ref_o, ref_l = [], []
+    for b in range(B):
+        _, qr, c, kr = oracle.decode_case_rows(case, b)
+        ol, l = oracle.mqa_decode_rows(ql[b], qr, c, kr, case.softmax_scale)
+        ref_o.append(oracle.up_proj_v(ol, oracle.bf16_to_f64(P["w_uv"]), 128, 128))
+        ref_l.append(l)
+    assert_bf16_close(g, np.stack(ref_o).reshape(T_q, 128, 128), f"random step seed={seed}")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64).reshape(B, s_q, 128), np.stack(ref_l), "lse")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_mha_randomized_shapes(seed):
+    """MHA-mode prefill (MFMA kernel) on seeded random lengths and head
+    counts against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    T = int(rng.integers(1, 700))
+    n_h = int(rng.integers(1, 20))
+    say(f"random prefill seed={seed}: T={T} n_h={n_h}")
+    inp = inputs.prefill_inputs(1010 + seed, T, n_h=n_h, d_c=64)
+    q, k_c, k_r, v_c = _pf_dev(inp, "q", "k_c", "k_r", "v_c")
+    o, lse = binding.prefill_mha(q, k_c, k_r, v_c, inp["scale"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = _pf_oracle(inp)
+    assert_bf16_close(o.cpu().numpy().astype(np.float64), ref_o, f"random prefill seed={seed}")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64), ref_lse, "lse")
+
+
 @pytest.mark.parametrize("kv,lens,splits", [("bf16", [2, 33, 1500, 4096], 0), ("fp8", [700, 64], 2)])
 def test_decode_step_stages_equal_the_whole_step(kv, lens, splits):
     """mla_decode_step_stages run one stage per call (on one workspace, with
