@@ -942,6 +942,23 @@ def test_gqa_decode_bf16_rising_scores(force_generic):
     assert_lse_close(gl, ol, "gqa stepped lse")
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_gqa_decode_randomized_configurations(seed):
+    """GQA path on seeded random configurations: groups and new tokens drawn
+    from the MFMA kernel's (16 heads x 2 tokens, 32 x 1, 8 x 4) and other
+    combinations (portable kernel), random batch and log-uniform lengths."""
+    rng = np.random.default_rng(1100 + seed)
+    n_g, s_q = [(8, 2), (4, 1), (16, 4), (8, 1)][seed]
+    B = int(rng.integers(1, 7))
+    lens = np.maximum(np.exp(rng.uniform(np.log(s_q), np.log(5000), size=B)).astype(np.int32), s_q)
+    say(f"random gqa seed={seed}: n_g={n_g} s_q={s_q} B={B} lens={lens.tolist()}")
+    case = inputs.gqa_case(1110 + seed, B=B, seq_lens=lens, s_q=s_q, n_g=n_g)
+    g, gl = _gqa_gpu(case)
+    o, ol = _gqa_oracle(case)
+    assert_bf16_close(g, o, f"random gqa seed={seed}")
+    assert_lse_close(gl, ol, "lse")
+
+
 def test_gqa_decode_bf16_four_tokens_of_eight_heads():
     """16 groups of 8 heads with s_q = 4: the MFMA kernel's 32 rows are four
     query tokens of eight heads (causal among the four)."""
