@@ -546,7 +546,7 @@ def _exact_rows(inp):
     return y[:, :d_c], oracle.rope(y[:, d_c:], inp["pos"])
 
 
-@pytest.mark.parametrize("T,skip", [(64, 0), (1, 0), (37, 5), (130, 0)])
+@pytest.mark.parametrize("T,skip", [(64, 0), (1, 0), (37, 5), (130, 0), (257, 3)])
 def test_cache_append_bf16_v3(T, skip):
     say(f"cache append bf16 T={T}")
     inp = inputs.append_inputs(70 + T, T, skip_every=skip)
@@ -571,7 +571,7 @@ def test_cache_append_bf16_v3(T, skip):
     assert same >= 0.97                                                    # rounding ties aside, the oracle's bits
 
 
-@pytest.mark.parametrize("T", [64, 19])
+@pytest.mark.parametrize("T", [64, 19, 150])
 def test_cache_append_fp8_v3(T):
     say(f"cache append fp8 T={T}")
     inp = inputs.append_inputs(90 + T, T, skip_every=7)
